@@ -1,0 +1,167 @@
+"""CPU oracle for the dense GEMM C = A x B.  TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports it, and the two share no code.
+
+The arithmetic lives in ``oracle.cpp`` (built with g++, OpenMP over rows, FP64
+accumulation, one round-to-nearest-even rounding to the output format).  This
+module only builds and loads that library, marshals numpy arrays, and holds
+the acceptance check.
+
+Definition followed: "Optimizing GEMM in HIP", section "GEMM fundamentals"
+(C_ij = inner product of row i of A and column j of B); storage layouts from
+"FP16 GEMM Optimization on AMD RDNA 3 and RDNA 4", section "What We Are
+Computing" (TN: A row-major, B column-major, C column-major, ld = M).
+
+Parity status: pinned (see tests/test_oracle_pins.py).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32, F16, BF16, E4M3 = 0, 1, 2, 3
+NN, TN = 0, 1
+
+FMT = {"f32": F32, "f16": F16, "bf16": BF16, "e4m3": E4M3}
+_BITS_DTYPE = {F32: np.uint32, F16: np.uint16, BF16: np.uint16, E4M3: np.uint8}
+
+# Acceptance bounds on max_ij |c - c_ref| / sum_k |a_ik b_kj|, per output.
+TOL = {"f32": 1e-6, "f16": 2.0 ** -10, "bf16": 2.0 ** -7, "fp8": 2.0 ** -7}
+
+
+def build(force: bool = False) -> str:
+    """Compile liboracle.so with g++ (no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["g++", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-std=c++17", "-fPIC", "-shared", _SRC, "-o", tmp]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        i64, vp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)
+        L.oracle_gemm.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, i64,
+                                  vp, i64, vp, i64, vp, i64, vp, vp, vp, ctypes.c_int]
+        L.oracle_gemm.restype = ctypes.c_int
+        L.oracle_gemm_plain.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, i64,
+                                        vp, i64, vp, i64, vp, vp, vp]
+        L.oracle_gemm_plain.restype = ctypes.c_int
+        L.oracle_decode.argtypes = [ctypes.c_int, vp, i64, vp]
+        L.oracle_decode.restype = None
+        L.oracle_encode.argtypes = [ctypes.c_int, vp, i64, vp]
+        L.oracle_encode.restype = None
+        L.oracle_max_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def out_fmt_of(in_fmt: int) -> int:
+    """FP8 inputs produce FP32 output; every other input format is its own output format."""
+    return F32 if in_fmt == E4M3 else in_fmt
+
+
+def gemm(in_fmt, layout, M, N, K, A, lda, B, ldb, rows=None, threads=0, plain=False):
+    """Run the oracle.
+
+    A, B are numpy arrays of raw storage bits (uint32 for f32, uint16 for
+    f16/bf16, uint8 for e4m3) holding the operands in their storage layout
+    (flattened with the given leading dimensions).  Returns (c_bits, s, sab),
+    each shaped [len(rows) or M][N] and indexed [i][j] whatever the layout.
+    """
+    A = np.ascontiguousarray(A).view(_BITS_DTYPE[in_fmt])
+    B = np.ascontiguousarray(B).view(_BITS_DTYPE[in_fmt])
+    of = out_fmt_of(in_fmt)
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+    nr = M if rows is None else len(rows)
+    c = np.zeros((nr, N), dtype=np.uint32 if of == F32 else np.uint16)
+    s = np.zeros((nr, N), dtype=np.float64)
+    sab = np.zeros((nr, N), dtype=np.float64)
+    if plain:
+        if rows is not None:
+            raise ValueError("plain loop computes all rows")
+        rc = lib().oracle_gemm_plain(in_fmt, of, layout, M, N, K, _ptr(A), lda, _ptr(B), ldb,
+                                     _ptr(c), _ptr(s), _ptr(sab))
+    else:
+        rc = lib().oracle_gemm(in_fmt, of, layout, M, N, K, _ptr(A), lda, _ptr(B), ldb,
+                               _ptr(rows), nr, _ptr(c), _ptr(s), _ptr(sab), int(threads))
+    if rc != 0:
+        raise ValueError("oracle_gemm rejected its arguments")
+    return c, s, sab
+
+
+def decode(fmt, bits) -> np.ndarray:
+    bits = np.ascontiguousarray(bits).view(_BITS_DTYPE[fmt])
+    out = np.empty(bits.shape, dtype=np.float64)
+    lib().oracle_decode(fmt, _ptr(bits), bits.size, _ptr(out))
+    return out
+
+
+def encode(fmt, x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint32 if fmt == F32 else np.uint16)
+    lib().oracle_encode(fmt, _ptr(x), x.size, _ptr(out))
+    return out
+
+
+def max_threads() -> int:
+    return lib().oracle_max_threads()
+
+
+def check(c_bits, c_ref_bits, sab, out_fmt, tol):
+    """Acceptance check of a computed C against the oracle.
+
+    err_ij = |c_ij - c_ref_ij| / sab_ij with both values decoded exactly, in
+    FP64.  Passes when max err <= tol, every element with sab == 0 matches
+    exactly, and no NaN/Inf appears where the reference is finite.
+    Returns (ok, max_err, n_bad).
+    """
+    c = decode(out_fmt, c_bits)
+    r = decode(out_fmt, c_ref_bits)
+    sab = np.asarray(sab, dtype=np.float64)
+    finite_ref = np.isfinite(r)
+    bad_nonfinite = finite_ref & ~np.isfinite(c)
+    diff = np.abs(c - r)
+    zero = sab == 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        err = np.where(zero, 0.0, diff / np.where(zero, 1.0, sab))
+    err = np.where(finite_ref, err, 0.0)
+    bad_zero = zero & finite_ref & (c != r)
+    bad = bad_nonfinite | bad_zero | (err > tol) | np.isnan(err)
+    max_err = float(np.nanmax(err)) if err.size else 0.0
+    return (not bad.any()), max_err, int(bad.sum())
+
+
+def bits_equal(c_bits, c_ref_bits, out_fmt) -> bool:
+    """Bit-exact comparison that treats +0 and -0 as equal."""
+    c = np.asarray(c_bits)
+    r = np.asarray(c_ref_bits)
+    sign = np.uint32(0x80000000) if out_fmt == F32 else np.uint16(0x8000)
+    mag_c = c & ~sign
+    mag_r = r & ~sign
+    both_zero = (mag_c == 0) & (mag_r == 0)
+    return bool(np.all(both_zero | (c == r)))

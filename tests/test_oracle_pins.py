@@ -1,0 +1,437 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+The pages print no worked numeric example of C, so the oracle is pinned by
+what mathematics and library routines fix:
+
+* exhaustive codec decoding against numpy / torch casts (every bit pattern);
+* round-to-nearest-even encoding against numpy / torch casts, and against an
+  exact-rational rounding where the library rounds twice;
+* brute force against exact rationals (``fractions.Fraction``) on tiny shapes,
+  every format and layout, with padded leading dimensions;
+* closed forms (all ones, alternating signs, rank one);
+* the identity invariant B = I => C = A ("Optimizing GEMM in HIP", note at the
+  top of the tutorial: every step is validated against B = I);
+* the +-1 invariant: every partial sum is an integer, so the result is exact
+  and must equal an integer matrix product ("FP16 GEMM Optimization on AMD
+  RDNA 3 and RDNA 4", section "What We Are Computing"; "FP8 GEMM Optimization
+  on AMD RDNA 4", section "Results");
+* FP8 exactness: E4M3 values are multiples of 2^-9, so scaled integer matrix
+  products give the exact sum;
+* thread-count independence and equality with the unblocked triple loop;
+* sensitivity: a transposed operand, a dropped term or a wrong sign each make
+  a pin fail.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dense_gemm_02_amd import inputs
+
+FMT = {"f32": oracle.F32, "f16": oracle.F16, "bf16": oracle.BF16, "fp8": oracle.E4M3}
+LAY = {"nn": oracle.NN, "tn": oracle.TN}
+
+
+# ---- independent library decoders -----------------------------------------
+
+def lib_decode(dtype, bits):
+    bits = np.asarray(bits)
+    if dtype == "f32":
+        return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    t = torch.from_numpy(np.ascontiguousarray(bits))
+    if dtype == "bf16":
+        return t.view(torch.bfloat16).to(torch.float64).numpy()
+    return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def frac_rne(q: Fraction, P: int, emin: int, emax: int) -> float:
+    """Exact-rational round-to-nearest-even onto a binary format with P
+    significand bits, normal exponents [emin, emax], gradual underflow."""
+    if q == 0:
+        return 0.0
+    sgn = -1.0 if q < 0 else 1.0
+    a = abs(q)
+    E = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** E > a:
+        E -= 1
+    while Fraction(2) ** (E + 1) <= a:
+        E += 1
+    e = max(E, emin)
+    quantum = Fraction(2) ** (e - (P - 1))
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    v = fl * quantum
+    if v >= Fraction(2) ** (emax + 1):
+        return sgn * float("inf")
+    return sgn * float(v)
+
+
+FMT_PARAMS = {"f16": (11, -14, 15), "bf16": (8, -126, 127), "f32": (24, -126, 127)}
+
+
+def lib_round(out, x):
+    """Round FP64 values to the output format with a library cast (single rounding)."""
+    x = np.asarray(x, dtype=np.float64)
+    if out == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    if out == "f16":
+        with np.errstate(over="ignore"):
+            return x.astype(np.float16).astype(np.float64)
+    return np.array([frac_rne(Fraction(float(v)), *FMT_PARAMS["bf16"]) for v in x.ravel()]).reshape(x.shape)
+
+
+def out_of(dtype):
+    return "f32" if dtype in ("f32", "fp8") else dtype
+
+
+def out_fmt(dtype):
+    return FMT[out_of(dtype)]
+
+
+def run(p, rows=None, threads=0, plain=False):
+    return oracle.gemm(FMT[p.dtype], LAY[p.layout], p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb,
+                       rows=rows, threads=threads, plain=plain)
+
+
+def exact_sums(p):
+    """Exact rational sums and abs-sums from library-decoded operands."""
+    a = lib_decode(p.dtype, p.A)
+    b = lib_decode(p.dtype, p.B)
+    S = [[Fraction(0)] * p.N for _ in range(p.M)]
+    SA = [[Fraction(0)] * p.N for _ in range(p.M)]
+    for i in range(p.M):
+        for j in range(p.N):
+            s = Fraction(0)
+            sa = Fraction(0)
+            for k in range(p.K):
+                av = Fraction(float(a[i, k]))
+                bv = Fraction(float(b[k, j] if p.layout == "nn" else b[j, k]))
+                s += av * bv
+                sa += abs(av * bv)
+            S[i][j] = s
+            SA[i][j] = sa
+    return S, SA
+
+
+# ---- codecs ------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,n", [("f16", 1 << 16), ("bf16", 1 << 16), ("fp8", 256)])
+def test_decode_exhaustive(oracle_lib, dtype, n):
+    bits = np.arange(n, dtype=np.uint16 if n > 256 else np.uint8)
+    ours = oracle.decode(FMT[dtype], bits)
+    ref = lib_decode(dtype, bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+
+
+def test_decode_e4m3_landmarks(oracle_lib):
+    # OCP E4M3: max 448, min normal 2^-6, min subnormal 2^-9, NaN = S.1111.111
+    v = oracle.decode(oracle.E4M3, np.array([0x7E, 0x08, 0x01, 0x38, 0x7F, 0xFF, 0x80], dtype=np.uint8))
+    assert v[0] == 448.0 and v[1] == 2.0 ** -6 and v[2] == 2.0 ** -9 and v[3] == 1.0
+    assert np.isnan(v[4]) and np.isnan(v[5]) and v[6] == 0.0 and np.signbit(v[6])
+
+
+def _f16_probe_values():
+    allv = np.arange(1 << 16, dtype=np.uint16).view(np.float16).astype(np.float64)
+    fin = np.sort(np.unique(allv[np.isfinite(allv)]))
+    mids = (fin[1:] + fin[:-1]) / 2.0               # exact in FP64
+    eps = np.abs(mids) * 2.0 ** -40 + 2.0 ** -60
+    return np.concatenate([fin, mids, mids + eps, mids - eps,
+                           [65504.0, 65519.0, 65519.999, 65520.0, 1e6, -65520.0, 2.0 ** -25, 2.0 ** -26]])
+
+
+def test_encode_f16_vs_numpy(oracle_lib):
+    x = _f16_probe_values()
+    ours = oracle.encode(oracle.F16, x)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_encode_bf16_vs_torch_on_fp32_inputs(oracle_lib):
+    allv = torch.arange(1 << 16, dtype=torch.int32).to(torch.int16).view(torch.bfloat16).to(torch.float64).numpy()
+    fin = np.sort(np.unique(allv[np.isfinite(allv)]))
+    mids = ((fin[1:] + fin[:-1]) / 2.0).astype(np.float32)    # exact in FP32
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(-np.inf))
+    x32 = np.concatenate([fin.astype(np.float32), mids, up, dn,
+                          np.array([3.3895314e38, 3.4e38, np.float32(np.finfo(np.float32).max)], np.float32)])
+    ours = oracle.encode(oracle.BF16, x32.astype(np.float64))
+    ref = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_encode_bf16_double_inputs_vs_exact_rounding(oracle_lib):
+    # torch rounds FP64 -> bf16 through FP32 (twice); check single rounding exactly.
+    rng = np.random.default_rng(11)
+    allv = torch.arange(1 << 16, dtype=torch.int32).to(torch.int16).view(torch.bfloat16).to(torch.float64).numpy()
+    fin = np.sort(np.unique(allv[np.isfinite(allv)]))
+    pick = rng.choice(len(fin) - 1, 3000)
+    mids = (fin[pick] + fin[pick + 1]) / 2.0
+    x = np.concatenate([mids, mids * (1 + 2.0 ** -40), mids * (1 - 2.0 ** -40), rng.standard_normal(500)])
+    x = x[np.isfinite(x)]
+    ours = oracle.decode(oracle.BF16, oracle.encode(oracle.BF16, x))
+    ref = np.array([frac_rne(Fraction(float(v)), 8, -126, 127) for v in x])
+    assert np.array_equal(ours, ref)
+
+
+def test_frac_rne_matches_numpy_f16(oracle_lib):
+    # The exact-rational rounding used as a reference is itself checked against numpy.
+    x = _f16_probe_values()[::37]
+    ref = np.array([frac_rne(Fraction(float(v)), 11, -14, 15) for v in x])
+    with np.errstate(over="ignore"):
+        lib = x.astype(np.float16).astype(np.float64)
+    assert np.array_equal(ref, lib)
+
+
+def test_encode_f32_vs_numpy(oracle_lib):
+    rng = np.random.default_rng(12)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000), [0.0, -0.0, 1e39]])
+    ours = oracle.encode(oracle.F32, x)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float32).view(np.uint32)
+    assert np.array_equal(ours, ref)
+
+
+# ---- brute force against exact rationals ------------------------------------
+
+BRUTE_SHAPES = [(1, 1, 1), (1, 3, 2), (2, 1, 5), (3, 4, 7), (5, 2, 9), (9, 9, 9), (7, 5, 0)]
+
+
+def _check_against_exact(p, c, s, sab):
+    S, SA = exact_sums(p)
+    ob = out_of(p.dtype)
+    u = 2.0 ** -53
+    for i in range(p.M):
+        for j in range(p.N):
+            ex, exa = S[i][j], SA[i][j]
+            bound = float(exa) * p.K * u * 1.01
+            assert abs(Fraction(float(s[i, j])) - ex) <= Fraction(bound), (i, j)
+            assert abs(Fraction(float(sab[i, j])) - exa) <= Fraction(bound), (i, j)
+            # c is the single rounding of the FP64 sum ...
+            got = oracle.decode(FMT[ob], np.array([c[i, j]]))[0]
+            assert got == lib_round(ob, [s[i, j]])[0] or (got == 0 and lib_round(ob, [s[i, j]])[0] == 0)
+            # ... and of the exact sum, whenever the FP64 sum was exact.
+            if Fraction(float(s[i, j])) == ex:
+                P, emin, emax = FMT_PARAMS[ob]
+                assert got == frac_rne(ex, P, emin, emax)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "fp8"])
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+def test_bruteforce_exact_rationals(oracle_lib, dtype, layout):
+    dist = {"f32": "uniform", "f16": "normal", "bf16": "normal", "fp8": "uniform4"}[dtype]
+    rng = np.random.default_rng(100 + 10 * FMT[dtype] + LAY[layout])
+    shapes = list(BRUTE_SHAPES) + [tuple(int(v) for v in rng.integers(1, 34, 3)) for _ in range(3)]
+    for (M, N, K) in shapes:
+        la, lb, _ = inputs.min_ld(layout, M, N, K)
+        p = inputs.make(dtype, layout, M, N, K, int(rng.integers(1 << 30)), dist,
+                        lda=la + int(rng.integers(0, 3)), ldb=lb + int(rng.integers(0, 3)))
+        c, s, sab = run(p)
+        if K == 0:
+            assert np.all(s == 0) and np.all(sab == 0)
+            assert np.all(oracle.decode(out_fmt(dtype), c) == 0)
+            continue
+        _check_against_exact(p, c, s, sab)
+
+
+def test_bruteforce_integer_valued_inputs_exact(oracle_lib):
+    # Small-integer operands: every FP64 sum is exact, so c must be the single
+    # rounding of the exact rational sum -- including f16/bf16 overflow to inf.
+    rng = np.random.default_rng(7)
+    for dtype in ("f32", "f16", "bf16"):
+        for layout in ("nn", "tn"):
+            M, N, K = 4, 5, 6
+            sa, sb = inputs.storage_shapes(layout, M, N, K, *inputs.min_ld(layout, M, N, K)[:2])
+            conv = {"f32": np.float32, "f16": np.float16}
+            a = rng.integers(-300, 300, sa).astype(np.float64)
+            b = rng.integers(-300, 300, sb).astype(np.float64)
+            if dtype == "bf16":
+                a = np.round(a / 2); b = np.round(b / 2)   # 8 significant bits
+                A = torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+                B = torch.from_numpy(b.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            else:
+                A = a.astype(conv[dtype]).view(np.uint32 if dtype == "f32" else np.uint16)
+                B = b.astype(conv[dtype]).view(np.uint32 if dtype == "f32" else np.uint16)
+            la, lb, lc = inputs.min_ld(layout, M, N, K)
+            p = inputs.Problem(dtype, layout, M, N, K, A, B, la, lb, lc)
+            c, s, sab = run(p)
+            _check_against_exact(p, c, s, sab)
+
+
+# ---- closed forms -------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "fp8"])
+def test_closed_forms(oracle_lib, dtype):
+    for layout in ("nn", "tn"):
+        for K in (1, 2, 3, 17, 256, 257):
+            M, N = 3, 4
+            p = inputs.make(dtype, layout, M, N, K, 0, "ones")
+            c, s, sab = run(p)
+            ob = out_of(dtype)
+            assert np.all(s == K) and np.all(sab == K)
+            assert np.all(oracle.decode(out_fmt(dtype), c) == lib_round(ob, [float(K)])[0])
+            # alternating signs along k: A = 1, b(k, j) = (-1)^k  =>  C = K mod 2
+            B = p.B.copy()
+            neg = inputs.draw(np.random.default_rng(0), (1,), "ones", dtype, 1)[0] | \
+                {"f32": np.uint32(0x80000000), "f16": np.uint16(0x8000), "bf16": np.uint16(0x8000),
+                 "fp8": np.uint8(0x80)}[dtype]
+            if layout == "nn":
+                B[1::2, :] = neg
+            else:
+                B[:, 1::2] = neg
+            q = inputs.Problem(dtype, layout, M, N, K, p.A, B, p.lda, p.ldb, p.ldc)
+            c2, s2, _ = run(q)
+            assert np.all(s2 == K % 2)
+    # rank one: A = u 1^T, B = 1 v^T  =>  C_ij = K u_i v_j
+    u = np.array([1.0, -2.0, 3.0, 0.5])
+    v = np.array([2.0, -1.0, 0.25])
+    K = 9
+    for layout in ("nn", "tn"):
+        Af = np.repeat(u[:, None], K, axis=1)
+        Bf = np.repeat(v[None, :], K, axis=0) if layout == "nn" else np.repeat(v[:, None], K, axis=1)
+        A = inputs._to_bits(Af, dtype)
+        B = inputs._to_bits(Bf, dtype)
+        la, lb, lc = inputs.min_ld(layout, 4, 3, K)
+        p = inputs.Problem(dtype, layout, 4, 3, K, A, B, la, lb, lc)
+        _, s, _ = run(p)
+        assert np.array_equal(s, K * np.outer(u, v))
+
+
+# ---- identity and +-1 invariants -------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "fp8"])
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+def test_identity(oracle_lib, dtype, layout):
+    dist = {"f32": "uniform", "f16": "normal", "bf16": "normal", "fp8": "uniform4"}[dtype]
+    M, n = 37, 33
+    p0 = inputs.make(dtype, layout, M, n, n, 5, dist)
+    p = inputs.identity(dtype, layout, n, p0.A, p0.lda)
+    c, s, _ = run(p)
+    a = lib_decode(dtype, p0.A)[:, :n]
+    assert np.array_equal(s, a)
+    if dtype != "fp8":
+        assert oracle.bits_equal(c, p0.A[:, :n], out_fmt(dtype))
+    else:
+        assert np.array_equal(oracle.decode(oracle.F32, c), a)
+
+
+def test_identity_f32_256_workload(oracle_lib):
+    p, ident = inputs.workload("f32_nn_256")
+    c, _, _ = run(ident)
+    assert oracle.bits_equal(c, p.A, oracle.F32)
+
+
+@pytest.mark.parametrize("dtype,layout,K", [("f16", "tn", 8192), ("f16", "tn", 8191), ("bf16", "tn", 1000),
+                                            ("fp8", "tn", 4096), ("f32", "nn", 2049)])
+def test_pm1_exact_against_integer_matmul(oracle_lib, dtype, layout, K):
+    M, N = 24, 20
+    p = inputs.make(dtype, layout, M, N, K, 2, "pm1")
+    c, s, sab = run(p)
+    a = lib_decode(dtype, p.A).astype(np.int64)
+    b = lib_decode(dtype, p.B).astype(np.int64)
+    ref = a @ (b if layout == "nn" else b.T)
+    assert np.array_equal(s, ref.astype(np.float64))
+    assert np.all(sab == K)
+    assert np.all((ref - K) % 2 == 0)
+    assert np.array_equal(oracle.decode(out_fmt(dtype), c), lib_round(out_of(dtype), ref.astype(np.float64)))
+
+
+def test_fp8_exact_against_scaled_integer_matmul(oracle_lib):
+    M, N, K = 16, 24, 4096
+    p = inputs.make("fp8", "tn", M, N, K, 5, "uniform4")
+    _, s, sab = run(p)
+    a = (lib_decode("fp8", p.A) * 512).astype(np.int64)     # multiples of 2^-9
+    b = (lib_decode("fp8", p.B) * 512).astype(np.int64)
+    ref = a @ b.T
+    assert np.array_equal(s * 2.0 ** 18, ref.astype(np.float64))
+    assert np.array_equal(sab * 2.0 ** 18, (np.abs(a) @ np.abs(b).T).astype(np.float64))
+
+
+def test_f32_against_library_matmul_bound(oracle_lib):
+    p = inputs.make("f32", "nn", 40, 50, 300, 1, "uniform")
+    _, s, sab = run(p)
+    a = lib_decode("f32", p.A)
+    b = lib_decode("f32", p.B)
+    ref = a @ b
+    assert np.all(np.abs(s - ref) <= 2 * 300 * 2.0 ** -53 * sab)
+
+
+# ---- determinism and loop equivalence ----------------------------------------
+
+def test_threads_rows_and_plain_loop_agree(oracle_lib):
+    for dtype, layout in (("bf16", "tn"), ("f32", "nn"), ("fp8", "tn"), ("f16", "nn")):
+        dist = {"f32": "uniform", "f16": "normal", "bf16": "normal", "fp8": "uniform4"}[dtype]
+        p = inputs.make(dtype, layout, 23, 19, 301, 3, dist)
+        c1, s1, a1 = run(p, threads=1)
+        c8, s8, a8 = run(p, threads=8)
+        cp, sp, ap = run(p, plain=True)
+        for x, y, z in ((c1, c8, cp), (s1, s8, sp), (a1, a8, ap)):
+            assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+            assert np.array_equal(x.view(np.uint8), z.view(np.uint8))
+        rows = np.array([22, 0, 7, 7, 13])
+        cr, sr, ar = run(p, rows=rows)
+        assert np.array_equal(cr, c1[rows]) and np.array_equal(sr.view(np.uint64), s1[rows].view(np.uint64))
+
+
+# ---- acceptance checker -------------------------------------------------------
+
+def test_checker_accepts_and_rejects_as_predicted(oracle_lib):
+    p = inputs.make("bf16", "tn", 16, 16, 64, 9, "normal")
+    c, s, sab = run(p)
+    ok, err, nbad = oracle.check(c, c, sab, oracle.BF16, oracle.TOL["bf16"])
+    assert ok and err == 0 and nbad == 0
+    # one bf16 ulp on one element: relative to sab it is well inside 2^-7
+    c1 = c.copy(); c1[3, 4] += 1
+    ok, err, _ = oracle.check(c1, c, sab, oracle.BF16, oracle.TOL["bf16"])
+    assert ok and err > 0
+    # an error of 2^-6 * sab on one element must fail
+    bad = c.copy()
+    target = oracle.decode(oracle.BF16, c)[5, 6] + sab[5, 6] * 2.0 ** -6
+    bad[5, 6] = oracle.encode(oracle.BF16, np.array([target]))[0]
+    ok, _, nbad = oracle.check(bad, c, sab, oracle.BF16, oracle.TOL["bf16"])
+    assert not ok and nbad == 1
+    # NaN where the reference is finite fails
+    nanc = c.copy(); nanc[0, 0] = 0x7fc0
+    assert not oracle.check(nanc, c, sab, oracle.BF16, 1.0)[0]
+    # sab == 0 requires exact equality
+    z = np.zeros((1, 1), np.uint16)
+    assert oracle.check(z, z, np.zeros((1, 1)), oracle.BF16, 1.0)[0]
+    assert not oracle.check(z + 1, z, np.zeros((1, 1)), oracle.BF16, 1.0)[0]
+    # bit equality treats +0 and -0 alike, nothing else
+    assert oracle.bits_equal(np.array([0x8000], np.uint16), np.array([0], np.uint16), oracle.BF16)
+    assert not oracle.bits_equal(np.array([0x8001], np.uint16), np.array([1], np.uint16), oracle.BF16)
+
+
+# ---- sensitivity: planted mistakes must trip a pin ---------------------------
+
+def test_pins_catch_planted_mistakes(oracle_lib):
+    p = inputs.make("f16", "tn", 6, 6, 40, 21, "pm1")
+    a = lib_decode("f16", p.A).astype(np.int64)
+    b = lib_decode("f16", p.B).astype(np.int64)
+    ref = a @ b.T
+    assert np.array_equal(run(p)[1], ref)
+    # transposed operand: read the square TN B storage as if it were NN
+    sq = inputs.make("f16", "tn", 6, 6, 6, 23, "pm1")
+    sref = lib_decode("f16", sq.A).astype(np.int64) @ lib_decode("f16", sq.B).astype(np.int64).T
+    _, s_t, _ = oracle.gemm(oracle.F16, oracle.NN, 6, 6, 6, sq.A, 6, sq.B, 6)
+    assert not np.array_equal(s_t, sref)
+    # dropped term: K - 1 instead of K
+    _, s_d, _ = oracle.gemm(oracle.F16, oracle.TN, 6, 6, 39, p.A, p.lda, p.B, p.ldb)
+    assert not np.array_equal(s_d, ref)
+    # wrong sign of one operand
+    _, s_n, _ = oracle.gemm(oracle.F16, oracle.TN, 6, 6, 40, p.A ^ np.uint16(0x8000), p.lda, p.B, p.ldb)
+    assert not np.array_equal(s_n, ref)
+    # wrong index: row i of A paired with row i+1
+    _, s_i, _ = oracle.gemm(oracle.F16, oracle.TN, 5, 6, 40, p.A[1:].copy(), p.lda, p.B, p.ldb)
+    assert not np.array_equal(s_i, ref[:5])
