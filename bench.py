@@ -1,0 +1,202 @@
+"""Benchmark of the dense GEMM hot path on one MI355X.
+
+One step = one C = A x B through the C ABI (host dispatch, tile scheduler,
+buffer loads, swizzled LDS, MFMA pipeline, converting epilogue) on inputs
+already resident in HBM.  Default workload: FP16 TN, M = N = K = 8192,
+A and B i.i.d. N(0,1)/sqrt(K) rounded to FP16 (seed 3), FP32 accumulation,
+FP16 output.  BF16 TN and FP8 E4M3 TN at the same size are timed in the
+same run and reported under "per_dtype".
+
+Timing: W untimed warm-up steps, then exactly K steps between two
+synchronisations, with HIP events recorded on the stream the kernels run on.
+TFLOP/s = 2*M*N*K / t.  Prints one JSON line.
+
+cpu_baseline: the CPU oracle (test infrastructure, never tuned) timed on a
+bounded sample of whole output rows of the same workload, on this host's
+cores; its rate is scaled to TFLOP/s of useful work.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s + % of dense MFMA peak (FP16/BF16/FP8, M=N=K=8192)"
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}
+HBM_GBS = 8000.0
+WORKLOADS = {
+    "f16": ("f16", "tn", 8192, 8192, 8192, 3, "normal"),
+    "bf16": ("bf16", "tn", 8192, 8192, 8192, 4, "normal"),
+    "fp8": ("fp8", "tn", 8192, 8192, 8192, 5, "uniform4"),
+}
+DTYPE_NAME = {"f16": "f16", "bf16": "bf16", "fp8": "fp8 (e4m3) x fp8 -> f32", "f32": "f32"}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_gemm_02_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if they were
+    taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    w = t.get("workloads", {}).get(workload)
+    return None if w is None else float(w["hbm_bytes_per_launch"])
+
+
+def make_inputs(dtype):
+    import torch
+    from dense_gemm_02_amd import inputs
+    dt, layout, M, N, K, seed, dist = WORKLOADS[dtype]
+    p = inputs.make(dt, layout, M, N, K, seed, dist)
+
+    def dev(x):
+        x = np.ascontiguousarray(x)
+        v = {np.dtype(np.uint32): np.int32, np.dtype(np.uint16): np.int16, np.dtype(np.uint8): np.uint8}[x.dtype]
+        return torch.from_numpy(x.view(v)).cuda()
+
+    A, B = dev(p.A), dev(p.B)
+    out32 = dt in ("f32", "fp8")
+    C = torch.empty((N, p.ldc) if layout == "tn" else (M, p.ldc),
+                    dtype=torch.int32 if out32 else torch.int16, device="cuda")
+    return p, A, B, C
+
+
+def time_gemm(dtype, steps, warmup):
+    import torch
+    from dense_gemm_02_amd import binding
+    p, A, B, C = make_inputs(dtype)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        binding.gemm(p.dtype, p.layout, p.M, p.N, p.K, A, p.lda, B, p.ldb, C, p.ldc, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    flops = p.flops
+    return p, {"ms_per_launch": ms, "tflops": flops / (ms * 1e-3) / 1e12, "wall_s": wall}
+
+
+def cpu_baseline(dtype, target_s=12.0):
+    """The oracle on whole output rows of the same workload, timed wall-clock."""
+    import oracle
+    from dense_gemm_02_amd import inputs
+    dt, layout, M, N, K, seed, dist = WORKLOADS[dtype]
+    p = inputs.make(dt, layout, M, N, K, seed, dist)
+    fmt = {"f32": oracle.F32, "f16": oracle.F16, "bf16": oracle.BF16, "fp8": oracle.E4M3}[dt]
+    lay = oracle.TN if layout == "tn" else oracle.NN
+    threads = oracle.max_threads()
+    rng = np.random.default_rng(0)
+    nrows = 8
+    while True:
+        rows = np.sort(rng.choice(M, nrows, replace=False))
+        t0 = time.perf_counter()
+        oracle.gemm(fmt, lay, M, N, K, p.A, p.lda, p.B, p.ldb, rows=rows, threads=threads)
+        dt_s = time.perf_counter() - t0
+        if dt_s >= target_s * 0.5 or nrows >= M:
+            break
+        nrows = min(M, max(nrows * 2, int(nrows * target_s / max(dt_s, 1e-3))))
+    flops = 2.0 * nrows * N * K
+    return {"value": flops / dt_s / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nrows} of {M} output rows (all {N} columns, K={K}) of {dtype} {layout} "
+                      f"{M}x{N}x{K}, {dt_s:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--dtype", default="f16", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", action="store_true", help="time only --dtype")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(see the sharding note in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from dense_gemm_02_amd import binding
+    binding.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    p, head = time_gemm(args.dtype, args.steps, args.warmup)
+    print(f"[bench] {args.dtype}: {head['ms_per_launch']:.4f} ms/launch, {head['tflops']:.1f} TFLOP/s",
+          file=sys.stderr, flush=True)
+    per = {}
+    if not args.only:
+        for d in WORKLOADS:
+            if d == args.dtype:
+                continue
+            _, r = time_gemm(d, args.steps, args.warmup)
+            per[d] = {"tflops": round(r["tflops"], 1), "ms_per_launch": round(r["ms_per_launch"], 4),
+                      "frac_of_peak": round(r["tflops"] / PEAK_TFLOPS[d], 4)}
+            print(f"[bench] {d}: {r['ms_per_launch']:.4f} ms/launch, {r['tflops']:.1f} TFLOP/s",
+                  file=sys.stderr, flush=True)
+
+    workload = f"{p.dtype}_{p.layout}_{p.M}x{p.N}x{p.K}"
+    traffic = load_traffic(workload)
+    roof = {"bound": "mfma", "achieved": round(head["tflops"], 2), "peak": PEAK_TFLOPS[args.dtype],
+            "unit": "TFLOP/s", "frac": round(head["tflops"] / PEAK_TFLOPS[args.dtype], 4),
+            "traffic": traffic}
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.dtype)
+    line = {
+        "metric": METRIC,
+        "value": round(head["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_launch"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.dtype,
+        "data": "synthetic",
+        "config": {"workload": workload, "M": p.M, "N": p.N, "K": p.K, "layout": p.layout,
+                   "inputs": f"{p.meta['dist']} seed {p.meta['seed']}", "accumulate": "f32",
+                   "kernel_sources": kernel_source_hash()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_dtype": per,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,120 @@
+"""ctypes binding of ``libdgemm.so`` (declared in ``include/dgemm.h``).
+
+Argument marshalling only: every step of the product runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current HIP stream.
+There is no fallback: if the library is missing or a call fails, a
+``DgemmError`` is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIBNAME = "libdgemm.so"
+
+DGEMM_NN, DGEMM_TN = 0, 1
+_LAYOUTS = {"nn": DGEMM_NN, "tn": DGEMM_TN}
+
+
+class DgemmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {gemm_strerror(status)} (status {status})")
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIBNAME)
+
+
+_lib = None
+
+
+def load_library():
+    """Load libdgemm.so (built by ``__graft_entry__.build()``); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(path)
+    i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    for name in ("gemm_f32", "gemm_f16", "gemm_bf16", "gemm_fp8"):
+        fn = getattr(L, name)
+        fn.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, vp]
+        fn.restype = ci
+    L.gemm_strerror.argtypes = [ci]
+    L.gemm_strerror.restype = ctypes.c_char_p
+    L.dgemm_tile_map.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.dgemm_tile_map.restype = ci
+    L.dgemm_lds_bytes.argtypes = [ci, ci, ci, ci, ci, ci]
+    L.dgemm_lds_bytes.restype = i64
+    L.dgemm_kernel_config.argtypes = [ci, ci, i64, i64, i64, ctypes.c_char_p, i64]
+    L.dgemm_kernel_config.restype = ci
+    _lib = L
+    return L
+
+
+def gemm_strerror(status: int) -> str:
+    try:
+        return load_library().gemm_strerror(int(status)).decode()
+    except ImportError:
+        return "unknown status"
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _raw(fn_name, M, N, K, A, lda, B, ldb, C, ldc, layout, stream):
+    L = load_library()
+    lay = _LAYOUTS.get(layout, layout) if isinstance(layout, str) else layout
+    st = getattr(L, fn_name)(int(M), int(N), int(K), A, int(lda), B, int(ldb), C, int(ldc),
+                             int(lay), _stream_handle(stream))
+    if st != 0:
+        raise DgemmError(st, fn_name)
+
+
+def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, layout="nn", stream=None):
+    """Raw-pointer call: A, B, C are device addresses (ints)."""
+    _raw("gemm_f32", M, N, K, A, lda, B, ldb, C, ldc, layout, stream)
+
+
+def gemm_f16(M, N, K, A, lda, B, ldb, C, ldc, layout="tn", stream=None):
+    _raw("gemm_f16", M, N, K, A, lda, B, ldb, C, ldc, layout, stream)
+
+
+def gemm_bf16(M, N, K, A, lda, B, ldb, C, ldc, layout="tn", stream=None):
+    _raw("gemm_bf16", M, N, K, A, lda, B, ldb, C, ldc, layout, stream)
+
+
+def gemm_fp8(M, N, K, A, lda, B, ldb, C, ldc, layout="tn", stream=None):
+    _raw("gemm_fp8", M, N, K, A, lda, B, ldb, C, ldc, layout, stream)
+
+
+_BY_DTYPE = {"f32": gemm_f32, "f16": gemm_f16, "bf16": gemm_bf16, "fp8": gemm_fp8}
+_ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+
+
+def gemm(dtype, layout, M, N, K, A, lda, B, ldb, C, ldc, stream=None):
+    """Tensor-level call.  A, B, C are torch device tensors holding the
+    operands' storage (any integer or float dtype of the right width); the
+    leading dimensions are in elements."""
+    import torch
+    for t in (A, B, C):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError("A, B and C must be device tensors")
+    ebytes = _ELEM[dtype]
+    if A.element_size() != ebytes or B.element_size() != ebytes:
+        raise TypeError(f"{dtype} operands need {ebytes}-byte elements")
+    cbytes = 4 if dtype in ("f32", "fp8") else 2
+    if C.element_size() != cbytes:
+        raise TypeError(f"{dtype} output needs {cbytes}-byte elements")
+    _BY_DTYPE[dtype](M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, layout, stream)

@@ -1,0 +1,91 @@
+// Shared device/host pieces of the gfx950 GEMM kernels: vector types, buffer
+// resource descriptors, the block -> tile scheduler and LDS sizing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Number of XCDs on MI355X; workgroups are dispatched round-robin over them.
+constexpr int kXcds = 8;
+
+// Offset used to force a buffer load out of range.  Every descriptor built by
+// these kernels has num_records < 2^31, so this offset always reads zero.
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+// Raw (untyped, stride 0) buffer descriptor, word 3 of the gfx9-family
+// encoding (data format 32-bit; the RDNA word printed on the pages does not
+// apply to CDNA).  Loads at offsets >= num_records return zero instead of
+// faulting ("FP16 GEMM Optimization on AMD RDNA 3 and RDNA 4", section
+// "Step 4: Buffer Resource Descriptors for Global Loads").
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_records) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_records, kBufferWord3);
+}
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+}
+
+// ---- block -> tile scheduler -------------------------------------------------
+// 1. XCD spread: block `pid` runs on XCD pid % 8.  Renumber blocks so that
+//    each XCD receives a contiguous range of logical tile ids; neighbouring
+//    tiles then share that XCD's private L2.  Ranges differ in length by at
+//    most one when the block count is not a multiple of 8, keeping the map a
+//    bijection.
+// 2. Grouping ("FP16 GEMM Optimization on AMD RDNA 3 and RDNA 4", Step 6):
+//    logical ids walk `group` tiles along p, then step along q, so blocks in
+//    flight at the same time reuse the same operand panels; the last group
+//    may be shorter.
+__host__ __device__ inline void tile_map(int64_t tiles_p, int64_t tiles_q, int64_t group, int64_t pid,
+                                         int64_t* tp, int64_t* tq) {
+  const int64_t total = tiles_p * tiles_q;
+  const int64_t per = total / kXcds, extra = total % kXcds;
+  const int64_t xcd = pid % kXcds, local = pid / kXcds;
+  const int64_t lid = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + local;
+  const int64_t width = group * tiles_q;
+  const int64_t g = lid / width;
+  const int64_t first = g * group;
+  const int64_t rest = tiles_p - first;
+  const int64_t gsz = rest < group ? rest : group;
+  const int64_t in = lid - g * width;
+  *tp = first + in % gsz;
+  *tq = in / gsz;
+}
+
+// LDS bytes of a block tile: (BM + BN) rows of BK*elem bytes plus a per-row pad,
+// times the number of buffers.
+__host__ __device__ constexpr int64_t lds_bytes(int bm, int bn, int bk, int elem, int pad, int bufs) {
+  return (int64_t)(bm + bn) * (int64_t)(bk * elem + pad) * (int64_t)bufs;
+}
+
+constexpr int64_t kLdsLimit = 163840;  // 160 KiB per workgroup on gfx950
+
+// Kernel arguments shared by every GEMM kernel.  The kernels compute
+// D[p][q] = sum_k P(p,k) * Q(q,k) and store D[p][q] at C[q*ldc + p]:
+//   TN: P = A (p = i), Q = B (q = j), C column-major  -> C[j*ldc + i]
+//   NN: P = B^T (p = j), Q = A (q = i), C row-major   -> C[i*ldc + j]
+// so p is always the contiguous direction of C.
+struct GemmArgs {
+  const char* P;     // operand P base
+  const char* Q;     // operand Q base
+  void* C;
+  int64_t ldp;       // bytes between consecutive rows of P's storage
+  int64_t ldq;       // bytes between consecutive rows of Q's storage
+  int64_t ldc;       // elements between consecutive q of C
+  int64_t Pn, Qn, K; // extents of p, q and k
+  int64_t tiles_p, tiles_q, group;
+  int vec_store;     // C and ldc allow 4-element vector stores
+};
+
+}  // namespace dg

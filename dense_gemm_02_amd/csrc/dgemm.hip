@@ -1,0 +1,200 @@
+// libdgemm.so: the C ABI declared in include/dgemm.h.
+//
+// Host side of every call: validate the arguments, map (A, B, C, layout) onto
+// the kernels' (P, Q, D) form, pick a tile configuration, and launch on the
+// caller's stream.  No allocation, no synchronisation, no global state.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/dgemm.h"
+#include "common.hpp"
+#include "gemm_f32.hpp"
+#include "gemm_mfma.hpp"
+
+namespace dg {
+namespace {
+
+enum Dtype { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };
+
+constexpr int64_t kMaxDescBytes = (int64_t(1) << 31) - 64;
+
+int in_elem(int dt) { return dt == DT_F32 ? 4 : (dt == DT_FP8 ? 1 : 2); }
+int out_elem(int dt) { return (dt == DT_F32 || dt == DT_FP8) ? 4 : 2; }
+
+// A launchable configuration: a kernel symbol plus its tile geometry.
+struct Launch {
+  const void* fn;
+  const char* name;
+  int bp, bq, threads, lds;
+  bool p_trans;
+};
+
+// ---- kernel table ------------------------------------------------------------
+// 16-bit and FP8: 256 x 256 block tile, 8 waves as 2 (p) x 4 (q), wave tile
+// 128 x 64 (4 x 2 MFMA tiles of 32 x 32), 128 bytes of K per stage, two LDS
+// buffers (128 KiB).
+// FP32: 128 x 128 block tile, 4 waves as 2 x 2, wave tile 64 x 64, K = 32 per
+// stage, two buffers (64-68 KiB, so two workgroups fit one CU).
+
+template <class Op, bool PT>
+Launch mfma_launch(const char* name) {
+  using Cfg = MfmaCfg<Op, 256, 256, 2, 4, PT>;
+  return Launch{(const void*)&gemm_mfma_kernel<Op, 256, 256, 2, 4, PT>, name, 256, 256, Cfg::NT,
+                2 * Cfg::STAGE, PT};
+}
+
+template <bool PT>
+Launch f32_launch(const char* name) {
+  using Cfg = F32Cfg<128, 128, 2, 2, PT>;
+  return Launch{(const void*)&gemm_f32_kernel<128, 128, 2, 2, PT>, name, 128, 128, Cfg::NT, 2 * Cfg::STAGE, PT};
+}
+
+Launch select(int dt, int layout) {
+  const bool nn = layout == DGEMM_NN;
+  switch (dt) {
+    case DT_F32:  return nn ? f32_launch<true>("f32_nn_128x128") : f32_launch<false>("f32_tn_128x128");
+    case DT_F16:  return nn ? mfma_launch<OpF16, true>("f16_nn_256x256") : mfma_launch<OpF16, false>("f16_tn_256x256");
+    case DT_BF16: return nn ? mfma_launch<OpBF16, true>("bf16_nn_256x256") : mfma_launch<OpBF16, false>("bf16_tn_256x256");
+    default:      return nn ? mfma_launch<OpFP8, true>("fp8_nn_256x256") : mfma_launch<OpFP8, false>("fp8_tn_256x256");
+  }
+}
+
+struct Plan {
+  Launch L;
+  GemmArgs g;
+  int64_t grid;
+};
+
+// Validation in the documented order, then the (P, Q, D) mapping.
+int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+         void* C, int64_t ldc, int layout, Plan* out, bool check_pointers) {
+  if (layout != DGEMM_NN && layout != DGEMM_TN) return DGEMM_ERR_INVALID_LAYOUT;
+  if (M < 0 || N < 0 || K < 0) return DGEMM_ERR_INVALID_DIM;
+  if (M == 0 || N == 0) { out->grid = 0; return DGEMM_OK; }
+  if (check_pointers && ((K > 0 && (A == nullptr || B == nullptr)) || C == nullptr)) return DGEMM_ERR_NULL_POINTER;
+  const bool nn = layout == DGEMM_NN;
+  const int64_t min_lda = K > 0 ? K : 1;
+  const int64_t min_ldb = nn ? N : (K > 0 ? K : 1);
+  const int64_t min_ldc = nn ? N : M;
+  if (lda < min_lda || ldb < min_ldb || ldc < min_ldc) return DGEMM_ERR_INVALID_LD;
+  const int e = in_elem(dt);
+  if (check_pointers && K > 0 &&
+      ((((uintptr_t)A) & 15) != 0 || (((uintptr_t)B) & 15) != 0 || ((lda * e) & 15) != 0 || ((ldb * e) & 15) != 0))
+    return DGEMM_ERR_MISALIGNED;
+  if (((uintptr_t)C) % (uintptr_t)out_elem(dt) != 0) return DGEMM_ERR_MISALIGNED;
+
+  Launch L = select(dt, layout);
+  GemmArgs g{};
+  if (!nn) {
+    g.P = (const char*)A; g.ldp = lda * e; g.Pn = M;
+    g.Q = (const char*)B; g.ldq = ldb * e; g.Qn = N;
+  } else {
+    g.P = (const char*)B; g.ldp = ldb * e; g.Pn = N;
+    g.Q = (const char*)A; g.ldq = lda * e; g.Qn = M;
+  }
+  g.C = C; g.ldc = ldc; g.K = K;
+  // Descriptor ranges must stay below 2^31 bytes.
+  if ((int64_t)L.bq * g.ldq > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
+  if (!L.p_trans && (int64_t)L.bp * g.ldp > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
+  if (L.p_trans && K * g.ldp > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
+  if (K * e > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
+  g.tiles_p = (g.Pn + L.bp - 1) / L.bp;
+  g.tiles_q = (g.Qn + L.bq - 1) / L.bq;
+  g.group = 8;
+  const int oe = out_elem(dt);
+  g.vec_store = ((((uintptr_t)C) % (uintptr_t)(4 * oe)) == 0 && ((ldc * oe) % (4 * oe)) == 0) ? 1 : 0;
+  out->L = L;
+  out->g = g;
+  out->grid = g.tiles_p * g.tiles_q;
+  if (out->grid > 0x7fffffff) return DGEMM_ERR_UNSUPPORTED;
+  return DGEMM_OK;
+}
+
+int run(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+        void* C, int64_t ldc, int layout, void* stream) {
+  Plan pl;
+  const int st = plan(dt, M, N, K, A, lda, B, ldb, C, ldc, layout, &pl, true);
+  if (st != DGEMM_OK || pl.grid == 0) return st;
+  void* args[] = {(void*)&pl.g};
+  const hipError_t err = hipLaunchKernel(pl.L.fn, dim3((unsigned)pl.grid), dim3(pl.L.threads), args, 0,
+                                         (hipStream_t)stream);
+  if (err != hipSuccess) return DGEMM_ERR_HIP;
+  return hipGetLastError() == hipSuccess ? DGEMM_OK : DGEMM_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace dg
+
+extern "C" {
+
+int gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B, int64_t ldb, float* C,
+             int64_t ldc, int layout, void* stream) {
+  return dg::run(dg::DT_F32, M, N, K, A, lda, B, ldb, C, ldc, layout, stream);
+}
+
+int gemm_f16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+             uint16_t* C, int64_t ldc, int layout, void* stream) {
+  return dg::run(dg::DT_F16, M, N, K, A, lda, B, ldb, C, ldc, layout, stream);
+}
+
+int gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+              uint16_t* C, int64_t ldc, int layout, void* stream) {
+  return dg::run(dg::DT_BF16, M, N, K, A, lda, B, ldb, C, ldc, layout, stream);
+}
+
+int gemm_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+             float* C, int64_t ldc, int layout, void* stream) {
+  return dg::run(dg::DT_FP8, M, N, K, A, lda, B, ldb, C, ldc, layout, stream);
+}
+
+const char* gemm_strerror(int status) {
+  switch (status) {
+    case DGEMM_OK: return "success";
+    case DGEMM_ERR_INVALID_DIM: return "invalid dimension (M, N or K negative)";
+    case DGEMM_ERR_NULL_POINTER: return "null operand pointer";
+    case DGEMM_ERR_INVALID_LD: return "leading dimension below its minimum";
+    case DGEMM_ERR_INVALID_LAYOUT: return "layout is neither DGEMM_NN nor DGEMM_TN";
+    case DGEMM_ERR_MISALIGNED: return "operand base or pitch not 16-byte aligned";
+    case DGEMM_ERR_UNSUPPORTED: return "problem exceeds the supported size limits";
+    case DGEMM_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int dgemm_tile_map(int64_t tiles_p, int64_t tiles_q, int64_t group, int64_t pid, int64_t* tile_p, int64_t* tile_q) {
+  if (tiles_p <= 0 || tiles_q <= 0 || group <= 0 || pid < 0 || pid >= tiles_p * tiles_q || !tile_p || !tile_q)
+    return -1;
+  dg::tile_map(tiles_p, tiles_q, group, pid, tile_p, tile_q);
+  return 0;
+}
+
+int64_t dgemm_lds_bytes(int bm, int bn, int bk, int elem, int pad_bytes, int buffers) {
+  if (bm < 0 || bn < 0 || bk < 0 || elem < 0 || pad_bytes < 0 || buffers < 0) return -1;
+  return dg::lds_bytes(bm, bn, bk, elem, pad_bytes, buffers);
+}
+
+int dgemm_kernel_config(int dtype, int layout, int64_t M, int64_t N, int64_t K, char* buf, int64_t len) {
+  if (dtype < 0 || dtype > 3) return DGEMM_ERR_UNSUPPORTED;
+  const int e = dg::in_elem(dtype);
+  const bool nn = layout == DGEMM_NN;
+  // Minimal legal, aligned leading dimensions for the description.
+  int64_t lda = K > 0 ? K : 1, ldb = nn ? N : (K > 0 ? K : 1);
+  const int64_t al = 16 / e;
+  lda = (lda + al - 1) / al * al;
+  ldb = (ldb + al - 1) / al * al;
+  dg::Plan pl;
+  const int st = dg::plan(dtype, M, N, K, nullptr, lda, nullptr, ldb, nullptr, nn ? N : M, layout, &pl, false);
+  if (st != DGEMM_OK) return st;
+  if (buf && len > 0) {
+    if (pl.grid == 0)
+      snprintf(buf, (size_t)len, "none (empty output)");
+    else
+      snprintf(buf, (size_t)len, "%s tile=%dx%d threads=%d lds=%d grid=%lld tiles=%lldx%lld group=%lld",
+               pl.L.name, pl.L.bp, pl.L.bq, pl.L.threads, pl.L.lds, (long long)pl.grid, (long long)pl.g.tiles_p,
+               (long long)pl.g.tiles_q, (long long)pl.g.group);
+  }
+  return DGEMM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,352 @@
+// Tiled MFMA GEMM for 16-bit (FP16, BF16) and 8-bit (OCP E4M3) operands on
+// gfx950, FP32 accumulation.
+//
+// One workgroup computes a BP x BQ block of D[p][q] = sum_k P(p,k) Q(q,k)
+// (see GemmArgs for how A, B and C map onto P, Q and D).  The structure
+// follows the software pipeline the pages build up ("FP16 GEMM Optimization
+// on AMD RDNA 3 and RDNA 4", Steps 2-6; "An Educational GEMM Ladder for
+// Helios GPUs", Levels 1-5), re-derived for CDNA4:
+//
+//  * Global -> registers: 16-byte buffer loads through a descriptor whose
+//    num_records bounds the block's valid region; rows past the matrix edge
+//    and chunks past K are pushed out of range and read as zero (Step 4).
+//    A chunk that straddles K is masked element by element in registers.
+//  * Registers -> LDS: every LDS row holds one stage of K for one p (or q)
+//    index, 128 bytes, K-contiguous for both operands ("What We Are
+//    Computing": K last in every LDS tile).  16-byte chunks are XOR-swizzled
+//    with key (row / 2) mod 8 (Step 3's permutation, re-keyed for gfx950:
+//    64 banks x 4 bytes = 256 bytes per bank row hold two 128-byte tile rows,
+//    so rows 2r and 2r+1 share a key and differ in the bank half instead).
+//    The NN B operand arrives p-contiguous and is transposed element by
+//    element on its way into LDS.
+//  * Double buffering with a staged commit: the next stage's global loads are
+//    issued before the current stage's MFMAs and written to the other LDS
+//    buffer after them, one barrier per stage (Step 2).
+//  * MFMA: v_mfma_f32_32x32x16_{f16,bf16} (k = 16, 16 bytes per lane per
+//    operand) or v_mfma_scale_f32_32x32x64_f8f6f4 with unit E8M0 scales
+//    (k = 64, 32 bytes per lane), FP32 accumulators in registers.
+//  * Epilogue: each lane holds four consecutive p of one q, contiguous in C;
+//    convert with round-to-nearest-even and store 8 or 16 bytes at a time.
+#pragma once
+
+#include <type_traits>
+
+#include "common.hpp"
+
+namespace dg {
+
+// ---- per-format operations ---------------------------------------------------
+
+struct OpF16 {
+  static constexpr int ELEM = 2;   // bytes per input element
+  static constexpr int KI = 16;    // k per MFMA
+  static constexpr int FC = 1;     // 16-byte chunks per lane per operand per MFMA
+  static constexpr int OE = 2;     // bytes per output element
+  typedef f16x8 Frag;
+  __device__ static Frag frag(const char* base, const uint32_t* off) { return *(const Frag*)(base + off[0]); }
+  __device__ static f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static uint32_t pack2(float x, float y) {
+    const _Float16 hx = (_Float16)x, hy = (_Float16)y;
+    return (uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16);
+  }
+  __device__ static uint16_t one(float x) { const _Float16 h = (_Float16)x; return __builtin_bit_cast(uint16_t, h); }
+};
+
+struct OpBF16 {
+  static constexpr int ELEM = 2, KI = 16, FC = 1, OE = 2;
+  typedef bf16x8 Frag;
+  __device__ static Frag frag(const char* base, const uint32_t* off) { return *(const Frag*)(base + off[0]); }
+  __device__ static f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static uint32_t pack2(float x, float y) {
+    const __bf16 hx = (__bf16)x, hy = (__bf16)y;
+    return (uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16);
+  }
+  __device__ static uint16_t one(float x) { const __bf16 h = (__bf16)x; return __builtin_bit_cast(uint16_t, h); }
+};
+
+struct OpFP8 {
+  static constexpr int ELEM = 1, KI = 64, FC = 2, OE = 4;
+  typedef i32x8 Frag;
+  // 32 bytes of k per lane, read as two 16-byte (swizzled) chunks.
+  __device__ static Frag frag(const char* base, const uint32_t* off) {
+    const i32x4 lo = *(const i32x4*)(base + off[0]);
+    const i32x4 hi = *(const i32x4*)(base + off[1]);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // Formats 0/0 = E4M3 for both operands; scales 127 = 2^0 in E8M0.
+  __device__ static f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
+// Zero the bytes of a 16-byte chunk at and beyond `valid_bytes` (0..16).
+__device__ __forceinline__ u32x4 mask_tail(u32x4 v, int valid_bytes) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int vb = valid_bytes - 4 * d;
+    const uint32_t m = vb >= 4 ? 0xffffffffu : (vb <= 0 ? 0u : ((1u << (8 * vb)) - 1u));
+    v[d] &= m;
+  }
+  return v;
+}
+
+// ---- the kernel ---------------------------------------------------------------
+
+template <class Op, int BP, int BQ, int WP, int WQ, bool P_TRANS>
+struct MfmaCfg {
+  static constexpr int NT = WP * WQ * 64;
+  static constexpr int E = Op::ELEM;
+  static constexpr int ROWB = 128;            // bytes of k per LDS row per stage
+  static constexpr int BK = ROWB / E;         // k per stage
+  static constexpr int CPE = 16 / E;          // elements per 16-byte chunk
+  static constexpr int P_LDS = BP * ROWB;
+  static constexpr int Q_LDS = BQ * ROWB;
+  static constexpr int STAGE = P_LDS + Q_LDS;
+  static constexpr int PCH = BP * (ROWB / 16) / NT;  // P chunks per thread per stage
+  static constexpr int QCH = BQ * (ROWB / 16) / NT;
+  static constexpr int WTP = BP / WP, WTQ = BQ / WQ;
+  static constexpr int TP = WTP / 32, TQ = WTQ / 32;
+  static constexpr int KSTEPS = BK / Op::KI;
+  static constexpr int PT_CPR = BP * E / 16;  // chunks per k-row of a p-contiguous P tile
+  static_assert(NT % 8 == 0, "thread count");
+  static_assert(BP * 8 % NT == 0 && BQ * 8 % NT == 0, "chunks divide over threads");
+  static_assert(WTP % 32 == 0 && WTQ % 32 == 0, "wave tile is whole 32x32 MFMA tiles");
+  static_assert(lds_bytes(BP, BQ, BK, E, 0, 2) <= kLdsLimit, "LDS budget");
+  static_assert(!P_TRANS || (BP * E) % 16 == 0, "p-contiguous chunks");
+};
+
+template <class Op, int BP, int BQ, int WP, int WQ, bool P_TRANS>
+__global__ void __launch_bounds__(WP * WQ * 64)
+gemm_mfma_kernel(const GemmArgs a) {
+  using Cfg = MfmaCfg<Op, BP, BQ, WP, WQ, P_TRANS>;
+  constexpr int NT = Cfg::NT, E = Cfg::E, ROWB = Cfg::ROWB, BK = Cfg::BK, CPE = Cfg::CPE;
+  constexpr int PCH = Cfg::PCH, QCH = Cfg::QCH, TP = Cfg::TP, TQ = Cfg::TQ, FC = Op::FC;
+
+  __shared__ __attribute__((aligned(1024))) char smem[2 * Cfg::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wp = wave / WQ, wq = wave % WQ;
+
+  int64_t tp, tq;
+  tile_map(a.tiles_p, a.tiles_q, a.group, blockIdx.x, &tp, &tq);
+  const int64_t p0 = tp * BP, q0 = tq * BQ;
+  const int64_t K = a.K;
+  const int nst = (int)((K + BK - 1) / BK);
+  const uint32_t kbytes16 = (uint32_t)(((K * E) + 15) & ~(int64_t)15);
+
+  // ---- loader set-up (stage-independent parts) ----
+  // K-contiguous tiles: chunk c = i*NT + tid -> row c/8, k-chunk c%8 (= tid%8).
+  const int kc = tid & 7;
+  const int lrow = tid >> 3;                       // row within the first NT/8 rows
+  const int sw_w = (lrow >> 1) & 7;                // swizzle key of that row (same for all i)
+  const uint32_t lds_kc = (uint32_t)(lrow * ROWB + ((kc ^ sw_w) << 4));
+
+  // Q (always K-contiguous).
+  const char* qblk = a.Q + q0 * a.ldq;
+  const int64_t qrows = (a.Qn - q0) < BQ ? (a.Qn - q0) : BQ;
+  const uint32_t qnrec = (uint32_t)((qrows - 1) * a.ldq) + kbytes16;
+  uint32_t qvo[QCH];
+#pragma unroll
+  for (int i = 0; i < QCH; ++i) {
+    const int row = i * (NT / 8) + lrow;
+    qvo[i] = (row < qrows) ? (uint32_t)(row * a.ldq + kc * 16) : kOobOffset;
+  }
+
+  // P.
+  const char* pblk;
+  uint32_t pnrec;
+  uint32_t pvo[PCH];
+  if constexpr (!P_TRANS) {
+    pblk = a.P + p0 * a.ldp;
+    const int64_t prows = (a.Pn - p0) < BP ? (a.Pn - p0) : BP;
+    pnrec = (uint32_t)((prows - 1) * a.ldp) + kbytes16;
+#pragma unroll
+    for (int i = 0; i < PCH; ++i) {
+      const int row = i * (NT / 8) + lrow;
+      pvo[i] = (row < prows) ? (uint32_t)(row * a.ldp + kc * 16) : kOobOffset;
+    }
+  } else {
+    // p-contiguous storage: chunk c -> k-row c / PT_CPR, p-chunk c % PT_CPR.
+    pblk = a.P + p0 * E;
+    const int64_t pcols = (a.Pn - p0) < BP ? (a.Pn - p0) : BP;
+    pnrec = (uint32_t)((K - 1) * a.ldp) + (uint32_t)(((pcols * E) + 15) & ~(int64_t)15);
+#pragma unroll
+    for (int i = 0; i < PCH; ++i) {
+      const int c = i * NT + tid;
+      const int krow = c / Cfg::PT_CPR, pc = c % Cfg::PT_CPR;
+      pvo[i] = (pc * CPE < pcols) ? (uint32_t)(krow * a.ldp + pc * 16) : kOobOffset;
+    }
+  }
+
+  u32x4 pst[PCH], qst[QCH];
+
+  auto load_stage = [&](int s, auto tail_tag) {
+    constexpr bool tail = decltype(tail_tag)::value;
+    {
+      const uint32_t adv = (uint32_t)s * ROWB;
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(qblk + adv, qnrec - adv);
+      const int64_t kst = (int64_t)s * BK + kc * CPE;   // first k of this thread's chunks
+#pragma unroll
+      for (int i = 0; i < QCH; ++i) {
+        uint32_t off = qvo[i];
+        if (tail && kst >= K) off = kOobOffset;
+        qst[i] = load16(r, off);
+        if (tail && kst + CPE > K) qst[i] = mask_tail(qst[i], (int)((K - kst) * E));
+      }
+    }
+    if constexpr (!P_TRANS) {
+      const uint32_t adv = (uint32_t)s * ROWB;
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(pblk + adv, pnrec - adv);
+      const int64_t kst = (int64_t)s * BK + kc * CPE;
+#pragma unroll
+      for (int i = 0; i < PCH; ++i) {
+        uint32_t off = pvo[i];
+        if (tail && kst >= K) off = kOobOffset;
+        pst[i] = load16(r, off);
+        if (tail && kst + CPE > K) pst[i] = mask_tail(pst[i], (int)((K - kst) * E));
+      }
+    } else {
+      const uint32_t adv = (uint32_t)((int64_t)s * BK * a.ldp);
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(pblk + (int64_t)s * BK * a.ldp, pnrec - adv);
+#pragma unroll
+      for (int i = 0; i < PCH; ++i) {
+        uint32_t off = pvo[i];
+        const int krow = (i * NT + tid) / Cfg::PT_CPR;
+        if (tail && (int64_t)s * BK + krow >= K) off = kOobOffset;
+        pst[i] = load16(r, off);
+      }
+    }
+  };
+
+  auto commit_stage = [&](int buf) {
+    char* sp = smem + buf * Cfg::STAGE;
+    char* sq = sp + Cfg::P_LDS;
+#pragma unroll
+    for (int i = 0; i < QCH; ++i) *(u32x4*)(sq + lds_kc + i * (NT / 8) * ROWB) = qst[i];
+    if constexpr (!P_TRANS) {
+#pragma unroll
+      for (int i = 0; i < PCH; ++i) *(u32x4*)(sp + lds_kc + i * (NT / 8) * ROWB) = pst[i];
+    } else {
+      // Transpose on the way in: element e of the chunk is P(p = pc*CPE + e, k = krow).
+#pragma unroll
+      for (int i = 0; i < PCH; ++i) {
+        const int c = i * NT + tid;
+        const int krow = c / Cfg::PT_CPR, pc = c % Cfg::PT_CPR;
+        const int kchunk = krow / CPE, kin = (krow % CPE) * E;
+#pragma unroll
+        for (int e = 0; e < CPE; ++e) {
+          const int p = pc * CPE + e;
+          char* dst = sp + p * ROWB + ((kchunk ^ ((p >> 1) & 7)) << 4) + kin;
+          const uint32_t w = pst[i][(e * E) >> 2];
+          if constexpr (E == 2) *(uint16_t*)dst = (uint16_t)(w >> (((e * E) & 3) * 8));
+          else *(uint8_t*)dst = (uint8_t)(w >> (((e * E) & 3) * 8));
+        }
+      }
+    }
+  };
+
+  // ---- fragment addressing ----
+  const int l32 = lane & 31, h = lane >> 5;
+  const int sw_r = (l32 >> 1) & 7;                 // swizzle key of every fragment row of this lane
+  const uint32_t pf_base = (uint32_t)((wp * Cfg::WTP + l32) * ROWB);
+  const uint32_t qf_base = (uint32_t)(Cfg::P_LDS + (wq * Cfg::WTQ + l32) * ROWB);
+
+  f32x16 acc[TP][TQ];
+#pragma unroll
+  for (int i = 0; i < TP; ++i)
+#pragma unroll
+    for (int j = 0; j < TQ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto compute_stage = [&](int buf) {
+    const char* sb = smem + buf * Cfg::STAGE;
+#pragma unroll
+    for (int kk = 0; kk < Cfg::KSTEPS; ++kk) {
+      uint32_t off[FC];
+#pragma unroll
+      for (int f = 0; f < FC; ++f) off[f] = (uint32_t)((((kk * 2 + h) * FC + f) ^ sw_r) << 4);
+      typename Op::Frag bf[TQ];
+#pragma unroll
+      for (int j = 0; j < TQ; ++j) bf[j] = Op::frag(sb + qf_base + j * 32 * ROWB, off);
+#pragma unroll
+      for (int i = 0; i < TP; ++i) {
+        const typename Op::Frag af = Op::frag(sb + pf_base + i * 32 * ROWB, off);
+#pragma unroll
+        for (int j = 0; j < TQ; ++j) acc[i][j] = Op::mma(af, bf[j], acc[i][j]);
+      }
+    }
+  };
+
+  // ---- pipeline ----
+  // Stage s is computed from buffer s % 2 while stage s + 1 is fetched into
+  // registers and then committed to the other buffer.  Only the last stage can
+  // be partial in K, so only its load carries the K-tail checks.
+  if (nst > 0) {
+    if (nst == 1) load_stage(0, std::true_type{});
+    else load_stage(0, std::false_type{});
+    commit_stage(0);
+    __syncthreads();
+    int s = 0;
+    for (; s < nst - 2; ++s) {
+      load_stage(s + 1, std::false_type{});
+      compute_stage(s & 1);
+      commit_stage((s + 1) & 1);
+      __syncthreads();
+    }
+    if (s < nst - 1) {
+      load_stage(s + 1, std::true_type{});
+      compute_stage(s & 1);
+      commit_stage((s + 1) & 1);
+      __syncthreads();
+      ++s;
+    }
+    compute_stage(s & 1);
+  }
+
+
+  // ---- epilogue: D[p][q] -> C[q*ldc + p] ----
+#pragma unroll
+  for (int i = 0; i < TP; ++i) {
+#pragma unroll
+    for (int j = 0; j < TQ; ++j) {
+      const int64_t q = q0 + wq * Cfg::WTQ + 32 * j + l32;
+      if (q >= a.Qn) continue;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t p = p0 + wp * Cfg::WTP + 32 * i + 8 * g + 4 * h;
+        const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+        if constexpr (Op::OE == 4) {
+          float* c = (float*)a.C + q * a.ldc + p;
+          if (a.vec_store && p + 3 < a.Pn) {
+            *(f32x4*)c = f32x4{v0, v1, v2, v3};
+          } else {
+            if (p + 0 < a.Pn) c[0] = v0;
+            if (p + 1 < a.Pn) c[1] = v1;
+            if (p + 2 < a.Pn) c[2] = v2;
+            if (p + 3 < a.Pn) c[3] = v3;
+          }
+        } else {
+          uint16_t* c = (uint16_t*)a.C + q * a.ldc + p;
+          if (a.vec_store && p + 3 < a.Pn) {
+            typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+            *(u32x2*)c = u32x2{Op::pack2(v0, v1), Op::pack2(v2, v3)};
+          } else {
+            if (p + 0 < a.Pn) c[0] = Op::one(v0);
+            if (p + 1 < a.Pn) c[1] = Op::one(v1);
+            if (p + 2 < a.Pn) c[2] = Op::one(v2);
+            if (p + 3 < a.Pn) c[3] = Op::one(v3);
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace dg

@@ -125,14 +125,15 @@ def make(dtype: str, layout: str, M: int, N: int, K: int, seed: int, dist: str,
                    meta={"seed": seed, "dist": dist})
 
 
-def identity(dtype: str, layout: str, n: int, A: np.ndarray, lda: int) -> Problem:
+def identity(dtype: str, layout: str, n: int, A: np.ndarray, lda: int, ldb: int | None = None) -> Problem:
     """B = I (K = N = n) with the given A: C must equal A exactly."""
     one = {"f32": np.float32(1.0).view(np.uint32), "f16": np.uint16(0x3c00),
            "bf16": np.uint16(0x3f80), "fp8": np.uint8(0x38)}[dtype]
-    B = np.zeros((n, n), dtype=_BITS[dtype])
+    ldb = n if ldb is None else ldb
+    B = np.zeros((n, ldb), dtype=_BITS[dtype])
     B[np.arange(n), np.arange(n)] = one
     lc = n if layout == "nn" else A.shape[0]
-    return Problem(dtype, layout, A.shape[0], n, n, A, B, lda, n, lc, name="identity")
+    return Problem(dtype, layout, A.shape[0], n, n, A, B, lda, ldb, lc, name="identity")
 
 
 # ---- the five workload families, with their seeds --------------------------

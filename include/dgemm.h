@@ -1,0 +1,119 @@
+/*
+ * dgemm.h -- C ABI of libdgemm.so: tiled dense GEMM C = A x B on MI355X (gfx950).
+ *
+ * Operation.  Every entry point computes C = A x B, C_ij = sum_k A_ik * B_kj,
+ * 2*M*N*K flops ("Optimizing GEMM in HIP", ROCm optimization guide, section
+ * "GEMM fundamentals"), with products and sums in FP32 (FP32 accumulation for
+ * every input format) and one conversion of each FP32 result to the output
+ * format with round-to-nearest-even.  C is overwritten (no alpha/beta).
+ *
+ * Layouts (leading dimensions are in ELEMENTS):
+ *   DGEMM_NN  A is M x K row-major       A(i,k) = A[i*lda + k],  lda >= K
+ *             B is K x N row-major       B(k,j) = B[k*ldb + j],  ldb >= N
+ *             C is M x N row-major       C(i,j) = C[i*ldc + j],  ldc >= N
+ *   DGEMM_TN  the pairing named TN in "FP16 GEMM Optimization on AMD RDNA 3
+ *             and RDNA 4", section "What We Are Computing": both operands
+ *             contiguous along K, C column-major.
+ *             A is M x K row-major       A(i,k) = A[i*lda + k],  lda >= K
+ *             B is K x N column-major    B(k,j) = B[j*ldb + k],  ldb >= K
+ *             C is M x N column-major    C(i,j) = C[j*ldc + i],  ldc >= M
+ *
+ * Formats: FP32 = IEEE binary32; FP16 = IEEE binary16 bits; BF16 = bfloat16
+ * bits; FP8 = OCP E4M3 ("E4M3FN": bias 7, max 448, no infinity) bytes, used
+ * raw with no scale factors ("FP8 GEMM Optimization on AMD RDNA 4", section
+ * "What Changes at FP8"), producing FP32 output.
+ *
+ * Memory and ownership.  A, B and C are DEVICE pointers owned by the caller;
+ * the library never allocates, frees or retains them and keeps no mutable
+ * global state, so calls are reentrant.  A and B must not overlap C.
+ * Alignment: A and B must be 16-byte aligned and lda*elem, ldb*elem must be
+ * multiples of 16 bytes (elem = bytes per input element); C needs only its
+ * element alignment (wider stores are used when C and ldc allow them).
+ * Size limits: the bytes one block tile addresses in an operand must stay
+ * below 2^31 (for a K-contiguous operand: 256 rows * ld * elem; for the NN
+ * B operand: K * ldb * elem); beyond that the call returns DGEMM_ERR_UNSUPPORTED.
+ *
+ * Streams.  The work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) and the call returns without synchronising.  Faults inside the
+ * kernel surface at the caller's next synchronisation.
+ *
+ * Errors.  Each call returns a dgemm_status and never prints or aborts.
+ * Checks, in this order: layout -> DGEMM_ERR_INVALID_LAYOUT; any of M, N, K
+ * negative -> DGEMM_ERR_INVALID_DIM; M == 0 or N == 0 -> DGEMM_OK with no
+ * work; a NULL A or B (when K > 0) or NULL C -> DGEMM_ERR_NULL_POINTER; a
+ * leading dimension below its minimum -> DGEMM_ERR_INVALID_LD; misaligned A
+ * or B base or pitch -> DGEMM_ERR_MISALIGNED; size limits ->
+ * DGEMM_ERR_UNSUPPORTED; a HIP launch error -> DGEMM_ERR_HIP.
+ * K == 0 is valid: C is filled with zeros (the empty sum).
+ */
+#ifndef DGEMM_H
+#define DGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DGEMM_NN = 0, DGEMM_TN = 1 } dgemm_layout;
+
+typedef enum {
+  DGEMM_OK = 0,
+  DGEMM_ERR_INVALID_DIM = 1,
+  DGEMM_ERR_NULL_POINTER = 2,
+  DGEMM_ERR_INVALID_LD = 3,
+  DGEMM_ERR_INVALID_LAYOUT = 4,
+  DGEMM_ERR_MISALIGNED = 5,
+  DGEMM_ERR_UNSUPPORTED = 6,
+  DGEMM_ERR_HIP = 7
+} dgemm_status;
+
+/* FP32 x FP32 -> FP32. */
+int gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+             const float* B, int64_t ldb, float* C, int64_t ldc, int layout, void* stream);
+
+/* FP16 x FP16 -> FP16 (binary16 bit patterns), FP32 accumulation. */
+int gemm_f16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+             const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc, int layout, void* stream);
+
+/* BF16 x BF16 -> BF16 (bfloat16 bit patterns), FP32 accumulation. */
+int gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+              const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc, int layout, void* stream);
+
+/* OCP FP8 E4M3 x E4M3 -> FP32, FP32 accumulation, no scale factors. */
+int gemm_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+             const uint8_t* B, int64_t ldb, float* C, int64_t ldc, int layout, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* gemm_strerror(int status);
+
+/*
+ * Host-side introspection (no GPU work; used by host-only tests and reports).
+ *
+ * dgemm_tile_map: the block -> output-tile mapping the kernels use, for a grid
+ * of tiles_p x tiles_q tiles, grouping `group` tiles along p ("FP16 GEMM
+ * Optimization on AMD RDNA 3 and RDNA 4", section "Step 6: Block Scheduling
+ * for Cache Reuse") after spreading consecutive tiles over the 8 XCDs.
+ * Writes the tile coordinates of block `pid`; returns 0, or -1 for pid out of
+ * range or non-positive sizes.
+ *
+ * dgemm_lds_bytes: LDS footprint (BM + BN) * (BK * elem + pad_bytes) * buffers
+ * of a block tile, the sizing rule behind the LDS tables of "FP16 GEMM
+ * Optimization on AMD RDNA 3 and RDNA 4" (Step 5, Table 9) and "FP8 GEMM
+ * Optimization on AMD RDNA 4" (Configs 1-4).  Returns -1 for negative inputs.
+ *
+ * dgemm_kernel_config: writes a one-line description (kernel name, tile, wave
+ * grid, LDS bytes, grid size) of the kernel a call with these arguments would
+ * launch into buf (at most len bytes, NUL-terminated).  dtype: 0 f32, 1 f16,
+ * 2 bf16, 3 fp8.  Returns 0, or a dgemm_status for invalid arguments.
+ */
+int dgemm_tile_map(int64_t tiles_p, int64_t tiles_q, int64_t group, int64_t pid,
+                   int64_t* tile_p, int64_t* tile_q);
+int64_t dgemm_lds_bytes(int bm, int bn, int bk, int elem, int pad_bytes, int buffers);
+int dgemm_kernel_config(int dtype, int layout, int64_t M, int64_t N, int64_t K, char* buf, int64_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DGEMM_H */

@@ -1,0 +1,172 @@
+"""GPU parity at sizes the oracle checks completely: every element of C from
+the HIP path against the CPU oracle, through the C ABI.
+
+Bars (per output format): bit-exact on +-1 and identity inputs; otherwise
+max |c - c_ref| / sum_k |a b| <= 1e-6 (FP32), 2^-10 (FP16), 2^-7 (BF16, FP8
+with FP32 output)."""
+
+import numpy as np
+import pytest
+
+from dense_gemm_02_amd import inputs
+from gpu_util import alloc_c, c_host, compare, pad_untouched, run_gpu, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DIST = {"f32": "uniform", "f16": "normal", "bf16": "normal", "fp8": "uniform4"}
+COMBOS = [("f32", "nn"), ("f32", "tn"), ("f16", "tn"), ("f16", "nn"), ("bf16", "tn"), ("bf16", "nn"),
+          ("fp8", "tn"), ("fp8", "nn")]
+
+# Edges of the block tiles (256 for 16/8-bit, 128 for FP32), the 32-wide MFMA
+# tiles, the K stage (64 / 128 / 32 elements) and the 16-byte chunk.
+EDGE = [1, 2, 3, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 70, 127, 128, 129, 255, 256, 257]
+
+
+def shapes_for(dtype, layout, n=28, seed=0):
+    rng = np.random.default_rng(seed + 7 * len(dtype) + (layout == "nn"))
+    out = [(1, 1, 1), (1, 1, 70), (70, 1, 1), (1, 70, 1), (257, 255, 129), (33, 65, 300)]
+    for _ in range(n):
+        out.append(tuple(int(rng.choice(EDGE)) for _ in range(3)))
+    return out
+
+
+def aligned_ld(n, dtype, extra=0):
+    al = {"f32": 4, "f16": 8, "bf16": 8, "fp8": 16}[dtype]
+    return ((max(n, 1) + al - 1) // al) * al + extra * al
+
+
+def make_problem(dtype, layout, M, N, K, seed, dist=None, pad=0):
+    la, lb, lc = inputs.min_ld(layout, M, N, K)
+    lda = aligned_ld(la, dtype, pad)
+    ldb = aligned_ld(lb, dtype, pad)
+    return inputs.make(dtype, layout, M, N, K, seed, dist or DIST[dtype], lda=lda, ldb=ldb, ldc=lc + pad)
+
+
+@pytest.mark.parametrize("dtype,layout", COMBOS)
+def test_small_shapes_against_oracle(dtype, layout):
+    for idx, (M, N, K) in enumerate(shapes_for(dtype, layout)):
+        p = make_problem(dtype, layout, M, N, K, seed=1000 + idx, pad=idx % 3)
+        say(f"case {dtype} {layout} M={M} N={N} K={K} lda={p.lda} ldb={p.ldb} ldc={p.ldc}")
+        C = run_gpu(p)
+        cij, pad = c_host(p, C)
+        assert pad_untouched(pad, dtype), "kernel wrote outside the C matrix"
+        ok, err, nbad = compare(p, cij)
+        assert ok, f"{dtype} {layout} {(M, N, K)}: max err {err:.3e}, {nbad} bad"
+
+
+@pytest.mark.parametrize("dtype,layout", COMBOS)
+def test_multi_tile_ragged(dtype, layout):
+    for idx, (M, N, K) in enumerate([(600, 520, 333), (515, 777, 1029), (1024, 256, 64)]):
+        p = make_problem(dtype, layout, M, N, K, seed=2000 + idx, pad=1)
+        say(f"case {dtype} {layout} M={M} N={N} K={K}")
+        cij, pad = c_host(p, run_gpu(p))
+        assert pad_untouched(pad, dtype)
+        ok, err, nbad = compare(p, cij)
+        assert ok, f"{dtype} {layout} {(M, N, K)}: max err {err:.3e}, {nbad} bad"
+
+
+@pytest.mark.parametrize("dtype,layout", COMBOS)
+def test_pm1_bit_exact(dtype, layout):
+    for idx, (M, N, K) in enumerate([(300, 260, 1000), (64, 64, 4096), (257, 129, 77)]):
+        p = make_problem(dtype, layout, M, N, K, seed=3000 + idx, dist="pm1")
+        say(f"case pm1 {dtype} {layout} M={M} N={N} K={K}")
+        cij, _ = c_host(p, run_gpu(p))
+        ok, _, nbad = compare(p, cij, exact=True)
+        assert ok, f"{nbad} elements differ"
+
+
+@pytest.mark.parametrize("dtype,layout", COMBOS)
+def test_identity_bit_exact(dtype, layout):
+    for n, M in ((256, 300), (100, 77)):
+        p0 = make_problem(dtype, layout, M, n, n, seed=4000 + n)
+        p = inputs.identity(dtype, layout, n, p0.A, p0.lda, ldb=aligned_ld(n, dtype))
+        say(f"case identity {dtype} {layout} M={M} n={n}")
+        cij, _ = c_host(p, run_gpu(p))
+        a = p0.A[:, :n]
+        if dtype == "fp8":
+            from gpu_util import oracle
+            assert np.array_equal(oracle.decode(oracle.F32, cij), oracle.decode(oracle.E4M3, a))
+        else:
+            from gpu_util import oracle
+            assert oracle.bits_equal(cij, a, {"f32": oracle.F32, "f16": oracle.F16, "bf16": oracle.BF16}[dtype])
+
+
+def _midpoint_problem(dtype, layout, seed):
+    """Columns whose exact (and FP32) sums land on, or just beside, rounding
+    midpoints of the output format: a = (1, 1, 1), b = (v, d, e) with v an
+    output value, d a half or one-and-a-half output ulp of v, e tiny or 0."""
+    import torch
+    rng = np.random.default_rng(seed)
+    N, K, M = 512, 3, 4
+    frac = 10 if dtype == "f16" else 7
+    e = rng.integers(-3, 6, N).astype(np.float64)     # keeps every term a normal number
+    mant = rng.integers(0, 1 << frac, N).astype(np.float64)
+    v = (1.0 + mant / 2.0 ** frac) * 2.0 ** e * rng.choice([-1.0, 1.0], N)
+    ulp = 2.0 ** (e - frac)
+    d = np.sign(v) * ulp * rng.choice([0.5, 1.5, -0.5], N)
+    tiny = np.where(rng.random(N) < 0.3, np.sign(v) * ulp * 2.0 ** -6 * rng.choice([-1.0, 1.0], N), 0.0)
+    bt = np.stack([v, d, tiny], axis=1)         # [N][K]
+    def enc(x):
+        if dtype == "f16":
+            return x.astype(np.float16).view(np.uint16)
+        return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    A = enc(np.ones((M, K)))
+    if layout == "tn":
+        B = enc(bt)
+    else:
+        B = enc(np.ascontiguousarray(bt.T))
+    la, lb, lc = inputs.min_ld(layout, M, N, K)
+    lda, ldb = aligned_ld(la, dtype), aligned_ld(lb, dtype)
+    Ap = np.zeros((M, lda), np.uint16); Ap[:, :K] = A
+    Bp = np.zeros((B.shape[0], ldb), np.uint16); Bp[:, :B.shape[1]] = B
+    return inputs.Problem(dtype, layout, M, N, K, Ap, Bp, lda, ldb, lc)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("layout", ["tn", "nn"])
+def test_epilogue_rounds_to_nearest_even(dtype, layout):
+    p = _midpoint_problem(dtype, layout, seed=5 + len(dtype))
+    cij, _ = c_host(p, run_gpu(p))
+    ok, _, nbad = compare(p, cij, exact=True)
+    assert ok, f"{nbad} outputs not rounded to nearest even"
+
+
+def test_k_zero_writes_zeros_and_empty_is_noop():
+    for dtype, layout in COMBOS:
+        p = make_problem(dtype, layout, 70, 90, 0, seed=1)
+        cij, pad = c_host(p, run_gpu(p))
+        assert np.all(cij == 0) and pad_untouched(pad, dtype)
+    # M = 0 / N = 0: nothing to write, the call must still succeed and touch nothing
+    import torch
+    from dense_gemm_02_amd import binding
+    p = make_problem("bf16", "tn", 16, 16, 16, seed=1)
+    A, B, C = to_dev(p.A), to_dev(p.B), alloc_c(p)
+    binding.gemm("bf16", "tn", 0, 16, 16, A, 16, B, 16, C, 16)
+    binding.gemm("bf16", "tn", 16, 0, 16, A, 16, B, 16, C, 16)
+    torch.cuda.synchronize()
+    assert bool((C == -1).all())
+
+
+def test_deterministic_and_stream_ordered():
+    import torch
+    p = make_problem("bf16", "tn", 1000, 1000, 2000, seed=9)
+    A, B = to_dev(p.A), to_dev(p.B)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        C1 = run_gpu(p, A=A, B=B, stream=s, sync=False)
+        C2 = run_gpu(p, A=A, B=B, stream=s, sync=False)
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2)
+    ok, err, _ = compare(p, c_host(p, C1)[0])
+    assert ok, err
+
+
+def test_odd_ldc_scalar_store_path():
+    for dtype in ("bf16", "f16", "fp8", "f32"):
+        p = make_problem(dtype, "tn", 301, 133, 200, seed=11)
+        p.ldc = 303        # odd: columns start at every alignment
+        cij, pad = c_host(p, run_gpu(p))
+        assert pad_untouched(pad, dtype)
+        ok, err, nbad = compare(p, cij)
+        assert ok, (dtype, err, nbad)
