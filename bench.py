@@ -144,6 +144,9 @@ def main():
     ap.add_argument("--dtype", default="f16", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", action="store_true", help="time only --dtype")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the GEMM, run a plain device copy of MIB MiB three times "
+                         "(reference dispatch for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -154,6 +157,15 @@ def main():
     from dense_gemm_02_amd import binding
     binding.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
+        return
 
     p, head = time_gemm(args.dtype, args.steps, args.warmup)
     print(f"[bench] {args.dtype}: {head['ms_per_launch']:.4f} ms/launch, {head['tflops']:.1f} TFLOP/s",

@@ -22,6 +22,11 @@ constexpr int kXcds = 8;
 // these kernels has num_records < 2^31, so this offset always reads zero.
 constexpr uint32_t kOobOffset = 0x80000000u;
 
+// s_waitcnt immediate that waits for vmcnt == 0 only (gfx9 encoding: vmcnt
+// bits [3:0] and [15:14] zero, expcnt [6:4] and lgkmcnt [11:8] at their
+// maxima).  Direct global -> LDS copies are counted by vmcnt.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // Raw (untyped, stride 0) buffer descriptor, word 3 of the gfx9-family
 // encoding (data format 32-bit; the RDNA word printed on the pages does not
 // apply to CDNA).  Loads at offsets >= num_records return zero instead of

@@ -7,7 +7,7 @@
 #include <stdint.h>
 #include <stdio.h>
 
-#include "../../include/dgemm.h"
+#include "dgemm.h"
 #include "common.hpp"
 #include "gemm_f32.hpp"
 #include "gemm_mfma.hpp"

@@ -217,15 +217,23 @@ gemm_f32_kernel(const GemmArgs a) {
     commit_stage(0);
     __syncthreads();
     int s = 0;
+    // The scheduling fences keep the next stage's global loads ahead of the
+    // MFMAs (so their latency hides behind a whole stage of math) and the LDS
+    // commit after them; left alone, the compiler sinks the loads to the
+    // commit to shorten register live ranges, exposing the full latency.
     for (; s < nst - 2; ++s) {
       load_stage(s + 1, std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);
       compute_stage(s & 1);
+      __builtin_amdgcn_sched_barrier(0);
       commit_stage((s + 1) & 1);
       __syncthreads();
     }
     if (s < nst - 1) {
       load_stage(s + 1, std::true_type{});
+      __builtin_amdgcn_sched_barrier(0);
       compute_stage(s & 1);
+      __builtin_amdgcn_sched_barrier(0);
       commit_stage((s + 1) & 1);
       __syncthreads();
       ++s;

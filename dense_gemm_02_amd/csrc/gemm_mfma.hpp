@@ -106,8 +106,7 @@ struct MfmaCfg {
   static constexpr int P_LDS = BP * ROWB;
   static constexpr int Q_LDS = BQ * ROWB;
   static constexpr int STAGE = P_LDS + Q_LDS;
-  static constexpr int PCH = BP * (ROWB / 16) / NT;  // P chunks per thread per stage
-  static constexpr int QCH = BQ * (ROWB / 16) / NT;
+  static constexpr int PCH = BP * (ROWB / 16) / NT;  // P chunks per thread per stage (staged path)
   static constexpr int WTP = BP / WP, WTQ = BQ / WQ;
   static constexpr int TP = WTP / 32, TQ = WTQ / 32;
   static constexpr int KSTEPS = BK / Op::KI;
@@ -124,7 +123,7 @@ __global__ void __launch_bounds__(WP * WQ * 64)
 gemm_mfma_kernel(const GemmArgs a) {
   using Cfg = MfmaCfg<Op, BP, BQ, WP, WQ, P_TRANS>;
   constexpr int NT = Cfg::NT, E = Cfg::E, ROWB = Cfg::ROWB, BK = Cfg::BK, CPE = Cfg::CPE;
-  constexpr int PCH = Cfg::PCH, QCH = Cfg::QCH, TP = Cfg::TP, TQ = Cfg::TQ, FC = Op::FC;
+  constexpr int PCH = Cfg::PCH, TP = Cfg::TP, TQ = Cfg::TQ, FC = Op::FC;
 
   __shared__ __attribute__((aligned(1024))) char smem[2 * Cfg::STAGE];
 
@@ -139,39 +138,51 @@ gemm_mfma_kernel(const GemmArgs a) {
   const int nst = (int)((K + BK - 1) / BK);
   const uint32_t kbytes16 = (uint32_t)(((K * E) + 15) & ~(int64_t)15);
 
-  // ---- loader set-up (stage-independent parts) ----
-  // K-contiguous tiles: chunk c = i*NT + tid -> row c/8, k-chunk c%8 (= tid%8).
-  const int kc = tid & 7;
-  const int lrow = tid >> 3;                       // row within the first NT/8 rows
-  const int sw_w = (lrow >> 1) & 7;                // swizzle key of that row (same for all i)
-  const uint32_t lds_kc = (uint32_t)(lrow * ROWB + ((kc ^ sw_w) << 4));
+  // ---- loaders ----
+  // K-contiguous tiles are copied global -> LDS directly (buffer_load ... lds,
+  // 16 bytes per lane on gfx950), so no registers stage them and no LDS store
+  // instructions are issued.  One wave instruction fills one 1 KiB LDS
+  // segment = 8 tile rows: lane l lands at byte 16*l, i.e. row 8*seg + l/8,
+  // physical chunk l%8.  That slot holds logical k-chunk (l%8) ^ key(row), so
+  // the swizzle is applied to the global address each lane fetches.  With
+  // row = 8*seg + l/8 and seg = i*NW + wave, key(row) = (row/2) mod 8 =
+  // (4*(wave%2) + l/16) mod 8 for every i (NW even).
+  constexpr int NW = NT / 64;
+  static_assert(NW % 2 == 0, "segment parity must follow the wave index");
+  constexpr int QSEG = BQ / 8 / NW;              // LDS segments per wave per stage
+  constexpr int PSEG = BP / 8 / NW;
+  static_assert(BQ % (8 * NW) == 0 && BP % (8 * NW) == 0, "segments divide over waves");
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int seg_row = lane >> 3;
+  const int dkc = (lane & 7) ^ ((4 * (wave_u & 1) + (lane >> 4)) & 7);
+  const int64_t dkst0 = (int64_t)dkc * CPE;      // first k of this lane's chunk within a stage
 
-  // Q (always K-contiguous).
   const char* qblk = a.Q + q0 * a.ldq;
   const int64_t qrows = (a.Qn - q0) < BQ ? (a.Qn - q0) : BQ;
   const uint32_t qnrec = (uint32_t)((qrows - 1) * a.ldq) + kbytes16;
-  uint32_t qvo[QCH];
+  uint32_t qvo[QSEG];
 #pragma unroll
-  for (int i = 0; i < QCH; ++i) {
-    const int row = i * (NT / 8) + lrow;
-    qvo[i] = (row < qrows) ? (uint32_t)(row * a.ldq + kc * 16) : kOobOffset;
+  for (int i = 0; i < QSEG; ++i) {
+    const int row = 8 * (i * NW + wave_u) + seg_row;
+    qvo[i] = (row < qrows) ? (uint32_t)(row * a.ldq + dkc * 16) : kOobOffset;
   }
 
-  // P.
+  // P: direct like Q, or (NN's B) p-contiguous rows staged through registers
+  // and transposed element by element into the K-contiguous LDS layout.
   const char* pblk;
   uint32_t pnrec;
-  uint32_t pvo[PCH];
+  uint32_t pvo[P_TRANS ? PCH : PSEG];
   if constexpr (!P_TRANS) {
     pblk = a.P + p0 * a.ldp;
     const int64_t prows = (a.Pn - p0) < BP ? (a.Pn - p0) : BP;
     pnrec = (uint32_t)((prows - 1) * a.ldp) + kbytes16;
 #pragma unroll
-    for (int i = 0; i < PCH; ++i) {
-      const int row = i * (NT / 8) + lrow;
-      pvo[i] = (row < prows) ? (uint32_t)(row * a.ldp + kc * 16) : kOobOffset;
+    for (int i = 0; i < PSEG; ++i) {
+      const int row = 8 * (i * NW + wave_u) + seg_row;
+      pvo[i] = (row < prows) ? (uint32_t)(row * a.ldp + dkc * 16) : kOobOffset;
     }
   } else {
-    // p-contiguous storage: chunk c -> k-row c / PT_CPR, p-chunk c % PT_CPR.
+    // chunk c = i*NT + tid -> k-row c / PT_CPR, p-chunk c % PT_CPR.
     pblk = a.P + p0 * E;
     const int64_t pcols = (a.Pn - p0) < BP ? (a.Pn - p0) : BP;
     pnrec = (uint32_t)((K - 1) * a.ldp) + (uint32_t)(((pcols * E) + 15) & ~(int64_t)15);
@@ -182,34 +193,41 @@ gemm_mfma_kernel(const GemmArgs a) {
       pvo[i] = (pc * CPE < pcols) ? (uint32_t)(krow * a.ldp + pc * 16) : kOobOffset;
     }
   }
+  u32x4 pst[P_TRANS ? PCH : 1];
 
-  u32x4 pst[PCH], qst[QCH];
+  // Issue the direct copies of one K-contiguous tile for stage s.  In the last
+  // stage, chunks that start at or past K are forced out of range (zeros).
+  auto direct_tile = [&](const char* blk, uint32_t nrec, const uint32_t* vo, int nseg, char* lds_tile, int s,
+                         bool tail) {
+    const uint32_t adv = (uint32_t)s * ROWB;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(blk + adv, nrec - adv);
+    const bool past_k = tail && ((int64_t)s * BK + dkst0 >= K);
+#pragma unroll
+    for (int i = 0; i < nseg; ++i) {
+      const uint32_t off = past_k ? kOobOffset : vo[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(lds_tile + (i * NW + wave_u) * 1024), 16, off, 0, 0, 0);
+    }
+  };
+  // After the copies have landed: zero the k >= K part of a chunk that
+  // straddles K (only when K is not a multiple of the chunk width).
+  auto fix_tail = [&](char* lds_tile, int nseg, int s) {
+    const int64_t kst = (int64_t)s * BK + dkst0;
+    if (kst < K && kst + CPE > K) {
+#pragma unroll
+      for (int i = 0; i < nseg; ++i) {
+        u32x4* c = (u32x4*)(lds_tile + (i * NW + wave_u) * 1024 + lane * 16);
+        *c = mask_tail(*c, (int)((K - kst) * E));
+      }
+    }
+  };
 
   auto load_stage = [&](int s, auto tail_tag) {
     constexpr bool tail = decltype(tail_tag)::value;
-    {
-      const uint32_t adv = (uint32_t)s * ROWB;
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(qblk + adv, qnrec - adv);
-      const int64_t kst = (int64_t)s * BK + kc * CPE;   // first k of this thread's chunks
-#pragma unroll
-      for (int i = 0; i < QCH; ++i) {
-        uint32_t off = qvo[i];
-        if (tail && kst >= K) off = kOobOffset;
-        qst[i] = load16(r, off);
-        if (tail && kst + CPE > K) qst[i] = mask_tail(qst[i], (int)((K - kst) * E));
-      }
-    }
+    char* sb = smem + (s & 1) * Cfg::STAGE;
+    direct_tile(qblk, qnrec, qvo, QSEG, sb + Cfg::P_LDS, s, tail);
     if constexpr (!P_TRANS) {
-      const uint32_t adv = (uint32_t)s * ROWB;
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(pblk + adv, pnrec - adv);
-      const int64_t kst = (int64_t)s * BK + kc * CPE;
-#pragma unroll
-      for (int i = 0; i < PCH; ++i) {
-        uint32_t off = pvo[i];
-        if (tail && kst >= K) off = kOobOffset;
-        pst[i] = load16(r, off);
-        if (tail && kst + CPE > K) pst[i] = mask_tail(pst[i], (int)((K - kst) * E));
-      }
+      direct_tile(pblk, pnrec, pvo, PSEG, sb, s, tail);
     } else {
       const uint32_t adv = (uint32_t)((int64_t)s * BK * a.ldp);
       const __amdgpu_buffer_rsrc_t r = make_rsrc(pblk + (int64_t)s * BK * a.ldp, pnrec - adv);
@@ -223,16 +241,13 @@ gemm_mfma_kernel(const GemmArgs a) {
     }
   };
 
-  auto commit_stage = [&](int buf) {
-    char* sp = smem + buf * Cfg::STAGE;
-    char* sq = sp + Cfg::P_LDS;
-#pragma unroll
-    for (int i = 0; i < QCH; ++i) *(u32x4*)(sq + lds_kc + i * (NT / 8) * ROWB) = qst[i];
-    if constexpr (!P_TRANS) {
-#pragma unroll
-      for (int i = 0; i < PCH; ++i) *(u32x4*)(sp + lds_kc + i * (NT / 8) * ROWB) = pst[i];
-    } else {
-      // Transpose on the way in: element e of the chunk is P(p = pc*CPE + e, k = krow).
+  // Completes stage s's copies: register-staged data is written (transposed),
+  // the direct copies are waited for, and the K tail is trimmed.  The caller
+  // follows with a barrier.
+  auto finish_stage = [&](int s, auto tail_tag) {
+    constexpr bool tail = decltype(tail_tag)::value;
+    char* sb = smem + (s & 1) * Cfg::STAGE;
+    if constexpr (P_TRANS) {
 #pragma unroll
       for (int i = 0; i < PCH; ++i) {
         const int c = i * NT + tid;
@@ -241,11 +256,18 @@ gemm_mfma_kernel(const GemmArgs a) {
 #pragma unroll
         for (int e = 0; e < CPE; ++e) {
           const int p = pc * CPE + e;
-          char* dst = sp + p * ROWB + ((kchunk ^ ((p >> 1) & 7)) << 4) + kin;
+          char* dst = sb + p * ROWB + ((kchunk ^ ((p >> 1) & 7)) << 4) + kin;
           const uint32_t w = pst[i][(e * E) >> 2];
           if constexpr (E == 2) *(uint16_t*)dst = (uint16_t)(w >> (((e * E) & 3) * 8));
           else *(uint8_t*)dst = (uint8_t)(w >> (((e * E) & 3) * 8));
         }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if constexpr (tail) {
+      if (K % CPE != 0) {
+        fix_tail(sb + Cfg::P_LDS, QSEG, s);
+        if constexpr (!P_TRANS) fix_tail(sb, PSEG, s);
       }
     }
   };
@@ -264,51 +286,81 @@ gemm_mfma_kernel(const GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  // One stage of MFMAs.  Fragments for k-step kk+1 are read from LDS while
+  // the MFMAs of k-step kk run (two register sets), and the scheduling
+  // groups interleave one LDS read after each MFMA so the reads' latency
+  // hides under matrix work instead of stalling the wave.
+  typedef typename Op::Frag Frag;
+  auto read_frags = [&](const char* sb, int kk, Frag (&af)[TP], Frag (&bf)[TQ]) {
+    uint32_t off[FC];
+#pragma unroll
+    for (int f = 0; f < FC; ++f) off[f] = (uint32_t)((((kk * 2 + h) * FC + f) ^ sw_r) << 4);
+#pragma unroll
+    for (int j = 0; j < TQ; ++j) bf[j] = Op::frag(sb + qf_base + j * 32 * ROWB, off);
+#pragma unroll
+    for (int i = 0; i < TP; ++i) af[i] = Op::frag(sb + pf_base + i * 32 * ROWB, off);
+  };
+  constexpr int NREAD = (TP + TQ) * FC;      // ds_read_b128 per k-step
+  constexpr int NMFMA = TP * TQ;             // MFMAs per k-step
   auto compute_stage = [&](int buf) {
     const char* sb = smem + buf * Cfg::STAGE;
+    Frag af[2][TP], bf[2][TQ];
+    read_frags(sb, 0, af[0], bf[0]);
 #pragma unroll
     for (int kk = 0; kk < Cfg::KSTEPS; ++kk) {
-      uint32_t off[FC];
+      const int cur = kk & 1;
+      if (kk + 1 < Cfg::KSTEPS) read_frags(sb, kk + 1, af[cur ^ 1], bf[cur ^ 1]);
 #pragma unroll
-      for (int f = 0; f < FC; ++f) off[f] = (uint32_t)((((kk * 2 + h) * FC + f) ^ sw_r) << 4);
-      typename Op::Frag bf[TQ];
+      for (int i = 0; i < TP; ++i)
 #pragma unroll
-      for (int j = 0; j < TQ; ++j) bf[j] = Op::frag(sb + qf_base + j * 32 * ROWB, off);
+        for (int j = 0; j < TQ; ++j) acc[i][j] = Op::mma(af[cur][i], bf[cur][j], acc[i][j]);
+    }
+    // Order: the first k-step's reads, then per k-step its MFMAs with the
+    // next k-step's reads threaded between them.
+    __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
 #pragma unroll
-      for (int i = 0; i < TP; ++i) {
-        const typename Op::Frag af = Op::frag(sb + pf_base + i * 32 * ROWB, off);
+    for (int kk = 0; kk < Cfg::KSTEPS; ++kk) {
+      if (kk + 1 < Cfg::KSTEPS) {
 #pragma unroll
-        for (int j = 0; j < TQ; ++j) acc[i][j] = Op::mma(af, bf[j], acc[i][j]);
+        for (int t = 0; t < NMFMA; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (t < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, NMFMA, 0);
       }
     }
   };
 
   // ---- pipeline ----
-  // Stage s is computed from buffer s % 2 while stage s + 1 is fetched into
-  // registers and then committed to the other buffer.  Only the last stage can
-  // be partial in K, so only its load carries the K-tail checks.
+  // Stage s is computed from LDS buffer s % 2 while the copies of stage s + 1
+  // land in the other buffer; one barrier per stage.  Only the last stage can
+  // be partial in K, so only it carries the K-tail checks.  The scheduling
+  // fences keep each stage's copies ahead of its MFMAs.
   if (nst > 0) {
-    if (nst == 1) load_stage(0, std::true_type{});
-    else load_stage(0, std::false_type{});
-    commit_stage(0);
+    if (nst == 1) { load_stage(0, std::true_type{}); finish_stage(0, std::true_type{}); }
+    else { load_stage(0, std::false_type{}); finish_stage(0, std::false_type{}); }
     __syncthreads();
     int s = 0;
     for (; s < nst - 2; ++s) {
       load_stage(s + 1, std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);
       compute_stage(s & 1);
-      commit_stage((s + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      finish_stage(s + 1, std::false_type{});
       __syncthreads();
     }
     if (s < nst - 1) {
       load_stage(s + 1, std::true_type{});
+      __builtin_amdgcn_sched_barrier(0);
       compute_stage(s & 1);
-      commit_stage((s + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      finish_stage(s + 1, std::true_type{});
       __syncthreads();
       ++s;
     }
     compute_stage(s & 1);
   }
-
 
   // ---- epilogue: D[p][q] -> C[q*ldc + p] ----
 #pragma unroll
