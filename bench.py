@@ -40,6 +40,21 @@ WORKLOADS = {
     "bf16": ("bf16", "tn", 8192, 8192, 8192, 4, "normal"),
     "fp8": ("fp8", "tn", 8192, 8192, 8192, 5, "uniform4"),
 }
+# Other workload configurations, timed with --workload (not part of the
+# default line).  The skinny BF16 case is HBM-bound: B is rotated over
+# ROTATE copies (> 256 MB Infinity Cache + L2) so each launch reads it from HBM.
+EXTRA = {
+    "bf16_tn_16x8192x8192": ("bf16", "tn", 16, 8192, 8192, 4, "normal"),
+    "bf16_tn_4096x14336x4096": ("bf16", "tn", 4096, 14336, 4096, 4, "normal"),
+    "bf16_tn_4096x4096x14336": ("bf16", "tn", 4096, 4096, 14336, 4, "normal"),
+    "bf16_tn_8191x8190x8200": ("bf16", "tn", 8191, 8190, 8200, 4, "normal"),
+    "fp8_tn_4096x14336x4096": ("fp8", "tn", 4096, 14336, 4096, 5, "uniform4"),
+    "fp8_tn_4096x4096x14336": ("fp8", "tn", 4096, 4096, 14336, 5, "uniform4"),
+    "fp8_tn_8192x28672x8192": ("fp8", "tn", 8192, 28672, 8192, 5, "uniform4"),
+    "f32_nn_4096x4096x4096": ("f32", "nn", 4096, 4096, 4096, 1, "uniform"),
+    "f32_nn_256x256x256": ("f32", "nn", 256, 256, 256, 0, "uniform"),
+}
+ROTATE = 4
 DTYPE_NAME = {"f16": "f16", "bf16": "bf16", "fp8": "fp8 (e4m3) x fp8 -> f32", "f32": "f32"}
 
 
@@ -67,10 +82,10 @@ def load_traffic(workload: str):
     return None if w is None else float(w["hbm_bytes_per_launch"])
 
 
-def make_inputs(dtype):
+def make_inputs(dtype, spec=None):
     import torch
     from dense_gemm_02_amd import inputs
-    dt, layout, M, N, K, seed, dist = WORKLOADS[dtype]
+    dt, layout, M, N, K, seed, dist = spec or WORKLOADS[dtype]
     p = inputs.make(dt, layout, M, N, K, seed, dist)
 
     def dev(x):
@@ -85,14 +100,18 @@ def make_inputs(dtype):
     return p, A, B, C
 
 
-def time_gemm(dtype, steps, warmup):
+def time_gemm(dtype, steps, warmup, spec=None, rotate=1):
     import torch
     from dense_gemm_02_amd import binding
-    p, A, B, C = make_inputs(dtype)
+    p, A, B, C = make_inputs(dtype, spec)
+    Bs = [B] + [B.clone() for _ in range(rotate - 1)]
     stream = torch.cuda.current_stream()
+    it = [0]
 
     def step():
-        binding.gemm(p.dtype, p.layout, p.M, p.N, p.K, A, p.lda, B, p.ldb, C, p.ldc, stream=stream)
+        b = Bs[it[0] % len(Bs)]
+        it[0] += 1
+        binding.gemm(p.dtype, p.layout, p.M, p.N, p.K, A, p.lda, b, p.ldb, C, p.ldc, stream=stream)
 
     for _ in range(warmup):
         step()
@@ -144,6 +163,8 @@ def main():
     ap.add_argument("--dtype", default="f16", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", action="store_true", help="time only --dtype")
+    ap.add_argument("--workload", default=None, choices=sorted(EXTRA),
+                    help="time one other workload configuration instead (prints its own line)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the GEMM, run a plain device copy of MIB MiB three times "
                          "(reference dispatch for the HBM byte counters)")
@@ -165,6 +186,24 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
+        return
+
+    if args.workload:
+        spec = EXTRA[args.workload]
+        skinny = spec[2] <= 32
+        p, r = time_gemm(spec[0], args.steps, args.warmup, spec=spec, rotate=ROTATE if skinny else 1)
+        out_b = 4 if spec[0] in ("f32", "fp8") else 2
+        in_b = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}[spec[0]]
+        nbytes = (p.M * p.K + p.N * p.K) * in_b + p.M * p.N * out_b
+        gbs = nbytes / (r["ms_per_launch"] * 1e-3) / 1e9
+        roof = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_GBS, "unit": "GB/s",
+                 "frac": round(gbs / HBM_GBS, 4), "traffic": load_traffic(args.workload)} if skinny else
+                {"bound": "mfma", "achieved": round(r["tflops"], 2), "peak": PEAK_TFLOPS[spec[0]], "unit": "TFLOP/s",
+                 "frac": round(r["tflops"] / PEAK_TFLOPS[spec[0]], 4), "traffic": load_traffic(args.workload)})
+        print(json.dumps({"workload": args.workload, "value": round(r["tflops"], 2), "unit": "TFLOP/s",
+                          "ms_per_launch": round(r["ms_per_launch"], 5), "steps": args.steps,
+                          "warmup": args.warmup, "rotated_B_copies": ROTATE if skinny else 1,
+                          "roofline": roof}), flush=True)
         return
 
     p, head = time_gemm(args.dtype, args.steps, args.warmup)

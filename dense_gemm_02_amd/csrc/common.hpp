@@ -26,6 +26,11 @@ constexpr uint32_t kOobOffset = 0x80000000u;
 // bits [3:0] and [15:14] zero, expcnt [6:4] and lgkmcnt [11:8] at their
 // maxima).  Direct global -> LDS copies are counted by vmcnt.
 constexpr int kWaitVmcnt0 = 0x0F70;
+// ... and for lgkmcnt == 0 only (vmcnt 63, expcnt 7).
+constexpr int kWaitLgkmcnt0 = 0xC07F;
+// vmcnt <= n: kWaitVmcntBase | vmcnt_bits(n), n in [0, 63].
+constexpr int kWaitVmcntBase = 0x0F70;
+constexpr int vmcnt_bits(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14); }
 
 // Raw (untyped, stride 0) buffer descriptor, word 3 of the gfx9-family
 // encoding (data format 32-bit; the RDNA word printed on the pages does not

@@ -11,6 +11,7 @@
 #include "common.hpp"
 #include "gemm_f32.hpp"
 #include "gemm_mfma.hpp"
+#include "gemm_skinny.hpp"
 
 namespace dg {
 namespace {
@@ -50,6 +51,23 @@ Launch f32_launch(const char* name) {
   return Launch{(const void*)&gemm_f32_kernel<128, 128, 2, 2, PT>, name, 128, 128, Cfg::NT, 2 * Cfg::STAGE, PT};
 }
 
+template <class Op, int PF>
+Launch skinny_launch(const char* name) {
+  return Launch{(const void*)&gemm_skinny_kernel<Op, PF>, name, 16 * PF, SkinnyCfg<Op, PF>::BQ, SkinnyCfg<Op, PF>::NT,
+                (int)(sizeof(float) * SkinnyCfg<Op, PF>::NW * 32 * SkinnyCfg<Op, PF>::BQ), false};
+}
+
+// Skinny TN problems (at most 32 rows of A) stream B once with a split-K
+// kernel; everything else uses the block-tiled kernels.
+bool use_skinny(int dt, int layout, int64_t M) {
+  return layout == DGEMM_TN && (dt == DT_F16 || dt == DT_BF16) && M <= 32;
+}
+
+Launch select_skinny(int dt, int64_t M) {
+  if (dt == DT_F16) return M <= 16 ? skinny_launch<OpF16, 1>("f16_tn_skinny16") : skinny_launch<OpF16, 2>("f16_tn_skinny32");
+  return M <= 16 ? skinny_launch<OpBF16, 1>("bf16_tn_skinny16") : skinny_launch<OpBF16, 2>("bf16_tn_skinny32");
+}
+
 Launch select(int dt, int layout) {
   const bool nn = layout == DGEMM_NN;
   switch (dt) {
@@ -84,7 +102,8 @@ int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
     return DGEMM_ERR_MISALIGNED;
   if (((uintptr_t)C) % (uintptr_t)out_elem(dt) != 0) return DGEMM_ERR_MISALIGNED;
 
-  Launch L = select(dt, layout);
+  const bool skinny = use_skinny(dt, layout, M);
+  Launch L = skinny ? select_skinny(dt, M) : select(dt, layout);
   GemmArgs g{};
   if (!nn) {
     g.P = (const char*)A; g.ldp = lda * e; g.Pn = M;
@@ -99,7 +118,7 @@ int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
   if (!L.p_trans && (int64_t)L.bp * g.ldp > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
   if (L.p_trans && K * g.ldp > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
   if (K * e > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
-  g.tiles_p = (g.Pn + L.bp - 1) / L.bp;
+  g.tiles_p = skinny ? 1 : (g.Pn + L.bp - 1) / L.bp;
   g.tiles_q = (g.Qn + L.bq - 1) / L.bq;
   g.group = 8;
   const int oe = out_elem(dt);

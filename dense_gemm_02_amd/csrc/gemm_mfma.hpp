@@ -94,6 +94,36 @@ __device__ __forceinline__ u32x4 mask_tail(u32x4 v, int valid_bytes) {
   return v;
 }
 
+// Store D[p..p+3][q] (four consecutive p of one accumulator column) at
+// C[q*ldc + p], converted to the output format with round-to-nearest-even.
+// One 8- or 16-byte store when C allows it, element stores at the p edge.
+template <class Op>
+__device__ __forceinline__ void store4(const GemmArgs& a, int64_t q, int64_t p, float v0, float v1, float v2,
+                                       float v3) {
+  if constexpr (Op::OE == 4) {
+    float* c = (float*)a.C + q * a.ldc + p;
+    if (a.vec_store && p + 3 < a.Pn) {
+      *(f32x4*)c = f32x4{v0, v1, v2, v3};
+    } else {
+      if (p + 0 < a.Pn) c[0] = v0;
+      if (p + 1 < a.Pn) c[1] = v1;
+      if (p + 2 < a.Pn) c[2] = v2;
+      if (p + 3 < a.Pn) c[3] = v3;
+    }
+  } else {
+    uint16_t* c = (uint16_t*)a.C + q * a.ldc + p;
+    if (a.vec_store && p + 3 < a.Pn) {
+      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+      *(u32x2*)c = u32x2{Op::pack2(v0, v1), Op::pack2(v2, v3)};
+    } else {
+      if (p + 0 < a.Pn) c[0] = Op::one(v0);
+      if (p + 1 < a.Pn) c[1] = Op::one(v1);
+      if (p + 2 < a.Pn) c[2] = Op::one(v2);
+      if (p + 3 < a.Pn) c[3] = Op::one(v3);
+    }
+  }
+}
+
 // ---- the kernel ---------------------------------------------------------------
 
 template <class Op, int BP, int BQ, int WP, int WQ, bool P_TRANS>
@@ -118,8 +148,14 @@ struct MfmaCfg {
   static_assert(!P_TRANS || (BP * E) % 16 == 0, "p-contiguous chunks");
 };
 
+// Waves per SIMD the kernel is compiled for: 8-wave blocks run two waves on
+// each SIMD (256 registers each); 4-wave blocks run one and may use all 512.
+template <int WAVES>
+constexpr int waves_per_simd() { return WAVES >= 8 ? 2 : 1; }
+
 template <class Op, int BP, int BQ, int WP, int WQ, bool P_TRANS>
 __global__ void __launch_bounds__(WP * WQ * 64)
+__attribute__((amdgpu_waves_per_eu(waves_per_simd<WP * WQ>(), waves_per_simd<WP * WQ>())))
 gemm_mfma_kernel(const GemmArgs a) {
   using Cfg = MfmaCfg<Op, BP, BQ, WP, WQ, P_TRANS>;
   constexpr int NT = Cfg::NT, E = Cfg::E, ROWB = Cfg::ROWB, BK = Cfg::BK, CPE = Cfg::CPE;
@@ -201,10 +237,12 @@ gemm_mfma_kernel(const GemmArgs a) {
                          bool tail) {
     const uint32_t adv = (uint32_t)s * ROWB;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(blk + adv, nrec - adv);
-    const bool past_k = tail && ((int64_t)s * BK + dkst0 >= K);
+    // Chunks starting at or past K read zero: setting bit 31 puts the offset
+    // beyond num_records (< 2^31) without a branch.
+    const uint32_t kill = (tail && ((int64_t)s * BK + dkst0 >= K)) ? kOobOffset : 0u;
 #pragma unroll
     for (int i = 0; i < nseg; ++i) {
-      const uint32_t off = past_k ? kOobOffset : vo[i];
+      const uint32_t off = vo[i] | kill;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           r, (__attribute__((address_space(3))) void*)(lds_tile + (i * NW + wave_u) * 1024), 16, off, 0, 0, 0);
     }
@@ -372,30 +410,8 @@ gemm_mfma_kernel(const GemmArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int64_t p = p0 + wp * Cfg::WTP + 32 * i + 8 * g + 4 * h;
-        const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
-        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-        if constexpr (Op::OE == 4) {
-          float* c = (float*)a.C + q * a.ldc + p;
-          if (a.vec_store && p + 3 < a.Pn) {
-            *(f32x4*)c = f32x4{v0, v1, v2, v3};
-          } else {
-            if (p + 0 < a.Pn) c[0] = v0;
-            if (p + 1 < a.Pn) c[1] = v1;
-            if (p + 2 < a.Pn) c[2] = v2;
-            if (p + 3 < a.Pn) c[3] = v3;
-          }
-        } else {
-          uint16_t* c = (uint16_t*)a.C + q * a.ldc + p;
-          if (a.vec_store && p + 3 < a.Pn) {
-            typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-            *(u32x2*)c = u32x2{Op::pack2(v0, v1), Op::pack2(v2, v3)};
-          } else {
-            if (p + 0 < a.Pn) c[0] = Op::one(v0);
-            if (p + 1 < a.Pn) c[1] = Op::one(v1);
-            if (p + 2 < a.Pn) c[2] = Op::one(v2);
-            if (p + 3 < a.Pn) c[3] = Op::one(v3);
-          }
-        }
+        store4<Op>(a, q, p, acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                   acc[i][j][4 * g + 3]);
       }
     }
   }

@@ -83,8 +83,10 @@ def test_argument_validation_order(lib, name, elem):
 
 def test_size_limits_unsupported(lib):
     # a K-contiguous operand whose 256-row block would span >= 2^31 bytes
+    # (M = 300 selects the block-tiled kernel; the call must be rejected
+    # before anything touches the fake pointers)
     big = (1 << 23) + 8
-    assert call(lib, "gemm_bf16", 4, 4, 8, FAKE, big, FAKE, 8, FAKE, 4, 1) == 6
+    assert call(lib, "gemm_bf16", 300, 4, 8, FAKE, big, FAKE, 8, FAKE, 300, 1) == 6
 
 
 def tile_map(lib, tp, tq, g, pid):

@@ -170,3 +170,22 @@ def test_odd_ldc_scalar_store_path():
         assert pad_untouched(pad, dtype)
         ok, err, nbad = compare(p, cij)
         assert ok, (dtype, err, nbad)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_skinny_split_k_path(dtype):
+    # TN with at most 32 rows of A runs the split-K skinny kernel: K is cut
+    # into 8 slices whose boundaries and tail chunks must all line up.
+    idx = 0
+    for M in (1, 5, 16, 17, 31, 32):
+        for N in (1, 33, 300):
+            for K in (1, 7, 8, 31, 33, 255, 1000, 2049):
+                p = make_problem(dtype, "tn", M, N, K, seed=6000 + idx, pad=idx % 2)
+                idx += 1
+                cij, pad = c_host(p, run_gpu(p))
+                assert pad_untouched(pad, dtype)
+                ok, err, nbad = compare(p, cij)
+                assert ok, f"{dtype} {(M, N, K)}: max err {err:.3e}, {nbad} bad"
+    p = make_problem(dtype, "tn", 16, 700, 4096, seed=7, dist="pm1")
+    cij, _ = c_host(p, run_gpu(p))
+    assert compare(p, cij, exact=True)[0]
