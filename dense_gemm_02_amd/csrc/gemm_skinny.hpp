@@ -48,7 +48,7 @@ struct SkinnyCfg {
   static constexpr int BQ = 32;                 // rows of B (columns of C) per workgroup
   static constexpr int QF = BQ / 16;            // 16-wide MFMA tiles along q
   static constexpr int KS = 32;                 // k per MFMA (16x16x32)
-  static constexpr int DEPTH = 8;               // k-steps of loads in flight per wave
+  static constexpr int DEPTH = PF == 1 ? 12 : 8; // k-steps of loads in flight per wave
   static constexpr int LPS = QF + PF;           // loads per k-step
   static constexpr int E = Op::ELEM;
   static_assert(Op::ELEM == 2, "16-bit operands");
@@ -64,6 +64,7 @@ gemm_skinny_kernel(const GemmArgs a) {
   constexpr int LPS = Cfg::LPS, CPE = 16 / E;
 
   __shared__ __attribute__((aligned(16))) float red[NW][32][BQ];
+  static_assert(BQ % 16 == 0, "whole 16-wide q tiles");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -92,9 +93,12 @@ gemm_skinny_kernel(const GemmArgs a) {
   const int nt = t1 - t0;
 
   u32x4 qb[DEPTH][QF], pb[DEPTH][PF];
+  // Step t of this wave (any t >= 0): loads for t >= nt or k >= K are pushed
+  // out of range and read zero, so the loop below needs no bounds branches
+  // (a branch would make every wait drain all loads in flight).
   auto issue = [&](int t, int slot) {
     const int64_t k = (int64_t)(t0 + t) * KS + kg * CPE;        // first k of this lane's chunk
-    const uint32_t kill = (k >= K) ? kOobOffset : 0u;
+    const uint32_t kill = (t >= nt || k >= K) ? kOobOffset : 0u;
     const uint32_t koff = (uint32_t)((t0 + t) * KS * E);
 #pragma unroll
     for (int j = 0; j < QF; ++j) qb[slot][j] = load16(rq, (qoff[j] + koff) | kill);
@@ -107,36 +111,35 @@ gemm_skinny_kernel(const GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < QF; ++j) acc[i][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
   auto consume = [&](int t, int slot) {
+    // Keep only the bytes below K: all 16 for a full chunk, none past K,
+    // the leading ones for a chunk that straddles K (computed, not branched).
     const int64_t k = (int64_t)(t0 + t) * KS + kg * CPE;
-    if (k < K && k + CPE > K) {                                  // chunk straddling K
+    const int64_t rem = K - k;
+    const int vb = rem >= CPE ? 16 : (rem <= 0 ? 0 : (int)rem * E);
 #pragma unroll
-      for (int j = 0; j < QF; ++j) qb[slot][j] = mask_tail(qb[slot][j], (int)((K - k) * E));
+    for (int j = 0; j < QF; ++j) qb[slot][j] = mask_tail(qb[slot][j], vb);
 #pragma unroll
-      for (int i = 0; i < PF; ++i) pb[slot][i] = mask_tail(pb[slot][i], (int)((K - k) * E));
-    }
+    for (int i = 0; i < PF; ++i) pb[slot][i] = mask_tail(pb[slot][i], vb);
 #pragma unroll
     for (int i = 0; i < PF; ++i)
 #pragma unroll
       for (int j = 0; j < QF; ++j) acc[i][j] = Mma16<Op>::mma(pb[slot][i], qb[slot][j], acc[i][j]);
   };
 
-  // Register ring of DEPTH k-steps: step t lives in slot t % DEPTH.
+  // Register ring of DEPTH k-steps: step t lives in slot t % DEPTH.  Every
+  // iteration issues one step, so exactly DEPTH - 1 later steps are in flight
+  // when a step is consumed (loads complete in issue order).
 #pragma unroll
-  for (int u = 0; u < DEPTH; ++u)
-    if (u < nt) issue(u, u);
+  for (int u = 0; u < DEPTH; ++u) issue(u, u);
   for (int t = 0; t < nt; t += DEPTH) {
 #pragma unroll
     for (int u = 0; u < DEPTH; ++u) {
-      if (t + u < nt) {
-        // Loads complete in issue order: the DEPTH-1 later steps may still be
-        // in flight, except near the end where fewer were issued.
-        if (t + u + DEPTH <= nt) __builtin_amdgcn_s_waitcnt(kWaitVmcntBase | vmcnt_bits((DEPTH - 1) * LPS));
-        else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        consume(t + u, u);
-        if (t + u + DEPTH < nt) issue(t + u + DEPTH, u);
-      }
+      __builtin_amdgcn_s_waitcnt(kWaitVmcntBase | vmcnt_bits((DEPTH - 1) * LPS));
+      consume(t + u, u);
+      issue(t + u + DEPTH, u);
     }
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // Cross-wave reduction.  16x16 accumulator layout: lane l holds column
   // (l % 16) and rows 4*(l/16) .. 4*(l/16)+3.
@@ -147,8 +150,8 @@ gemm_skinny_kernel(const GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) red[wave_u][16 * i + 4 * kg + r][16 * j + r16] = acc[i][j][r];
   __syncthreads();
-  // 512 threads cover the 32 x 32 (p, q) block twice; p is the fast index so
-  // a column of C is written contiguously.
+  // The threads sweep the 32 x BQ (p, q) block; p is the fast index so a
+  // column of C is written contiguously.
 #pragma unroll
   for (int e = tid; e < 32 * BQ; e += Cfg::NT) {
     const int p = e & 31, q = e >> 5;
