@@ -96,6 +96,7 @@ struct GemmArgs {
   int64_t Pn, Qn, K; // extents of p, q and k
   int64_t tiles_p, tiles_q, group;
   int vec_store;     // C and ldc allow 4-element vector stores
+  int vec16;         // C and ldc allow 16-byte stores
 };
 
 }  // namespace dg

@@ -68,7 +68,8 @@ Launch select_skinny(int dt, int64_t M) {
   return M <= 16 ? skinny_launch<OpBF16, 1>("bf16_tn_skinny16") : skinny_launch<OpBF16, 2>("bf16_tn_skinny32");
 }
 
-Launch select(int dt, int layout) {
+Launch select(int dt, int layout, int64_t K) {
+  (void)K;
   const bool nn = layout == DGEMM_NN;
   switch (dt) {
     case DT_F32:  return nn ? f32_launch<true>("f32_nn_128x128") : f32_launch<false>("f32_tn_128x128");
@@ -103,7 +104,7 @@ int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
   if (((uintptr_t)C) % (uintptr_t)out_elem(dt) != 0) return DGEMM_ERR_MISALIGNED;
 
   const bool skinny = use_skinny(dt, layout, M);
-  Launch L = skinny ? select_skinny(dt, M) : select(dt, layout);
+  Launch L = skinny ? select_skinny(dt, M) : select(dt, layout, K);
   GemmArgs g{};
   if (!nn) {
     g.P = (const char*)A; g.ldp = lda * e; g.Pn = M;
@@ -123,6 +124,7 @@ int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
   g.group = 8;
   const int oe = out_elem(dt);
   g.vec_store = ((((uintptr_t)C) % (uintptr_t)(4 * oe)) == 0 && ((ldc * oe) % (4 * oe)) == 0) ? 1 : 0;
+  g.vec16 = ((((uintptr_t)C) % 16) == 0 && ((ldc * oe) % 16) == 0) ? 1 : 0;
   out->L = L;
   out->g = g;
   out->grid = g.tiles_p * g.tiles_q;

@@ -52,6 +52,9 @@ struct OpF16 {
     return (uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16);
   }
   __device__ static uint16_t one(float x) { const _Float16 h = (_Float16)x; return __builtin_bit_cast(uint16_t, h); }
+  __device__ static f32x16 mma_parts(const u32x4 (&a)[1], const u32x4 (&b)[1], f32x16 c) {
+    return mma(__builtin_bit_cast(Frag, a[0]), __builtin_bit_cast(Frag, b[0]), c);
+  }
 };
 
 struct OpBF16 {
@@ -66,6 +69,9 @@ struct OpBF16 {
     return (uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16);
   }
   __device__ static uint16_t one(float x) { const __bf16 h = (__bf16)x; return __builtin_bit_cast(uint16_t, h); }
+  __device__ static f32x16 mma_parts(const u32x4 (&a)[1], const u32x4 (&b)[1], f32x16 c) {
+    return mma(__builtin_bit_cast(Frag, a[0]), __builtin_bit_cast(Frag, b[0]), c);
+  }
 };
 
 struct OpFP8 {
@@ -80,6 +86,13 @@ struct OpFP8 {
   // Formats 0/0 = E4M3 for both operands; scales 127 = 2^0 in E8M0.
   __device__ static f32x16 mma(Frag a, Frag b, f32x16 c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+  __device__ static f32x16 mma_parts(const u32x4 (&a)[2], const u32x4 (&b)[2], f32x16 c) {
+    const i32x8 av = __builtin_shufflevector(__builtin_bit_cast(i32x4, a[0]), __builtin_bit_cast(i32x4, a[1]), 0, 1,
+                                             2, 3, 4, 5, 6, 7);
+    const i32x8 bv = __builtin_shufflevector(__builtin_bit_cast(i32x4, b[0]), __builtin_bit_cast(i32x4, b[1]), 0, 1,
+                                             2, 3, 4, 5, 6, 7);
+    return mma(av, bv, c);
   }
 };
 
@@ -120,6 +133,82 @@ __device__ __forceinline__ void store4(const GemmArgs& a, int64_t q, int64_t p, 
       if (p + 1 < a.Pn) c[1] = Op::one(v1);
       if (p + 2 < a.Pn) c[2] = Op::one(v2);
       if (p + 3 < a.Pn) c[3] = Op::one(v3);
+    }
+  }
+}
+
+// Epilogue D[p][q] -> C[q*ldc + p] for one wave's WTP x WTQ tile, staged
+// through LDS.  Each lane holds four consecutive p of one q per accumulator
+// group, so a direct store writes 8 or 16 bytes into each of 32 different
+// columns of C.  Instead the wave converts its tile into its own LDS region
+// `reg` (WTQ rows of 256 bytes, [q][p]) and reads it back as 16-byte chunks:
+// one store instruction then covers four columns with 256 contiguous bytes
+// each ("An Educational GEMM Ladder for Helios GPUs", the LDS-staged
+// epilogue).  Slots of four p are XOR-swizzled by the row so that both the
+// scattered writes and the row-wise reads are free of bank conflicts.  FP32
+// output needs twice the space and goes in two passes over p.  The caller
+// makes sure no other wave still uses `reg`.
+template <class Op, int WTP, int WTQ, int TP, int TQ>
+__device__ __forceinline__ void staged_epilogue(const GemmArgs& a, char* reg, const f32x16 (&acc)[TP][TQ], int lane,
+                                                int64_t pbase, int64_t qbase) {
+  constexpr int OE = Op::OE;
+  constexpr int PASSES = OE == 4 ? 2 : 1;
+  constexpr int TPP = TP / PASSES;            // accumulator tiles along p per pass
+  constexpr int RB = TPP * 32 * OE;           // bytes of one staged row (one q)
+  constexpr int SS = 4 * OE;                  // bytes of one slot (four p)
+  constexpr int NSL = RB / SS;                // slots per row
+  constexpr int EPC = 16 / OE;                // elements per 16-byte chunk
+  static_assert(RB == 256, "staged rows are 256 bytes");
+  static_assert(WTQ % 4 == 0, "four rows per read-back instruction");
+  const int l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass) {
+#pragma unroll
+    for (int i = 0; i < TPP; ++i)
+#pragma unroll
+      for (int j = 0; j < TQ; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& v = acc[pass * TPP + i][j];
+          const int row = 32 * j + l32;
+          const int slot = (8 * i + 2 * g + h) ^ (row % NSL);
+          char* dst = reg + row * RB + slot * SS;
+          if constexpr (OE == 4) {
+            *(f32x4*)dst = f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+          } else {
+            typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+            *(u32x2*)dst = u32x2{Op::pack2(v[4 * g], v[4 * g + 1]), Op::pack2(v[4 * g + 2], v[4 * g + 3])};
+          }
+        }
+    const int m = lane & 15;                  // 16-byte chunk within a row
+#pragma unroll
+    for (int it = 0; it < WTQ / 4; ++it) {
+      const int row = 4 * it + (lane >> 4);
+      u32x4 d;
+      if constexpr (OE == 4) {
+        d = *(const u32x4*)(reg + row * RB + ((m ^ (row % NSL)) * 16));
+      } else {
+        // Chunk m holds slots 2m and 2m+1, which the swizzle keeps in one
+        // aligned pair but swaps when the key is odd.
+        const int key = row % NSL;
+        const u32x4 raw = *(const u32x4*)(reg + row * RB + ((((2 * m) ^ key) & ~1) * SS));
+        d = (key & 1) ? u32x4{raw[2], raw[3], raw[0], raw[1]} : raw;
+      }
+      const int64_t q = qbase + row;
+      const int64_t p = pbase + pass * TPP * 32 + m * EPC;
+      if (q >= a.Qn) continue;
+      char* c = (char*)a.C + (q * a.ldc + p) * OE;
+      if (a.vec16 && p + EPC <= a.Pn) {
+        *(u32x4*)c = d;
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          if (p + e < a.Pn) {
+            if constexpr (OE == 4) ((uint32_t*)c)[e] = d[e];
+            else ((uint16_t*)c)[e] = (uint16_t)(d[e >> 1] >> ((e & 1) * 16));
+          }
+        }
+      }
     }
   }
 }
@@ -192,6 +281,7 @@ gemm_mfma_kernel(const GemmArgs a) {
   const int seg_row = lane >> 3;
   const int dkc = (lane & 7) ^ ((4 * (wave_u & 1) + (lane >> 4)) & 7);
   const int64_t dkst0 = (int64_t)dkc * CPE;      // first k of this lane's chunk within a stage
+  const int dkst0_32 = dkc * CPE;
 
   const char* qblk = a.Q + q0 * a.ldq;
   const int64_t qrows = (a.Qn - q0) < BQ ? (a.Qn - q0) : BQ;
@@ -236,10 +326,17 @@ gemm_mfma_kernel(const GemmArgs a) {
   auto direct_tile = [&](const char* blk, uint32_t nrec, const uint32_t* vo, int nseg, char* lds_tile, int s,
                          bool tail) {
     const uint32_t adv = (uint32_t)s * ROWB;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(blk + adv, nrec - adv);
+    // (readfirstlane keeps the clamped count in a scalar register: a vector
+    // select here would force a per-lane loop around every copy.)
+    const uint32_t left = (uint32_t)__builtin_amdgcn_readfirstlane((int)(adv < nrec ? nrec - adv : 0u));
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(blk + adv, left);
     // Chunks starting at or past K read zero: setting bit 31 puts the offset
-    // beyond num_records (< 2^31) without a branch.
-    const uint32_t kill = (tail && ((int64_t)s * BK + dkst0 >= K)) ? kOobOffset : 0u;
+    // beyond num_records (< 2^31) without a branch.  Stages past the last one
+    // (issued by the pipeline below to keep its loop branch-free) read zero
+    // throughout.
+    const int64_t rem64 = K - (int64_t)s * BK;
+    const int rem = (int)(rem64 < BK ? rem64 : BK);   // k left from this stage's start, at most BK
+    const uint32_t kill = (tail && dkst0_32 >= rem) ? kOobOffset : 0u;
 #pragma unroll
     for (int i = 0; i < nseg; ++i) {
       const uint32_t off = vo[i] | kill;
@@ -370,12 +467,154 @@ gemm_mfma_kernel(const GemmArgs a) {
     }
   };
 
-  // ---- pipeline ----
-  // Stage s is computed from LDS buffer s % 2 while the copies of stage s + 1
-  // land in the other buffer; one barrier per stage.  Only the last stage can
-  // be partial in K, so only it carries the K-tail checks.  The scheduling
-  // fences keep each stage's copies ahead of its MFMAs.
-  if (nst > 0) {
+  // ---- pipeline (K-contiguous P: both tiles copied directly) ----
+  // Stage s is computed from LDS buffer s % 2.  The one barrier per stage sits
+  // before the stage's last k-step: by then every wave holds that k-step's
+  // fragments in registers (so buffer s % 2 is free) and has waited for its
+  // own copies of stage s + 1.  After the barrier the wave reads stage s + 1's
+  // first fragments and starts copying stage s + 2 into buffer s % 2 while the
+  // last k-step's MFMAs run, so no MFMA waits on an LDS read at a stage
+  // boundary.
+  //
+  // The instruction order is spelled out slot by slot (one MFMA, then the LDS
+  // reads and copies assigned to that slot) and pinned with scheduling
+  // fences: copies issued in a burst fill the texture unit's queue and stall
+  // the issuing wave, MFMAs included, so they are spread one per MFMA slot.
+  if constexpr (!P_TRANS) {
+    constexpr int NDMA = QSEG + PSEG;          // copy instructions per wave per stage
+    static_assert(NDMA <= 31, "vmcnt range");
+    const bool ragged = (K % CPE) != 0;
+    // Copies of one tile for stage t: a descriptor advanced to the stage, and
+    // a kill bit for chunks at or past K (bit 31 puts the offset beyond
+    // num_records < 2^31, so the lane reads zero without a branch).  Stages
+    // past the last one read zero throughout.
+    auto copy_rsrc = [&](const char* blk, uint32_t nrec, int t) {
+      const uint32_t adv = (uint32_t)t * ROWB;
+      // (readfirstlane keeps the clamped count in a scalar register: a
+      // vector select here would force a per-lane loop around every copy.)
+      const uint32_t left = (uint32_t)__builtin_amdgcn_readfirstlane((int)(adv < nrec ? nrec - adv : 0u));
+      return make_rsrc(blk + adv, left);
+    };
+    auto copy_kill = [&](int t) {
+      const int64_t rem64 = K - (int64_t)t * BK;
+      const int rem = (int)(rem64 < BK ? rem64 : BK);
+      return dkst0_32 >= rem ? kOobOffset : 0u;
+    };
+    auto copy_one = [&](__amdgpu_buffer_rsrc_t r, uint32_t kill, const uint32_t* vo, char* lds_tile, int i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(lds_tile + (i * NW + wave_u) * 1024), 16, vo[i] | kill, 0, 0,
+          0);
+    };
+    // Copy instruction d of a stage: Q segments first, then P segments.
+    auto copy_d = [&](__amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rp, uint32_t kill, char* stage_lds, int d) {
+      if (d < QSEG) copy_one(rq, kill, qvo, stage_lds + Cfg::P_LDS, d);
+      else copy_one(rp, kill, pvo, stage_lds, d - QSEG);
+    };
+    auto trim = [&](int t, int b) {
+      char* sb = smem + b * Cfg::STAGE;
+      fix_tail(sb + Cfg::P_LDS, QSEG, t);
+      fix_tail(sb, PSEG, t);
+    };
+    // Fragments as 16-byte parts: [set][tile][part].
+    u32x4 fa[2][TP][FC], fb[2][TQ][FC];
+    // LDS read r of a k-step: B tiles first, then A tiles, FC parts each.
+    auto read_one = [&](const char* sb, int kk, int set, int r) {
+      const bool isb = r < TQ * FC;
+      const int rr = isb ? r : r - TQ * FC;
+      const int tile = rr / FC, f = rr % FC;
+      const uint32_t off = (uint32_t)((((kk * 2 + h) * FC + f) ^ sw_r) << 4);
+      const char* base = sb + (isb ? qf_base + tile * 32 * ROWB : pf_base + tile * 32 * ROWB);
+      const u32x4 v = *(const u32x4*)(base + off);
+      if (isb) fb[set][tile][f] = v; else fa[set][tile][f] = v;
+    };
+    auto mfma_one = [&](int set, int t) {
+      const int i = t / TQ, j = t % TQ;
+      acc[i][j] = Op::mma_parts(fa[set][i], fb[set][j], acc[i][j]);
+    };
+    // Slot of read r when NREAD reads are spread over `span` MFMA slots.
+    auto read_slot = [](int r, int span) { return r * span / NREAD; };
+    constexpr int LAST = (Cfg::KSTEPS - 1) & 1;        // fragment set of the last k-step
+    // Two stages per loop trip (fixed buffer offsets) where the registers
+    // allow it; FP8's 32-byte fragments leave no room for the extra
+    // loop-invariant addresses, so it selects the buffer at run time.
+    constexpr bool UNROLL2 = Op::FC == 1;
+    // B is the buffer index when it is known at compile time (-1: s % 2).
+    auto stage = [&](int s, auto buf) {
+      constexpr int B = decltype(buf)::value;
+      const int b = B >= 0 ? B : (s & 1);
+      const char* sb = smem + b * Cfg::STAGE;
+      // A ragged last stage is trimmed in LDS by each wave once its own
+      // copies have landed (once per tile, and only when K is not a multiple
+      // of the chunk width; the barrier below publishes it).  The branch sits
+      // ahead of the MFMAs so they stay in one block with the barrier.
+      if (ragged && s + 2 == nst) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        trim(s + 1, b ^ 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // k-steps before the barrier; the reads feeding the last of them are
+      // packed into the first half of their slots so they complete before it.
+#pragma unroll
+      for (int kk = 0; kk + 1 < Cfg::KSTEPS; ++kk) {
+        const int span = kk + 2 == Cfg::KSTEPS ? NMFMA / 2 : NMFMA;
+#pragma unroll
+        for (int t = 0; t < NMFMA; ++t) {
+          mfma_one(kk & 1, t);
+#pragma unroll
+          for (int r = 0; r < NREAD; ++r)
+            if (read_slot(r, span) == t) read_one(sb, kk + 1, (kk + 1) & 1, r);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      // Last k-step: next stage's first fragments, copies of stage s + 2.
+      const char* nb = smem + (b ^ 1) * Cfg::STAGE;
+      char* db = smem + b * Cfg::STAGE;
+      const __amdgpu_buffer_rsrc_t rq = copy_rsrc(qblk, qnrec, s + 2), rp = copy_rsrc(pblk, pnrec, s + 2);
+      const uint32_t kill = copy_kill(s + 2);
+#pragma unroll
+      for (int t = 0; t < NMFMA; ++t) {
+        mfma_one(LAST, t);
+#pragma unroll
+        for (int r = 0; r < NREAD; ++r)
+          if (read_slot(r, NMFMA) == t) read_one(nb, 0, 0, r);
+#pragma unroll
+        for (int d = 0; d < NDMA; ++d)
+          if (d * NMFMA / NDMA == t) copy_d(rq, rp, kill, db, d);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if (nst > 0) {
+      {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const __amdgpu_buffer_rsrc_t rq = copy_rsrc(qblk, qnrec, t), rp = copy_rsrc(pblk, pnrec, t);
+          const uint32_t kill = copy_kill(t);
+#pragma unroll
+          for (int d = 0; d < NDMA; ++d) copy_d(rq, rp, kill, smem + t * Cfg::STAGE, d);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitVmcntBase | vmcnt_bits(NDMA));
+      if (ragged && nst == 1) trim(0, 0);
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < NREAD; ++r) read_one(smem, 0, 0, r);
+      if constexpr (UNROLL2) {
+        int s = 0;
+        for (; s + 1 < nst; s += 2) {
+          stage(s, std::integral_constant<int, 0>{});
+          stage(s + 1, std::integral_constant<int, 1>{});
+        }
+        if (s < nst) stage(s, std::integral_constant<int, 0>{});
+      } else {
+        for (int s = 0; s < nst; ++s) stage(s, std::integral_constant<int, -1>{});
+      }
+      // Copies of the two stages past the end are still in flight.
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
+  } else if (nst > 0) {
     if (nst == 1) { load_stage(0, std::true_type{}); finish_stage(0, std::true_type{}); }
     else { load_stage(0, std::false_type{}); finish_stage(0, std::false_type{}); }
     __syncthreads();
@@ -400,20 +639,14 @@ gemm_mfma_kernel(const GemmArgs a) {
     compute_stage(s & 1);
   }
 
-  // ---- epilogue: D[p][q] -> C[q*ldc + p] ----
-#pragma unroll
-  for (int i = 0; i < TP; ++i) {
-#pragma unroll
-    for (int j = 0; j < TQ; ++j) {
-      const int64_t q = q0 + wq * Cfg::WTQ + 32 * j + l32;
-      if (q >= a.Qn) continue;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t p = p0 + wp * Cfg::WTP + 32 * i + 8 * g + 4 * h;
-        store4<Op>(a, q, p, acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                   acc[i][j][4 * g + 3]);
-      }
-    }
+  // ---- epilogue ----
+  {
+    static_assert(Cfg::WTQ * 256 * NW <= 2 * Cfg::STAGE, "staging fits in the stage buffers");
+    // Every copy has landed and every wave is done with the stage buffers.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    staged_epilogue<Op, Cfg::WTP, Cfg::WTQ, TP, TQ>(a, smem + wave_u * (Cfg::WTQ * 256), acc, lane,
+                                                     p0 + wp * Cfg::WTP, q0 + wq * Cfg::WTQ);
   }
 }
 
