@@ -12,6 +12,7 @@
 #include "gemm_f32.hpp"
 #include "gemm_mfma.hpp"
 #include "gemm_skinny.hpp"
+#include "gemm_tn.hpp"
 
 namespace dg {
 namespace {
@@ -24,11 +25,13 @@ int in_elem(int dt) { return dt == DT_F32 ? 4 : (dt == DT_FP8 ? 1 : 2); }
 int out_elem(int dt) { return (dt == DT_F32 || dt == DT_FP8) ? 4 : 2; }
 
 // A launchable configuration: a kernel symbol plus its tile geometry.
+// Persistent kernels run at most one workgroup per CU and walk the tiles.
 struct Launch {
   const void* fn;
   const char* name;
   int bp, bq, threads, lds;
   bool p_trans;
+  bool persistent;
 };
 
 // ---- kernel table ------------------------------------------------------------
@@ -42,19 +45,30 @@ template <class Op, bool PT>
 Launch mfma_launch(const char* name) {
   using Cfg = MfmaCfg<Op, 256, 256, 2, 4, PT>;
   return Launch{(const void*)&gemm_mfma_kernel<Op, 256, 256, 2, 4, PT>, name, 256, 256, Cfg::NT,
-                2 * Cfg::STAGE, PT};
+                2 * Cfg::STAGE, PT, false};
+}
+
+// Four-wave 256 x 256 TN kernel.  FP16/BF16 run one tile per workgroup with
+// the LDS-staged epilogue; FP8, whose FP32 output is twice as large, runs
+// persistently so that each tile's stores drain under the next tile's stages.
+template <class Op>
+Launch tn_launch(const char* name) {
+  using Cfg = TnCfg<Op>;
+  constexpr bool P = Op::ELEM == 1;
+  return Launch{(const void*)&gemm_tn_kernel<Op, P>, name, Cfg::BP, Cfg::BQ, Cfg::NT, 2 * Cfg::STAGE, false, P};
 }
 
 template <bool PT>
 Launch f32_launch(const char* name) {
   using Cfg = F32Cfg<128, 128, 2, 2, PT>;
-  return Launch{(const void*)&gemm_f32_kernel<128, 128, 2, 2, PT>, name, 128, 128, Cfg::NT, 2 * Cfg::STAGE, PT};
+  return Launch{(const void*)&gemm_f32_kernel<128, 128, 2, 2, PT>, name, 128, 128, Cfg::NT, 2 * Cfg::STAGE, PT,
+                false};
 }
 
 template <class Op, int PF>
 Launch skinny_launch(const char* name) {
   return Launch{(const void*)&gemm_skinny_kernel<Op, PF>, name, 16 * PF, SkinnyCfg<Op, PF>::BQ, SkinnyCfg<Op, PF>::NT,
-                (int)(sizeof(float) * SkinnyCfg<Op, PF>::NW * 32 * SkinnyCfg<Op, PF>::BQ), false};
+                (int)(sizeof(float) * SkinnyCfg<Op, PF>::NW * 32 * SkinnyCfg<Op, PF>::BQ), false, false};
 }
 
 // Skinny TN problems (at most 32 rows of A) stream B once with a split-K
@@ -69,8 +83,19 @@ Launch select_skinny(int dt, int64_t M) {
 }
 
 Launch select(int dt, int layout, int64_t K) {
-  (void)K;
   const bool nn = layout == DGEMM_NN;
+  // TN with K a whole number of 16-byte chunks and at least two stages: the
+  // four-wave kernel (gemm_tn.hpp).
+  if (!nn && dt != DT_F32) {
+    const int e = in_elem(dt);
+    if (K % (16 / e) == 0 && K >= 2 * (128 / e)) {
+      switch (dt) {
+        case DT_F16: return tn_launch<OpF16>("f16_tn_256x256_w4");
+        case DT_BF16: return tn_launch<OpBF16>("bf16_tn_256x256_w4");
+        default: return tn_launch<OpFP8>("fp8_tn_256x256_w4_persistent");
+      }
+    }
+  }
   switch (dt) {
     case DT_F32:  return nn ? f32_launch<true>("f32_nn_128x128") : f32_launch<false>("f32_tn_128x128");
     case DT_F16:  return nn ? mfma_launch<OpF16, true>("f16_nn_256x256") : mfma_launch<OpF16, false>("f16_tn_256x256");
@@ -137,6 +162,16 @@ int run(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
   Plan pl;
   const int st = plan(dt, M, N, K, A, lda, B, ldb, C, ldc, layout, &pl, true);
   if (st != DGEMM_OK || pl.grid == 0) return st;
+  if (pl.L.persistent) {
+    // One workgroup per CU, rounded down to a multiple of the XCD count so
+    // that every tile of a workgroup maps to the workgroup's own XCD.
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return DGEMM_ERR_HIP;
+    if (cus >= kXcds) cus -= cus % kXcds;
+    if (pl.grid > cus) pl.grid = cus;
+  }
   void* args[] = {(void*)&pl.g};
   const hipError_t err = hipLaunchKernel(pl.L.fn, dim3((unsigned)pl.grid), dim3(pl.L.threads), args, 0,
                                          (hipStream_t)stream);

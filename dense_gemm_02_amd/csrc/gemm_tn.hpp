@@ -1,0 +1,298 @@
+// Persistent TN GEMM for 16-bit and 8-bit operands on gfx950: four waves,
+// one per SIMD, each owning a 128 x 128 quarter of a 256 x 256 tile.
+//
+// Same operation and P/Q/D mapping as gemm_mfma.hpp (D[p][q] = sum_k
+// P(p,k) Q(q,k), stored at C[q*ldc + p]), for K-contiguous P and Q, K a whole
+// number of 16-byte chunks and at least two stages.  Differences:
+//
+//  * 128 x 128 wave tiles read 0.5 KiB of LDS per 32x32 MFMA instead of 0.75
+//    for the eight-wave 128 x 64 split, and one wave per SIMD leaves all 512
+//    registers to it (accumulators in AGPRs).
+//  * The grid is one workgroup per CU; each walks tiles blockIdx.x,
+//    blockIdx.x + gridDim.x, ...  The copy stream runs on across tiles: the
+//    last stages of a tile already copy and read the first stages of the next
+//    one, so a tile's epilogue stores drain while the next tile computes, and
+//    no tile starts with an exposed copy latency.  (With the grid a multiple
+//    of 8, every tile of a workgroup lies on the workgroup's XCD.)
+//  * Copies of a stage are split: NA go out right after the barrier two
+//    stages ahead, the other NDMA - NA over the first KB k-steps of the stage
+//    before, so the texture unit sees them spread out.
+#pragma once
+
+#include <type_traits>
+
+#include "common.hpp"
+#include "gemm_mfma.hpp"
+
+namespace dg {
+
+template <class Op>
+struct TnCfg {
+  static constexpr int BP = 256, BQ = 256, WP = 2, WQ = 2, NW = 4, NT = 256;
+  static constexpr int E = Op::ELEM, FC = Op::FC;
+  static constexpr int ROWB = 128;                // bytes of k per LDS row per stage
+  static constexpr int BK = ROWB / E;             // k per stage
+  static constexpr int CPE = 16 / E;              // elements per 16-byte chunk
+  static constexpr int P_LDS = BP * ROWB;
+  static constexpr int STAGE = (BP + BQ) * ROWB;  // 64 KiB
+  static constexpr int QSEG = BQ / 8 / NW, PSEG = BP / 8 / NW;
+  static constexpr int NDMA = QSEG + PSEG;        // copy instructions per wave per stage
+  static constexpr int WTP = BP / WP, WTQ = BQ / WQ;
+  static constexpr int TP = WTP / 32, TQ = WTQ / 32;
+  static constexpr int KSTEPS = BK / Op::KI;
+  static constexpr int NREAD = (TP + TQ) * FC;    // 16-byte LDS reads per k-step
+  static constexpr int NMFMA = TP * TQ;           // MFMAs per k-step
+  // Copy split: FP16/BF16 issue half of a stage's copies after the barrier
+  // two stages ahead and the rest over the first two k-steps of the stage
+  // before; FP8 (two k-steps per stage) issues them all after the barrier.
+  static constexpr int NA = Op::ELEM == 2 ? NDMA / 2 : NDMA;
+  static constexpr int NB = NDMA - NA;
+  static constexpr int KB = KSTEPS > 2 ? 2 : KSTEPS - 1;
+  static_assert(NB == 0 || KB >= 1, "part-B copies need k-steps before the barrier");
+  static_assert(2 * STAGE <= kLdsLimit, "LDS budget");
+};
+
+template <class Op, bool PERSIST>
+__device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
+  using Cfg = TnCfg<Op>;
+  constexpr int NW = Cfg::NW, E = Cfg::E, FC = Cfg::FC, ROWB = Cfg::ROWB, BK = Cfg::BK, CPE = Cfg::CPE;
+  constexpr int TP = Cfg::TP, TQ = Cfg::TQ, QSEG = Cfg::QSEG, NDMA = Cfg::NDMA;
+  constexpr int NREAD = Cfg::NREAD, NMFMA = Cfg::NMFMA, NA = Cfg::NA, NB = Cfg::NB, KB = Cfg::KB;
+
+  __shared__ __attribute__((aligned(1024))) char smem[2 * Cfg::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int wp = wave_u / Cfg::WQ, wq = wave_u % Cfg::WQ;
+  const int64_t K = a.K;
+  const int nst = (int)((K + BK - 1) / BK);
+  const uint32_t kbytes16 = (uint32_t)(((K * E) + 15) & ~(int64_t)15);
+  const int64_t ntiles = a.tiles_p * a.tiles_q;
+
+  // ---- copies ----
+  // One copy instruction fills one 1 KiB LDS segment = 8 rows of 128 bytes:
+  // lane l lands at byte 16*l, row 8*seg + l/8, physical chunk l%8, which
+  // holds logical chunk (l%8) ^ key(row), key(row) = (row/2) mod 8 =
+  // (4*(wave%2) + l/16) mod 8 for segment i*4 + wave.  Rows past the matrix
+  // edge need no test: their offsets are at least rows*ld >= num_records.
+  const int dkc = (lane & 7) ^ ((4 * (wave_u & 1) + (lane >> 4)) & 7);
+  const int dk0 = dkc * CPE;
+  uint32_t qvo[QSEG], pvo[Cfg::PSEG];
+#pragma unroll
+  for (int i = 0; i < QSEG; ++i) qvo[i] = (uint32_t)((8 * (i * NW + wave_u) + (lane >> 3)) * a.ldq + dkc * 16);
+#pragma unroll
+  for (int i = 0; i < Cfg::PSEG; ++i)
+    pvo[i] = (uint32_t)((8 * (i * NW + wave_u) + (lane >> 3)) * a.ldp + dkc * 16);
+  // Copy source of one tile: block base pointers and descriptor sizes.  A
+  // tile index past the end gives zero records (its copies read zeros).
+  struct Src {
+    const char* q;
+    const char* p;
+    uint32_t qn, pn;
+  };
+  auto tile_src = [&](int64_t tile) {
+    Src r;
+    if (tile < ntiles) {
+      int64_t tp, tq;
+      tile_map(a.tiles_p, a.tiles_q, a.group, tile, &tp, &tq);
+      const int64_t q0 = tq * Cfg::BQ, p0 = tp * Cfg::BP;
+      const int64_t qrows = (a.Qn - q0) < Cfg::BQ ? (a.Qn - q0) : Cfg::BQ;
+      const int64_t prows = (a.Pn - p0) < Cfg::BP ? (a.Pn - p0) : Cfg::BP;
+      r.q = a.Q + q0 * a.ldq;
+      r.p = a.P + p0 * a.ldp;
+      r.qn = (uint32_t)((qrows - 1) * a.ldq) + kbytes16;
+      r.pn = (uint32_t)((prows - 1) * a.ldp) + kbytes16;
+    } else {
+      r.q = a.Q;
+      r.p = a.P;
+      r.qn = 0;
+      r.pn = 0;
+    }
+    return r;
+  };
+  auto rsrc_at = [&](const char* blk, uint32_t nrec, int t) {
+    const uint32_t adv = (uint32_t)t * ROWB;
+    // (readfirstlane keeps the clamped count in a scalar register: a vector
+    // select here would force a per-lane loop around every copy.)
+    const uint32_t left = (uint32_t)__builtin_amdgcn_readfirstlane((int)(adv < nrec ? nrec - adv : 0u));
+    return make_rsrc(blk + adv, left);
+  };
+  // Chunks at or past K read zero: bit 31 puts the offset past num_records.
+  auto kill_at = [&](int t) {
+    const int64_t rem64 = K - (int64_t)t * BK;
+    const int rem = (int)(rem64 < BK ? rem64 : BK);
+    return dk0 >= rem ? kOobOffset : 0u;
+  };
+  auto copy_d = [&](__amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rp, uint32_t kill, char* stage_lds, int d) {
+    if (d < QSEG) {
+      char* dst = stage_lds + Cfg::P_LDS + (d * NW + wave_u) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)dst, 16, qvo[d] | kill, 0,
+                                               0, 0);
+    } else {
+      char* dst = stage_lds + ((d - QSEG) * NW + wave_u) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (__attribute__((address_space(3))) void*)dst, 16,
+                                               pvo[d - QSEG] | kill, 0, 0, 0);
+    }
+  };
+
+  // ---- fragments and MFMAs ----
+  const int l32 = lane & 31, h = lane >> 5;
+  const int sw_r = (l32 >> 1) & 7;               // swizzle key of every fragment row of this lane
+  const uint32_t pf_base = (uint32_t)((wp * Cfg::WTP + l32) * ROWB);
+  const uint32_t qf_base = (uint32_t)(Cfg::P_LDS + (wq * Cfg::WTQ + l32) * ROWB);
+  u32x4 fa[2][TP][FC], fb[2][TQ][FC];
+  auto read_one = [&](const char* sb, int kk, int set, int r) {
+    const bool isb = r < TQ * FC;
+    const int rr = isb ? r : r - TQ * FC;
+    const int tile = rr / FC, f = rr % FC;
+    const uint32_t off = (uint32_t)((((kk * 2 + h) * FC + f) ^ sw_r) << 4);
+    const char* base = sb + (isb ? qf_base : pf_base) + tile * 32 * ROWB;
+    const u32x4 v = *(const u32x4*)(base + off);
+    if (isb) fb[set][tile][f] = v; else fa[set][tile][f] = v;
+  };
+  f32x16 acc[TP][TQ];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < TP; ++i)
+#pragma unroll
+      for (int j = 0; j < TQ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  };
+  auto mfma_one = [&](int set, int t) {
+    const int i = t / TQ, j = t % TQ;
+    acc[i][j] = Op::mma_parts(fa[set][i], fb[set][j], acc[i][j]);
+  };
+  auto read_slot = [](int r, int span) { return r * span / NREAD; };
+  constexpr int LAST = (Cfg::KSTEPS - 1) & 1;
+
+  // ---- one stage ----
+  // Global stage g (buffer g % 2) is stage s of the current tile.  Copies
+  // issued here belong to the stream position g + 2 (after the barrier; NA
+  // of them) and g + 1 (before it; NB of them), which may already be stages
+  // of the next tile `nx`.
+  auto stage = [&](int g, int s, const Src& cu, const Src& nx) {
+    const int b = g & 1;
+    const char* sb = smem + b * Cfg::STAGE;
+    char* ob = smem + (b ^ 1) * Cfg::STAGE;
+    // stream position g + 1
+    const bool n1 = s + 1 >= nst;
+    const int t1 = n1 ? s + 1 - nst : s + 1;
+    const __amdgpu_buffer_rsrc_t rq1 = rsrc_at(n1 ? nx.q : cu.q, n1 ? nx.qn : cu.qn, t1);
+    const __amdgpu_buffer_rsrc_t rp1 = rsrc_at(n1 ? nx.p : cu.p, n1 ? nx.pn : cu.pn, t1);
+    const uint32_t kill1 = kill_at(t1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk + 1 < Cfg::KSTEPS; ++kk) {
+      const int span = kk + 2 == Cfg::KSTEPS ? NMFMA / 2 : NMFMA;
+#pragma unroll
+      for (int t = 0; t < NMFMA; ++t) {
+        mfma_one(kk & 1, t);
+#pragma unroll
+        for (int r = 0; r < NREAD; ++r)
+          if (read_slot(r, span) == t) read_one(sb, kk + 1, (kk + 1) & 1, r);
+        if constexpr (NB > 0) {
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            if (j * (KB * NMFMA) / NB == kk * NMFMA + t) copy_d(rq1, rp1, kill1, ob, NA + j);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // stream position g + 2
+    const bool n2 = s + 2 >= nst;
+    const int t2 = n2 ? s + 2 - nst : s + 2;
+    const __amdgpu_buffer_rsrc_t rq2 = rsrc_at(n2 ? nx.q : cu.q, n2 ? nx.qn : cu.qn, t2);
+    const __amdgpu_buffer_rsrc_t rp2 = rsrc_at(n2 ? nx.p : cu.p, n2 ? nx.pn : cu.pn, t2);
+    const uint32_t kill2 = kill_at(t2);
+    char* db = smem + b * Cfg::STAGE;
+#pragma unroll
+    for (int t = 0; t < NMFMA; ++t) {
+      mfma_one(LAST, t);
+#pragma unroll
+      for (int r = 0; r < NREAD; ++r)
+        if (read_slot(r, NMFMA) == t) read_one(ob, 0, 0, r);
+#pragma unroll
+      for (int d = 0; d < NA; ++d)
+        if (d * NMFMA / NA == t) copy_d(rq2, rp2, kill2, db, d);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- tiles ----
+  int64_t tile = blockIdx.x;
+  if (tile >= ntiles) return;
+  const int64_t step = PERSIST ? (int64_t)gridDim.x : ntiles;
+  Src cur = tile_src(tile);
+  Src nxt = tile_src(tile + step);
+  {
+    // Prologue: stream positions 0 and 1 (nst >= 2, so both are this tile's),
+    // and the part-B copies of position 1 are included.
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const __amdgpu_buffer_rsrc_t rq = rsrc_at(cur.q, cur.qn, t), rp = rsrc_at(cur.p, cur.pn, t);
+      const uint32_t kill = kill_at(t);
+#pragma unroll
+      for (int d = 0; d < (t == 0 ? NDMA : NA); ++d) copy_d(rq, rp, kill, smem + t * Cfg::STAGE, d);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcntBase | vmcnt_bits(NA));
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < NREAD; ++r) read_one(smem, 0, 0, r);
+  }
+  int g = 0;
+  for (;;) {
+    zero_acc();
+    for (int s = 0; s < nst; ++s, ++g) stage(g, s, cur, nxt);
+    if constexpr (!PERSIST) break;
+    // Epilogue: four consecutive p of one q per lane and group, stored
+    // straight from the accumulators; the stores drain while the next
+    // tile's stages (already copied) run.
+    {
+      int64_t tp, tq;
+      tile_map(a.tiles_p, a.tiles_q, a.group, tile, &tp, &tq);
+      const int64_t pb = tp * Cfg::BP + wp * Cfg::WTP, qb = tq * Cfg::BQ + wq * Cfg::WTQ;
+#pragma unroll
+      for (int i = 0; i < TP; ++i)
+#pragma unroll
+        for (int j = 0; j < TQ; ++j) {
+          const int64_t q = qb + 32 * j + l32;
+          if (q >= a.Qn) continue;
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            const int64_t p = pb + 32 * i + 8 * gg + 4 * h;
+            store4<Op>(a, q, p, acc[i][j][4 * gg + 0], acc[i][j][4 * gg + 1], acc[i][j][4 * gg + 2],
+                       acc[i][j][4 * gg + 3]);
+          }
+        }
+    }
+    tile += step;
+    if (tile >= ntiles) break;
+    cur = nxt;
+    nxt = tile_src(tile + step);
+  }
+  // Copies issued past the last tile read zeros; let them land before exit.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  if constexpr (!PERSIST) {
+    // One tile per workgroup: the stage buffers are free for an LDS-staged
+    // epilogue once every wave is past its last read.
+    __syncthreads();
+    int64_t tp, tq;
+    tile_map(a.tiles_p, a.tiles_q, a.group, tile, &tp, &tq);
+    static_assert(Cfg::WTQ * 256 * NW <= 2 * Cfg::STAGE, "staging fits in the stage buffers");
+    staged_epilogue<Op, Cfg::WTP, Cfg::WTQ, TP, TQ>(a, smem + wave_u * (Cfg::WTQ * 256), acc, lane,
+                                                     tp * Cfg::BP + wp * Cfg::WTP, tq * Cfg::BQ + wq * Cfg::WTQ);
+  }
+}
+
+template <class Op, bool PERSIST>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_tn_kernel(const GemmArgs a) {
+  gemm_tn_body<Op, PERSIST>(a);
+}
+
+}  // namespace dg
