@@ -43,6 +43,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_records, kBufferWord3);
 }
 
+// The same descriptor as four dwords (gfx9 layout: base, base[47:32] with
+// stride 0, num_records, word 3), for inline assembly.
+__device__ __forceinline__ i32x4 make_desc(const void* base, uint32_t num_records) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  return i32x4{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xffffu), (int)num_records, kBufferWord3};
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ...
+// lds) written as inline assembly.  The compiler does not see it as an LDS
+// write, so it adds no waits of its own for it: the caller waits (vmcnt)
+// before anything reads the destination, as the kernels here do before
+// every barrier that publishes a stage.  (Issued through the builtin, the
+// copy makes the compiler drain all copies in flight before every
+// transposing LDS read, which it cannot prove independent of them.)
+// M0 holds the LDS destination; one wait state separates its write from the
+// load that consumes it.
+__device__ __forceinline__ void copy16_lds(i32x4 desc, uint32_t voff, const void* lds_dst) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_dst;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(desc), "s"(m0)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
 }

@@ -51,11 +51,11 @@ Launch mfma_launch(const char* name) {
 // Four-wave 256 x 256 TN kernel.  FP16/BF16 run one tile per workgroup with
 // the LDS-staged epilogue; FP8, whose FP32 output is twice as large, runs
 // persistently so that each tile's stores drain under the next tile's stages.
-template <class Op>
+template <class Op, bool PKM>
 Launch tn_launch(const char* name) {
-  using Cfg = TnCfg<Op>;
+  using Cfg = TnCfg<Op, PKM>;
   constexpr bool P = Op::ELEM == 1;
-  return Launch{(const void*)&gemm_tn_kernel<Op, P>, name, Cfg::BP, Cfg::BQ, Cfg::NT, 2 * Cfg::STAGE, false, P};
+  return Launch{(const void*)&gemm_tn_kernel<Op, P, PKM>, name, Cfg::BP, Cfg::BQ, Cfg::NT, 2 * Cfg::STAGE, PKM, P};
 }
 
 template <bool PT>
@@ -84,15 +84,22 @@ Launch select_skinny(int dt, int64_t M) {
 
 Launch select(int dt, int layout, int64_t K) {
   const bool nn = layout == DGEMM_NN;
-  // TN with K a whole number of 16-byte chunks and at least two stages: the
-  // four-wave kernel (gemm_tn.hpp).
-  if (!nn && dt != DT_F32) {
+  // K a whole number of 16-byte chunks and at least two stages: the
+  // four-wave kernel (gemm_tn.hpp); NN reads B with transposing LDS reads.
+  if (dt != DT_F32) {
     const int e = in_elem(dt);
     if (K % (16 / e) == 0 && K >= 2 * (128 / e)) {
+      if (nn) {
+        switch (dt) {
+          case DT_F16: return tn_launch<OpF16, true>("f16_nn_256x256_w4");
+          case DT_BF16: return tn_launch<OpBF16, true>("bf16_nn_256x256_w4");
+          default: return tn_launch<OpFP8, true>("fp8_nn_256x256_w4_persistent");
+        }
+      }
       switch (dt) {
-        case DT_F16: return tn_launch<OpF16>("f16_tn_256x256_w4");
-        case DT_BF16: return tn_launch<OpBF16>("bf16_tn_256x256_w4");
-        default: return tn_launch<OpFP8>("fp8_tn_256x256_w4_persistent");
+        case DT_F16: return tn_launch<OpF16, false>("f16_tn_256x256_w4");
+        case DT_BF16: return tn_launch<OpBF16, false>("bf16_tn_256x256_w4");
+        default: return tn_launch<OpFP8, false>("fp8_tn_256x256_w4_persistent");
       }
     }
   }

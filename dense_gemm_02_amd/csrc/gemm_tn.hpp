@@ -26,7 +26,7 @@
 
 namespace dg {
 
-template <class Op>
+template <class Op, bool PKM>
 struct TnCfg {
   static constexpr int BP = 256, BQ = 256, WP = 2, WQ = 2, NW = 4, NT = 256;
   static constexpr int E = Op::ELEM, FC = Op::FC;
@@ -40,7 +40,17 @@ struct TnCfg {
   static constexpr int WTP = BP / WP, WTQ = BQ / WQ;
   static constexpr int TP = WTP / 32, TQ = WTQ / 32;
   static constexpr int KSTEPS = BK / Op::KI;
-  static constexpr int NREAD = (TP + TQ) * FC;    // 16-byte LDS reads per k-step
+  // LDS reads per k-step: 16-byte reads of Q fragments, and of P fragments
+  // either 16-byte reads (K-contiguous P) or twice as many 8-byte
+  // transposing reads (p-contiguous P).
+  static constexpr int PRD = PKM ? 2 * FC : FC;   // reads per P fragment
+  static constexpr int NREAD = TQ * FC + TP * PRD;
+  // p-contiguous P: LDS rows of k, BP*E bytes, in units of one 32-row MFMA
+  // tile (UB bytes) XOR-swizzled by k mod KEYM.
+  static constexpr int PROWB = BP * E;            // bytes of one LDS row of P (one k)
+  static constexpr int UB = 32 * E;
+  static constexpr int KEYM = 256 / UB;
+  static constexpr int RPSG = 1024 / PROWB;       // rows of P per 1 KiB copy segment
   static constexpr int NMFMA = TP * TQ;           // MFMAs per k-step
   // Copy split: FP16/BF16 issue half of a stage's copies after the barrier
   // two stages ahead and the rest over the first two k-steps of the stage
@@ -52,9 +62,9 @@ struct TnCfg {
   static_assert(2 * STAGE <= kLdsLimit, "LDS budget");
 };
 
-template <class Op, bool PERSIST>
+template <class Op, bool PERSIST, bool PKM>
 __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
-  using Cfg = TnCfg<Op>;
+  using Cfg = TnCfg<Op, PKM>;
   constexpr int NW = Cfg::NW, E = Cfg::E, FC = Cfg::FC, ROWB = Cfg::ROWB, BK = Cfg::BK, CPE = Cfg::CPE;
   constexpr int TP = Cfg::TP, TQ = Cfg::TQ, QSEG = Cfg::QSEG, NDMA = Cfg::NDMA;
   constexpr int NREAD = Cfg::NREAD, NMFMA = Cfg::NMFMA, NA = Cfg::NA, NB = Cfg::NB, KB = Cfg::KB;
@@ -81,9 +91,24 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   uint32_t qvo[QSEG], pvo[Cfg::PSEG];
 #pragma unroll
   for (int i = 0; i < QSEG; ++i) qvo[i] = (uint32_t)((8 * (i * NW + wave_u) + (lane >> 3)) * a.ldq + dkc * 16);
+  if constexpr (!PKM) {
 #pragma unroll
-  for (int i = 0; i < Cfg::PSEG; ++i)
-    pvo[i] = (uint32_t)((8 * (i * NW + wave_u) + (lane >> 3)) * a.ldp + dkc * 16);
+    for (int i = 0; i < Cfg::PSEG; ++i)
+      pvo[i] = (uint32_t)((8 * (i * NW + wave_u) + (lane >> 3)) * a.ldp + dkc * 16);
+  } else {
+    // p-contiguous P (NN's B): a segment holds RPSG rows of k; lane l lands
+    // at row l*16 / PROWB, byte (l*16) % PROWB, i.e. physical unit pu with
+    // offset w, which holds logical unit pu ^ (k mod KEYM).  Rows past K are
+    // past num_records and read zero; columns past the tile edge read
+    // whatever follows in B (those p are never stored).
+#pragma unroll
+    for (int i = 0; i < Cfg::PSEG; ++i) {
+      const int kr = Cfg::RPSG * (i * NW + wave_u) + (lane * 16) / Cfg::PROWB;
+      const int br = (lane * 16) % Cfg::PROWB;
+      const int lu = (br / Cfg::UB) ^ (kr % Cfg::KEYM);
+      pvo[i] = (uint32_t)(kr * a.ldp + lu * Cfg::UB + br % Cfg::UB);
+    }
+  }
   // Copy source of one tile: block base pointers and descriptor sizes.  A
   // tile index past the end gives zero records (its copies read zeros).
   struct Src {
@@ -100,9 +125,14 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       const int64_t qrows = (a.Qn - q0) < Cfg::BQ ? (a.Qn - q0) : Cfg::BQ;
       const int64_t prows = (a.Pn - p0) < Cfg::BP ? (a.Pn - p0) : Cfg::BP;
       r.q = a.Q + q0 * a.ldq;
-      r.p = a.P + p0 * a.ldp;
       r.qn = (uint32_t)((qrows - 1) * a.ldq) + kbytes16;
-      r.pn = (uint32_t)((prows - 1) * a.ldp) + kbytes16;
+      if constexpr (!PKM) {
+        r.p = a.P + p0 * a.ldp;
+        r.pn = (uint32_t)((prows - 1) * a.ldp) + kbytes16;
+      } else {
+        r.p = a.P + p0 * E;
+        r.pn = (uint32_t)((K - 1) * a.ldp) + (uint32_t)(((prows * E) + 15) & ~(int64_t)15);
+      }
     } else {
       r.q = a.Q;
       r.p = a.P;
@@ -111,12 +141,18 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     }
     return r;
   };
-  auto rsrc_at = [&](const char* blk, uint32_t nrec, int t) {
-    const uint32_t adv = (uint32_t)t * ROWB;
+  // Descriptor advanced to stage t: K-contiguous operands move along the
+  // row, p-contiguous P moves down BK rows.
+  // With p-contiguous P the copies go through inline assembly (see
+  // copy16_lds), which takes the descriptor as four dwords.
+  using Rsrc = std::conditional_t<PKM, i32x4, __amdgpu_buffer_rsrc_t>;
+  auto rsrc_at = [&](const char* blk, uint32_t nrec, int t, bool pkm_p) -> Rsrc {
+    const uint32_t adv = pkm_p ? (uint32_t)((int64_t)t * BK * a.ldp) : (uint32_t)t * ROWB;
     // (readfirstlane keeps the clamped count in a scalar register: a vector
     // select here would force a per-lane loop around every copy.)
     const uint32_t left = (uint32_t)__builtin_amdgcn_readfirstlane((int)(adv < nrec ? nrec - adv : 0u));
-    return make_rsrc(blk + adv, left);
+    if constexpr (PKM) return make_desc(blk + adv, left);
+    else return make_rsrc(blk + adv, left);
   };
   // Chunks at or past K read zero: bit 31 puts the offset past num_records.
   auto kill_at = [&](int t) {
@@ -124,8 +160,11 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     const int rem = (int)(rem64 < BK ? rem64 : BK);
     return dk0 >= rem ? kOobOffset : 0u;
   };
-  auto copy_d = [&](__amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rp, uint32_t kill, char* stage_lds, int d) {
-    if (d < QSEG) {
+  auto copy_d = [&](Rsrc rq, Rsrc rp, uint32_t kill, char* stage_lds, int d) {
+    if constexpr (PKM) {
+      if (d < QSEG) copy16_lds(rq, qvo[d] | kill, stage_lds + Cfg::P_LDS + (d * NW + wave_u) * 1024);
+      else copy16_lds(rp, pvo[d - QSEG], stage_lds + ((d - QSEG) * NW + wave_u) * 1024);
+    } else if (d < QSEG) {
       char* dst = stage_lds + Cfg::P_LDS + (d * NW + wave_u) * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)dst, 16, qvo[d] | kill, 0,
                                                0, 0);
@@ -142,14 +181,46 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   const uint32_t pf_base = (uint32_t)((wp * Cfg::WTP + l32) * ROWB);
   const uint32_t qf_base = (uint32_t)(Cfg::P_LDS + (wq * Cfg::WTQ + l32) * ROWB);
   u32x4 fa[2][TP][FC], fb[2][TQ][FC];
+  // Transposing reads of p-contiguous P (ds_read_b64_tr_b16 / _tr_b8): in
+  // each 16-lane group, output lane i receives element i % 4 (bytes: i % 8)
+  // of source lanes i/4 + 4j (i/8 + 2j).  So a source lane addresses 4 (8)
+  // consecutive p of row k = kbase + s/4 (s/2), s = lane % 16, and output
+  // lane i ends up with 4 (8) consecutive k of p = pbase + i.  Every row a
+  // lane addresses has the same swizzle key, s/4 (s/2).
+  const int tg = lane >> 4, ts = lane & 15;
+  constexpr int TRK = 8 / E;                    // k per transposing read
+  const int tkey = ts / (2 * E);                // k mod KEYM of every row this lane addresses
   auto read_one = [&](const char* sb, int kk, int set, int r) {
     const bool isb = r < TQ * FC;
-    const int rr = isb ? r : r - TQ * FC;
-    const int tile = rr / FC, f = rr % FC;
-    const uint32_t off = (uint32_t)((((kk * 2 + h) * FC + f) ^ sw_r) << 4);
-    const char* base = sb + (isb ? qf_base : pf_base) + tile * 32 * ROWB;
-    const u32x4 v = *(const u32x4*)(base + off);
-    if (isb) fb[set][tile][f] = v; else fa[set][tile][f] = v;
+    if (isb || !PKM) {
+      const int rr = isb ? r : r - TQ * FC;
+      const int tile = rr / FC, f = rr % FC;
+      const uint32_t off = (uint32_t)((((kk * 2 + h) * FC + f) ^ sw_r) << 4);
+      const char* base = sb + (isb ? qf_base : pf_base) + tile * 32 * ROWB;
+      const u32x4 v = *(const u32x4*)(base + off);
+      if (isb) fb[set][tile][f] = v; else fa[set][tile][f] = v;
+    } else {
+      const int rr = r - TQ * FC;
+      const int tile = rr / Cfg::PRD, q8 = rr % Cfg::PRD;   // which 8-byte piece of the fragment
+      // k of this lane's row: the k-step, the lane half h = tg / 2 (its
+      // block of Op::KI / 2 k), the piece q8 (TRK k each), and tkey.
+      const int krow = kk * Op::KI + (tg >> 1) * (Op::KI / 2) + q8 * TRK + tkey;
+      const int unit = (wp * (Cfg::WTP / 32) + tile) ^ tkey;
+      const char* src = sb + krow * Cfg::PROWB + unit * Cfg::UB + (tg & 1) * (16 * E) + (ts % (2 * E)) * 8;
+      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+      u32x2 v;
+      if constexpr (E == 2) {
+        typedef __fp16 h16x4 __attribute__((ext_vector_type(4)));
+        v = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                                          (__attribute__((address_space(3))) h16x4*)src));
+      } else {
+        typedef int i32x2v __attribute__((ext_vector_type(2)));
+        v = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                          (__attribute__((address_space(3))) i32x2v*)src));
+      }
+      fa[set][tile][q8 >> 1][2 * (q8 & 1)] = v[0];
+      fa[set][tile][q8 >> 1][2 * (q8 & 1) + 1] = v[1];
+    }
   };
   f32x16 acc[TP][TQ];
   auto zero_acc = [&]() {
@@ -179,8 +250,8 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     // stream position g + 1
     const bool n1 = s + 1 >= nst;
     const int t1 = n1 ? s + 1 - nst : s + 1;
-    const __amdgpu_buffer_rsrc_t rq1 = rsrc_at(n1 ? nx.q : cu.q, n1 ? nx.qn : cu.qn, t1);
-    const __amdgpu_buffer_rsrc_t rp1 = rsrc_at(n1 ? nx.p : cu.p, n1 ? nx.pn : cu.pn, t1);
+    const Rsrc rq1 = rsrc_at(n1 ? nx.q : cu.q, n1 ? nx.qn : cu.qn, t1, false);
+    const Rsrc rp1 = rsrc_at(n1 ? nx.p : cu.p, n1 ? nx.pn : cu.pn, t1, PKM);
     const uint32_t kill1 = kill_at(t1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -206,8 +277,8 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     // stream position g + 2
     const bool n2 = s + 2 >= nst;
     const int t2 = n2 ? s + 2 - nst : s + 2;
-    const __amdgpu_buffer_rsrc_t rq2 = rsrc_at(n2 ? nx.q : cu.q, n2 ? nx.qn : cu.qn, t2);
-    const __amdgpu_buffer_rsrc_t rp2 = rsrc_at(n2 ? nx.p : cu.p, n2 ? nx.pn : cu.pn, t2);
+    const Rsrc rq2 = rsrc_at(n2 ? nx.q : cu.q, n2 ? nx.qn : cu.qn, t2, false);
+    const Rsrc rp2 = rsrc_at(n2 ? nx.p : cu.p, n2 ? nx.pn : cu.pn, t2, PKM);
     const uint32_t kill2 = kill_at(t2);
     char* db = smem + b * Cfg::STAGE;
 #pragma unroll
@@ -234,7 +305,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     // and the part-B copies of position 1 are included.
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const __amdgpu_buffer_rsrc_t rq = rsrc_at(cur.q, cur.qn, t), rp = rsrc_at(cur.p, cur.pn, t);
+      const Rsrc rq = rsrc_at(cur.q, cur.qn, t, false), rp = rsrc_at(cur.p, cur.pn, t, PKM);
       const uint32_t kill = kill_at(t);
 #pragma unroll
       for (int d = 0; d < (t == 0 ? NDMA : NA); ++d) copy_d(rq, rp, kill, smem + t * Cfg::STAGE, d);
@@ -289,10 +360,10 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   }
 }
 
-template <class Op, bool PERSIST>
+template <class Op, bool PERSIST, bool PKM>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_tn_kernel(const GemmArgs a) {
-  gemm_tn_body<Op, PERSIST>(a);
+  gemm_tn_body<Op, PERSIST, PKM>(a);
 }
 
 }  // namespace dg

@@ -74,23 +74,25 @@ def kernel_name(dtype, layout, M, N, K):
     return buf.value.decode()
 
 
-# The four-wave TN kernel (K a multiple of the 16-byte chunk, at least two
-# 128-byte stages): exactly two stages, an odd stage count with edge tiles,
-# and more tiles than CUs, which makes the persistent FP8 variant walk several
-# tiles per workgroup with its copy stream running across tile boundaries.
-@pytest.mark.parametrize("dtype", ["f16", "bf16", "fp8"])
-def test_tn_four_wave_kernel(dtype):
+# The four-wave kernel (K a multiple of the 16-byte chunk, at least two
+# 128-byte stages; NN reads B through transposing LDS reads): exactly two
+# stages, an odd stage count with edge tiles (N not a multiple of 8 in NN, so
+# B's rows are padded and the last p tile reads past the row end), a partial
+# last stage, and more tiles than CUs, which makes the persistent FP8 variant
+# walk several tiles per workgroup with its copy stream crossing tiles.
+@pytest.mark.parametrize("dtype,layout", [(d, l) for d in ("f16", "bf16", "fp8") for l in ("tn", "nn")])
+def test_four_wave_kernel(dtype, layout):
     bk = {"f16": 64, "bf16": 64, "fp8": 128}[dtype]
-    shapes = [(512, 512, 2 * bk), (300, 520, 3 * bk), (4352, 4352, 3 * bk), (1000, 1100, 9 * bk + 16)]
+    shapes = [(512, 512, 2 * bk), (300, 521, 3 * bk), (4352, 4352, 3 * bk), (1000, 1100, 9 * bk + 16)]
     for idx, (M, N, K) in enumerate(shapes):
-        assert "_w4" in kernel_name(dtype, "tn", M, N, K)
-        p = make_problem(dtype, "tn", M, N, K, seed=5000 + idx, pad=idx % 2)
-        say(f"case w4 {dtype} M={M} N={N} K={K}")
+        assert "_w4" in kernel_name(dtype, layout, M, N, K)
+        p = make_problem(dtype, layout, M, N, K, seed=5000 + idx, pad=idx % 2)
+        say(f"case w4 {dtype} {layout} M={M} N={N} K={K}")
         cij, pad = c_host(p, run_gpu(p))
         assert pad_untouched(pad, dtype)
         ok, err, nbad = compare(p, cij)
-        assert ok, f"{dtype} tn {(M, N, K)}: max err {err:.3e}, {nbad} bad"
-    p = make_problem(dtype, "tn", 260, 300, 16 * bk, seed=5100, dist="pm1")
+        assert ok, f"{dtype} {layout} {(M, N, K)}: max err {err:.3e}, {nbad} bad"
+    p = make_problem(dtype, layout, 260, 300, 16 * bk, seed=5100, dist="pm1")
     cij, _ = c_host(p, run_gpu(p))
     ok, _, nbad = compare(p, cij, exact=True)
     assert ok, f"pm1: {nbad} elements differ"
