@@ -48,14 +48,60 @@ Launch mfma_launch(const char* name) {
                 2 * Cfg::STAGE, PT, false};
 }
 
-// Four-wave 256 x 256 TN kernel.  FP16/BF16 run one tile per workgroup with
-// the LDS-staged epilogue; FP8, whose FP32 output is twice as large, runs
-// persistently so that each tile's stores drain under the next tile's stages.
-template <class Op, bool PKM>
+// Four-wave kernel (gemm_tn.hpp).  256 x 256 FP8, whose FP32 output is twice
+// as large, runs persistently so that each tile's stores drain under the next
+// tile's stages; every other shape runs one tile per workgroup.
+template <class Op, bool PKM, int BP, int BQ>
 Launch tn_launch(const char* name) {
-  using Cfg = TnCfg<Op, PKM>;
-  constexpr bool P = Op::ELEM == 1;
-  return Launch{(const void*)&gemm_tn_kernel<Op, P, PKM>, name, Cfg::BP, Cfg::BQ, Cfg::NT, 2 * Cfg::STAGE, PKM, P};
+  using Cfg = TnCfg<Op, PKM, BP, BQ>;
+  constexpr bool P = Op::ELEM == 1 && BP == 256 && BQ == 256;
+  return Launch{(const void*)&gemm_tn_kernel<Op, P, PKM, BP, BQ>, name, BP, BQ, Cfg::NT, 2 * Cfg::STAGE, PKM, P};
+}
+
+// Block tiles of the four-wave kernel and their throughput relative to the
+// 256 x 256 tile when every CU is busy, measured on MI355X at 8192^3 class
+// sizes (bf16 and fp8 TN; 128 x 128 runs two workgroups per CU): smaller
+// tiles re-read more of A and B per flop and give each wave fewer MFMAs per
+// fragment read, but fill the CUs when the problem has few tiles. With these
+// rates 128 x 128 never loses to 256 x 128, so the latter serves only FP8
+// with p-contiguous P, whose transposing-read swizzle needs 256-byte rows.
+// The choice minimises ceil(tiles / slots) * tile work / rate, i.e. the
+// number of rounds of workgroups times the time of one round ("FP16 GEMM
+// Optimization on AMD RDNA 3 and RDNA 4", Where That Leaves Us: no single
+// tile is best on every shape).
+struct TileChoice {
+  int bp, bq, per_cu;   // tile, workgroups resident per CU
+  double rate;          // CU throughput relative to 256 x 256
+};
+constexpr TileChoice kTiles[3] = {{256, 256, 1, 1.00}, {256, 128, 1, 0.76}, {128, 128, 2, 0.78}};
+constexpr int kPlanCus = 256;  // MI355X CUs, for the tile choice only
+
+int pick_tile(int64_t Pn, int64_t Qn, unsigned allowed) {
+  int best = -1;
+  double best_t = 0.0;
+  for (int i = 0; i < 3; ++i) {
+    if (!(allowed >> i & 1u)) continue;
+    const TileChoice& c = kTiles[i];
+    const int64_t tiles = ((Pn + c.bp - 1) / c.bp) * ((Qn + c.bq - 1) / c.bq);
+    const int64_t slots = (int64_t)kPlanCus * c.per_cu;
+    const double rounds = (double)((tiles + slots - 1) / slots);
+    const double t = rounds * (double)c.bp * c.bq * c.per_cu / c.rate;
+    if (best < 0 || t < best_t) { best = i; best_t = t; }
+  }
+  return best;
+}
+
+template <class Op, bool PKM>
+Launch tn_pick(const char* const names[3], int64_t Pn, int64_t Qn) {
+  // p-contiguous FP8 P keeps 256-wide rows (the transposing-read swizzle
+  // needs eight 32-byte units per row).
+  if constexpr (PKM && Op::ELEM == 1) {
+    if (pick_tile(Pn, Qn, 0b011) == 1) return tn_launch<Op, PKM, 256, 128>(names[1]);
+    return tn_launch<Op, PKM, 256, 256>(names[0]);
+  } else {
+    if (pick_tile(Pn, Qn, 0b101) == 2) return tn_launch<Op, PKM, 128, 128>(names[2]);
+    return tn_launch<Op, PKM, 256, 256>(names[0]);
+  }
 }
 
 template <bool PT>
@@ -82,24 +128,32 @@ Launch select_skinny(int dt, int64_t M) {
   return M <= 16 ? skinny_launch<OpBF16, 1>("bf16_tn_skinny16") : skinny_launch<OpBF16, 2>("bf16_tn_skinny32");
 }
 
-Launch select(int dt, int layout, int64_t K) {
+Launch select(int dt, int layout, int64_t M, int64_t N, int64_t K) {
   const bool nn = layout == DGEMM_NN;
   // K a whole number of 16-byte chunks and at least two stages: the
-  // four-wave kernel (gemm_tn.hpp); NN reads B with transposing LDS reads.
+  // four-wave kernel (gemm_tn.hpp), tile chosen by shape; NN reads B with
+  // transposing LDS reads.
   if (dt != DT_F32) {
     const int e = in_elem(dt);
     if (K % (16 / e) == 0 && K >= 2 * (128 / e)) {
+      const int64_t Pn = nn ? N : M, Qn = nn ? M : N;
+      static const char* const f16n[3] = {"f16_nn_256x256_w4", nullptr, "f16_nn_128x128_w4"};
+      static const char* const bf16n[3] = {"bf16_nn_256x256_w4", nullptr, "bf16_nn_128x128_w4"};
+      static const char* const fp8n[3] = {"fp8_nn_256x256_w4_persistent", "fp8_nn_256x128_w4", nullptr};
+      static const char* const f16t[3] = {"f16_tn_256x256_w4", nullptr, "f16_tn_128x128_w4"};
+      static const char* const bf16t[3] = {"bf16_tn_256x256_w4", nullptr, "bf16_tn_128x128_w4"};
+      static const char* const fp8t[3] = {"fp8_tn_256x256_w4_persistent", nullptr, "fp8_tn_128x128_w4"};
       if (nn) {
         switch (dt) {
-          case DT_F16: return tn_launch<OpF16, true>("f16_nn_256x256_w4");
-          case DT_BF16: return tn_launch<OpBF16, true>("bf16_nn_256x256_w4");
-          default: return tn_launch<OpFP8, true>("fp8_nn_256x256_w4_persistent");
+          case DT_F16: return tn_pick<OpF16, true>(f16n, Pn, Qn);
+          case DT_BF16: return tn_pick<OpBF16, true>(bf16n, Pn, Qn);
+          default: return tn_pick<OpFP8, true>(fp8n, Pn, Qn);
         }
       }
       switch (dt) {
-        case DT_F16: return tn_launch<OpF16, false>("f16_tn_256x256_w4");
-        case DT_BF16: return tn_launch<OpBF16, false>("bf16_tn_256x256_w4");
-        default: return tn_launch<OpFP8, false>("fp8_tn_256x256_w4_persistent");
+        case DT_F16: return tn_pick<OpF16, false>(f16t, Pn, Qn);
+        case DT_BF16: return tn_pick<OpBF16, false>(bf16t, Pn, Qn);
+        default: return tn_pick<OpFP8, false>(fp8t, Pn, Qn);
       }
     }
   }
@@ -136,7 +190,7 @@ int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
   if (((uintptr_t)C) % (uintptr_t)out_elem(dt) != 0) return DGEMM_ERR_MISALIGNED;
 
   const bool skinny = use_skinny(dt, layout, M);
-  Launch L = skinny ? select_skinny(dt, M) : select(dt, layout, K);
+  Launch L = skinny ? select_skinny(dt, M) : select(dt, layout, M, N, K);
   GemmArgs g{};
   if (!nn) {
     g.P = (const char*)A; g.ldp = lda * e; g.Pn = M;

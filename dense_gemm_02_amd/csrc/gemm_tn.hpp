@@ -26,9 +26,9 @@
 
 namespace dg {
 
-template <class Op, bool PKM>
+template <class Op, bool PKM, int BP_ = 256, int BQ_ = 256>
 struct TnCfg {
-  static constexpr int BP = 256, BQ = 256, WP = 2, WQ = 2, NW = 4, NT = 256;
+  static constexpr int BP = BP_, BQ = BQ_, WP = 2, WQ = 2, NW = 4, NT = 256;
   static constexpr int E = Op::ELEM, FC = Op::FC;
   static constexpr int ROWB = 128;                // bytes of k per LDS row per stage
   static constexpr int BK = ROWB / E;             // k per stage
@@ -60,11 +60,18 @@ struct TnCfg {
   static constexpr int KB = KSTEPS > 2 ? 2 : KSTEPS - 1;
   static_assert(NB == 0 || KB >= 1, "part-B copies need k-steps before the barrier");
   static_assert(2 * STAGE <= kLdsLimit, "LDS budget");
+  static_assert(!PKM || PROWB / UB >= KEYM, "swizzle keys stay within a row of P");
+  // The LDS-staged epilogue needs 256-byte staged rows; smaller wave tiles
+  // store straight from the accumulators.
+  static constexpr bool STAGED_EPI = (TP / (Op::OE == 4 ? 2 : 1)) * 32 * Op::OE == 256;
+  // Waves per SIMD the kernel is compiled for: a 64x64 wave tile is small
+  // enough for two (two workgroups per CU).
+  static constexpr int WPE = TP * TQ <= 4 ? 2 : 1;
 };
 
-template <class Op, bool PERSIST, bool PKM>
+template <class Op, bool PERSIST, bool PKM, int BP, int BQ>
 __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
-  using Cfg = TnCfg<Op, PKM>;
+  using Cfg = TnCfg<Op, PKM, BP, BQ>;
   constexpr int NW = Cfg::NW, E = Cfg::E, FC = Cfg::FC, ROWB = Cfg::ROWB, BK = Cfg::BK, CPE = Cfg::CPE;
   constexpr int TP = Cfg::TP, TQ = Cfg::TQ, QSEG = Cfg::QSEG, NDMA = Cfg::NDMA;
   constexpr int NREAD = Cfg::NREAD, NMFMA = Cfg::NMFMA, NA = Cfg::NA, NB = Cfg::NB, KB = Cfg::KB;
@@ -315,32 +322,34 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
 #pragma unroll
     for (int r = 0; r < NREAD; ++r) read_one(smem, 0, 0, r);
   }
+  // Epilogue straight from the accumulators: four consecutive p of one q per
+  // lane and group, one 8- or 16-byte store each.
+  auto direct_epilogue = [&](int64_t t) {
+    int64_t tp, tq;
+    tile_map(a.tiles_p, a.tiles_q, a.group, t, &tp, &tq);
+    const int64_t pb = tp * Cfg::BP + wp * Cfg::WTP, qb = tq * Cfg::BQ + wq * Cfg::WTQ;
+#pragma unroll
+    for (int i = 0; i < TP; ++i)
+#pragma unroll
+      for (int j = 0; j < TQ; ++j) {
+        const int64_t q = qb + 32 * j + l32;
+        if (q >= a.Qn) continue;
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int64_t p = pb + 32 * i + 8 * gg + 4 * h;
+          store4<Op>(a, q, p, acc[i][j][4 * gg + 0], acc[i][j][4 * gg + 1], acc[i][j][4 * gg + 2],
+                     acc[i][j][4 * gg + 3]);
+        }
+      }
+  };
   int g = 0;
   for (;;) {
     zero_acc();
     for (int s = 0; s < nst; ++s, ++g) stage(g, s, cur, nxt);
     if constexpr (!PERSIST) break;
-    // Epilogue: four consecutive p of one q per lane and group, stored
-    // straight from the accumulators; the stores drain while the next
-    // tile's stages (already copied) run.
-    {
-      int64_t tp, tq;
-      tile_map(a.tiles_p, a.tiles_q, a.group, tile, &tp, &tq);
-      const int64_t pb = tp * Cfg::BP + wp * Cfg::WTP, qb = tq * Cfg::BQ + wq * Cfg::WTQ;
-#pragma unroll
-      for (int i = 0; i < TP; ++i)
-#pragma unroll
-        for (int j = 0; j < TQ; ++j) {
-          const int64_t q = qb + 32 * j + l32;
-          if (q >= a.Qn) continue;
-#pragma unroll
-          for (int gg = 0; gg < 4; ++gg) {
-            const int64_t p = pb + 32 * i + 8 * gg + 4 * h;
-            store4<Op>(a, q, p, acc[i][j][4 * gg + 0], acc[i][j][4 * gg + 1], acc[i][j][4 * gg + 2],
-                       acc[i][j][4 * gg + 3]);
-          }
-        }
-    }
+    // Persistent: the stores drain while the next tile's stages (already
+    // copied) run.
+    direct_epilogue(tile);
     tile += step;
     if (tile >= ntiles) break;
     cur = nxt;
@@ -349,21 +358,26 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   // Copies issued past the last tile read zeros; let them land before exit.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   if constexpr (!PERSIST) {
-    // One tile per workgroup: the stage buffers are free for an LDS-staged
-    // epilogue once every wave is past its last read.
-    __syncthreads();
-    int64_t tp, tq;
-    tile_map(a.tiles_p, a.tiles_q, a.group, tile, &tp, &tq);
-    static_assert(Cfg::WTQ * 256 * NW <= 2 * Cfg::STAGE, "staging fits in the stage buffers");
-    staged_epilogue<Op, Cfg::WTP, Cfg::WTQ, TP, TQ>(a, smem + wave_u * (Cfg::WTQ * 256), acc, lane,
-                                                     tp * Cfg::BP + wp * Cfg::WTP, tq * Cfg::BQ + wq * Cfg::WTQ);
+    if constexpr (Cfg::STAGED_EPI) {
+      // One tile per workgroup: the stage buffers are free for an LDS-staged
+      // epilogue once every wave is past its last read.
+      __syncthreads();
+      int64_t tp, tq;
+      tile_map(a.tiles_p, a.tiles_q, a.group, tile, &tp, &tq);
+      static_assert(!Cfg::STAGED_EPI || Cfg::WTQ * 256 * NW <= 2 * Cfg::STAGE, "staging fits in the stage buffers");
+      staged_epilogue<Op, Cfg::WTP, Cfg::WTQ, TP, TQ>(a, smem + wave_u * (Cfg::WTQ * 256), acc, lane,
+                                                       tp * Cfg::BP + wp * Cfg::WTP, tq * Cfg::BQ + wq * Cfg::WTQ);
+    } else {
+      direct_epilogue(tile);
+    }
   }
 }
 
-template <class Op, bool PERSIST, bool PKM>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <class Op, bool PERSIST, bool PKM, int BP, int BQ>
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(TnCfg<Op, PKM, BP, BQ>::WPE, TnCfg<Op, PKM, BP, BQ>::WPE)))
 gemm_tn_kernel(const GemmArgs a) {
-  gemm_tn_body<Op, PERSIST, PKM>(a);
+  gemm_tn_body<Op, PERSIST, PKM, BP, BQ>(a);
 }
 
 }  // namespace dg

@@ -142,3 +142,33 @@ def test_kernel_config_description(lib):
     assert "f32_nn" in buf.value.decode()
     assert lib.dgemm_kernel_config(1, 1, 0, 5, 5, buf, 256) == 0
     assert lib.dgemm_kernel_config(1, 9, 5, 5, 5, buf, 256) == 4
+
+
+def _kernel(lib, dt, layout, M, N, K):
+    buf = ctypes.create_string_buffer(256)
+    assert lib.dgemm_kernel_config(dt, layout, M, N, K, buf, 256) == 0
+    return buf.value.decode()
+
+
+# Tile choice of the four-wave kernel: rounds of workgroups over 256 CUs
+# times the time of one round. 256 x 256 tiles cost 1 per round, 128 x 128
+# ones (two per CU) 1/0.78 * 1/2, 256 x 128 ones 1/0.76 * 1/2.
+@pytest.mark.parametrize("M,N,K,tile16,tile8nn", [
+    (8192, 8192, 8192, "256x256", "256x256"),    # 1024 tiles: 4 rounds vs 8 of 128 x 128
+    (4096, 4096, 4096, "256x256", "256x256"),    # one full round vs two
+    (3072, 4096, 8192, "256x256", "256x256"),    # 192 tiles: one round vs two
+    (5120, 5120, 1024, "256x256", "256x256"),    # 400 tiles: 2 rounds (2) vs 4 (2.56)
+    (4352, 4352, 1024, "128x128", "256x128"),    # 289 tiles: 2 rounds (2) vs 3 (1.92)
+    (2048, 2048, 2048, "128x128", "256x128"),    # 64 tiles leave 192 CUs idle
+    (300, 521, 512, "128x128", "256x128"),
+])
+def test_tile_choice(lib, M, N, K, tile16, tile8nn):
+    for dt in (1, 2, 3):
+        for layout in (0, 1):
+            d = _kernel(lib, dt, layout, M, N, K)
+            want = tile8nn if (dt, layout) == (3, 0) else tile16
+            assert f"_{want}_w4" in d, (dt, layout, d)
+    # FP8 TN at 256 x 256 runs persistent workgroups, a multiple of the 8 XCDs.
+    assert "persistent" in _kernel(lib, 3, 1, 5120, 5120, 1024)
+    # K not a whole number of 16-byte chunks: the eight-wave kernel.
+    assert "_w4" not in _kernel(lib, 2, 1, 4096, 4096, 4100)
