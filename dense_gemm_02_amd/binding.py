@@ -21,7 +21,11 @@ _LAYOUTS = {"nn": DGEMM_NN, "tn": DGEMM_TN}
 class DgemmError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
-        super().__init__(f"{what}: {gemm_strerror(status)} (status {status})")
+        msg = f"{what}: {gemm_strerror(status)} (status {status})"
+        if status == 7 and _lib is not None:
+            code = _lib.dgemm_last_hip_error()
+            msg += f" [hipError {code}: {_lib.dgemm_hip_error_string(code).decode()}]"
+        super().__init__(msg)
 
 
 def library_path() -> str:
@@ -39,12 +43,24 @@ def load_library():
     path = library_path()
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built; run __graft_entry__.build() first")
+    # One HIP runtime per process.  PyTorch ships its own copy of the HIP
+    # runtime (soname libamdhip64.so.7) and loads it by another file name, so
+    # if libdgemm.so came first the process would hold two runtimes, and the
+    # one initialised second finds no device (hipErrorNoDevice at launch).
+    # With torch loaded first, libdgemm.so binds to torch's copy by soname.
+    import torch  # noqa: F401
     L = ctypes.CDLL(path)
     i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     for name in ("gemm_f32", "gemm_f16", "gemm_bf16", "gemm_fp8"):
         fn = getattr(L, name)
         fn.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, vp]
         fn.restype = ci
+    L.gemm_fp8_scaled.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, ci, vp]
+    L.gemm_fp8_scaled.restype = ci
+    L.dgemm_last_hip_error.argtypes = []
+    L.dgemm_last_hip_error.restype = ci
+    L.dgemm_hip_error_string.argtypes = [ci]
+    L.dgemm_hip_error_string.restype = ctypes.c_char_p
     L.gemm_strerror.argtypes = [ci]
     L.gemm_strerror.restype = ctypes.c_char_p
     L.dgemm_tile_map.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
@@ -99,6 +115,19 @@ def gemm_fp8(M, N, K, A, lda, B, ldb, C, ldc, layout="tn", stream=None):
     _raw("gemm_fp8", M, N, K, A, lda, B, ldb, C, ldc, layout, stream)
 
 
+def gemm_fp8_scaled(M, N, K, A, lda, B, ldb, C, ldc, scale_a, n_scale_a, scale_b, n_scale_b, layout="tn",
+                    stream=None):
+    """Raw-pointer call with FP32 scale factors (device addresses): n_scale_a
+    is 1 (per tensor) or M (per row of A), n_scale_b is 1 or N (per column
+    of B)."""
+    L = load_library()
+    lay = _LAYOUTS.get(layout, layout) if isinstance(layout, str) else layout
+    st = L.gemm_fp8_scaled(int(M), int(N), int(K), A, int(lda), B, int(ldb), C, int(ldc), scale_a, int(n_scale_a),
+                           scale_b, int(n_scale_b), int(lay), _stream_handle(stream))
+    if st != 0:
+        raise DgemmError(st, "gemm_fp8_scaled")
+
+
 _BY_DTYPE = {"f32": gemm_f32, "f16": gemm_f16, "bf16": gemm_bf16, "fp8": gemm_fp8}
 _ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 
@@ -118,3 +147,20 @@ def gemm(dtype, layout, M, N, K, A, lda, B, ldb, C, ldc, stream=None):
     if C.element_size() != cbytes:
         raise TypeError(f"{dtype} output needs {cbytes}-byte elements")
     _BY_DTYPE[dtype](M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, layout, stream)
+
+
+def gemm_scaled(layout, M, N, K, A, lda, B, ldb, C, ldc, scale_a, scale_b, stream=None):
+    """Tensor-level FP8 call with scale factors: A, B hold E4M3 bytes, C FP32
+    storage, scale_a / scale_b are FP32 device tensors of 1 or M / 1 or N
+    values."""
+    import torch
+    for t in (A, B, C, scale_a, scale_b):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError("A, B, C and the scale factors must be device tensors")
+    if A.element_size() != 1 or B.element_size() != 1 or C.element_size() != 4:
+        raise TypeError("fp8 operands need 1-byte elements and a 4-byte output")
+    for t in (scale_a, scale_b):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError("scale factors must be contiguous float32 tensors")
+    gemm_fp8_scaled(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, scale_a.data_ptr(),
+                    scale_a.numel(), scale_b.data_ptr(), scale_b.numel(), layout, stream)

@@ -121,6 +121,11 @@ struct GemmArgs {
   int64_t tiles_p, tiles_q, group;
   int vec_store;     // C and ldc allow 4-element vector stores
   int vec16;         // C and ldc allow 16-byte stores
+  // Scale factors (FP8 scaled entry point only): D[p][q] is multiplied by
+  // sp[p] * sq[q] (sp_row / sq_row = 1) or by sp[0] / sq[0] (= 0).
+  const float* sp;
+  const float* sq;
+  int sp_row, sq_row;
 };
 
 }  // namespace dg

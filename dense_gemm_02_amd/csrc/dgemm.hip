@@ -2,7 +2,8 @@
 //
 // Host side of every call: validate the arguments, map (A, B, C, layout) onto
 // the kernels' (P, Q, D) form, pick a tile configuration, and launch on the
-// caller's stream.  No allocation, no synchronisation, no global state.
+// caller's stream.  No allocation, no synchronisation; the only state is a
+// thread-local copy of the last HIP error code.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -17,12 +18,21 @@
 namespace dg {
 namespace {
 
-enum Dtype { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };
+// hipError_t behind the calling thread's most recent DGEMM_ERR_HIP.
+thread_local int g_last_hip_error = 0;
+
+int hip_failed(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return DGEMM_ERR_HIP;
+}
+
+// DT_FP8S: FP8 with scale factors (gemm_fp8_scaled).
+enum Dtype { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3, DT_FP8S = 4 };
 
 constexpr int64_t kMaxDescBytes = (int64_t(1) << 31) - 64;
 
-int in_elem(int dt) { return dt == DT_F32 ? 4 : (dt == DT_FP8 ? 1 : 2); }
-int out_elem(int dt) { return (dt == DT_F32 || dt == DT_FP8) ? 4 : 2; }
+int in_elem(int dt) { return dt == DT_F32 ? 4 : ((dt == DT_FP8 || dt == DT_FP8S) ? 1 : 2); }
+int out_elem(int dt) { return (dt == DT_F32 || dt == DT_FP8 || dt == DT_FP8S) ? 4 : 2; }
 
 // A launchable configuration: a kernel symbol plus its tile geometry.
 // Persistent kernels run at most one workgroup per CU and walk the tiles.
@@ -143,16 +153,20 @@ Launch select(int dt, int layout, int64_t M, int64_t N, int64_t K) {
       static const char* const f16t[3] = {"f16_tn_256x256_w4", nullptr, "f16_tn_128x128_w4"};
       static const char* const bf16t[3] = {"bf16_tn_256x256_w4", nullptr, "bf16_tn_128x128_w4"};
       static const char* const fp8t[3] = {"fp8_tn_256x256_w4_persistent", nullptr, "fp8_tn_128x128_w4"};
+      static const char* const fp8sn[3] = {"fp8s_nn_256x256_w4_persistent", "fp8s_nn_256x128_w4", nullptr};
+      static const char* const fp8st[3] = {"fp8s_tn_256x256_w4_persistent", nullptr, "fp8s_tn_128x128_w4"};
       if (nn) {
         switch (dt) {
           case DT_F16: return tn_pick<OpF16, true>(f16n, Pn, Qn);
           case DT_BF16: return tn_pick<OpBF16, true>(bf16n, Pn, Qn);
+          case DT_FP8S: return tn_pick<OpFP8S, true>(fp8sn, Pn, Qn);
           default: return tn_pick<OpFP8, true>(fp8n, Pn, Qn);
         }
       }
       switch (dt) {
         case DT_F16: return tn_pick<OpF16, false>(f16t, Pn, Qn);
         case DT_BF16: return tn_pick<OpBF16, false>(bf16t, Pn, Qn);
+        case DT_FP8S: return tn_pick<OpFP8S, false>(fp8st, Pn, Qn);
         default: return tn_pick<OpFP8, false>(fp8t, Pn, Qn);
       }
     }
@@ -161,6 +175,7 @@ Launch select(int dt, int layout, int64_t M, int64_t N, int64_t K) {
     case DT_F32:  return nn ? f32_launch<true>("f32_nn_128x128") : f32_launch<false>("f32_tn_128x128");
     case DT_F16:  return nn ? mfma_launch<OpF16, true>("f16_nn_256x256") : mfma_launch<OpF16, false>("f16_tn_256x256");
     case DT_BF16: return nn ? mfma_launch<OpBF16, true>("bf16_nn_256x256") : mfma_launch<OpBF16, false>("bf16_tn_256x256");
+    case DT_FP8S: return nn ? mfma_launch<OpFP8S, true>("fp8s_nn_256x256") : mfma_launch<OpFP8S, false>("fp8s_tn_256x256");
     default:      return nn ? mfma_launch<OpFP8, true>("fp8_nn_256x256") : mfma_launch<OpFP8, false>("fp8_tn_256x256");
   }
 }
@@ -171,13 +186,23 @@ struct Plan {
   int64_t grid;
 };
 
+// Scale factors of gemm_fp8_scaled: na values at sa (1 or M), nb at sb (1 or N).
+struct Scales {
+  const float* sa;
+  int64_t na;
+  const float* sb;
+  int64_t nb;
+};
+
 // Validation in the documented order, then the (P, Q, D) mapping.
 int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-         void* C, int64_t ldc, int layout, Plan* out, bool check_pointers) {
+         void* C, int64_t ldc, int layout, Plan* out, bool check_pointers, const Scales* sc = nullptr) {
   if (layout != DGEMM_NN && layout != DGEMM_TN) return DGEMM_ERR_INVALID_LAYOUT;
   if (M < 0 || N < 0 || K < 0) return DGEMM_ERR_INVALID_DIM;
+  if (sc && ((sc->na != 1 && sc->na != M) || (sc->nb != 1 && sc->nb != N))) return DGEMM_ERR_INVALID_DIM;
   if (M == 0 || N == 0) { out->grid = 0; return DGEMM_OK; }
   if (check_pointers && ((K > 0 && (A == nullptr || B == nullptr)) || C == nullptr)) return DGEMM_ERR_NULL_POINTER;
+  if (check_pointers && sc && (sc->sa == nullptr || sc->sb == nullptr)) return DGEMM_ERR_NULL_POINTER;
   const bool nn = layout == DGEMM_NN;
   const int64_t min_lda = K > 0 ? K : 1;
   const int64_t min_ldb = nn ? N : (K > 0 ? K : 1);
@@ -188,6 +213,7 @@ int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
       ((((uintptr_t)A) & 15) != 0 || (((uintptr_t)B) & 15) != 0 || ((lda * e) & 15) != 0 || ((ldb * e) & 15) != 0))
     return DGEMM_ERR_MISALIGNED;
   if (((uintptr_t)C) % (uintptr_t)out_elem(dt) != 0) return DGEMM_ERR_MISALIGNED;
+  if (sc && ((((uintptr_t)sc->sa) & 3) != 0 || (((uintptr_t)sc->sb) & 3) != 0)) return DGEMM_ERR_MISALIGNED;
 
   const bool skinny = use_skinny(dt, layout, M);
   Launch L = skinny ? select_skinny(dt, M) : select(dt, layout, M, N, K);
@@ -200,6 +226,14 @@ int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
     g.Q = (const char*)A; g.ldq = lda * e; g.Qn = M;
   }
   g.C = C; g.ldc = ldc; g.K = K;
+  if (sc) {
+    // Factor vectors are addressed through buffer descriptors in bytes.
+    if (sc->na * 4 > kMaxDescBytes || sc->nb * 4 > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
+    g.sp = nn ? sc->sb : sc->sa;
+    g.sp_row = (nn ? sc->nb : sc->na) > 1 ? 1 : 0;
+    g.sq = nn ? sc->sa : sc->sb;
+    g.sq_row = (nn ? sc->na : sc->nb) > 1 ? 1 : 0;
+  }
   // Descriptor ranges must stay below 2^31 bytes.
   if ((int64_t)L.bq * g.ldq > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
   if (!L.p_trans && (int64_t)L.bp * g.ldp > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
@@ -219,25 +253,26 @@ int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
 }
 
 int run(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-        void* C, int64_t ldc, int layout, void* stream) {
+        void* C, int64_t ldc, int layout, void* stream, const Scales* sc = nullptr) {
   Plan pl;
-  const int st = plan(dt, M, N, K, A, lda, B, ldb, C, ldc, layout, &pl, true);
+  const int st = plan(dt, M, N, K, A, lda, B, ldb, C, ldc, layout, &pl, true, sc);
   if (st != DGEMM_OK || pl.grid == 0) return st;
   if (pl.L.persistent) {
     // One workgroup per CU, rounded down to a multiple of the XCD count so
     // that every tile of a workgroup maps to the workgroup's own XCD.
     int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      return DGEMM_ERR_HIP;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_failed(e);
+    if (cus <= 0) return hip_failed(hipErrorInvalidValue);
     if (cus >= kXcds) cus -= cus % kXcds;
     if (pl.grid > cus) pl.grid = cus;
   }
   void* args[] = {(void*)&pl.g};
   const hipError_t err = hipLaunchKernel(pl.L.fn, dim3((unsigned)pl.grid), dim3(pl.L.threads), args, 0,
                                          (hipStream_t)stream);
-  if (err != hipSuccess) return DGEMM_ERR_HIP;
-  return hipGetLastError() == hipSuccess ? DGEMM_OK : DGEMM_ERR_HIP;
+  if (err != hipSuccess) return hip_failed(err);
+  return DGEMM_OK;
 }
 
 }  // namespace
@@ -265,6 +300,13 @@ int gemm_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, con
   return dg::run(dg::DT_FP8, M, N, K, A, lda, B, ldb, C, ldc, layout, stream);
 }
 
+int gemm_fp8_scaled(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+                    float* C, int64_t ldc, const float* scale_a, int64_t n_scale_a, const float* scale_b,
+                    int64_t n_scale_b, int layout, void* stream) {
+  const dg::Scales sc{scale_a, n_scale_a, scale_b, n_scale_b};
+  return dg::run(dg::DT_FP8S, M, N, K, A, lda, B, ldb, C, ldc, layout, stream, &sc);
+}
+
 const char* gemm_strerror(int status) {
   switch (status) {
     case DGEMM_OK: return "success";
@@ -279,6 +321,10 @@ const char* gemm_strerror(int status) {
   }
 }
 
+int dgemm_last_hip_error(void) { return dg::g_last_hip_error; }
+
+const char* dgemm_hip_error_string(int code) { return hipGetErrorString((hipError_t)code); }
+
 int dgemm_tile_map(int64_t tiles_p, int64_t tiles_q, int64_t group, int64_t pid, int64_t* tile_p, int64_t* tile_q) {
   if (tiles_p <= 0 || tiles_q <= 0 || group <= 0 || pid < 0 || pid >= tiles_p * tiles_q || !tile_p || !tile_q)
     return -1;
@@ -292,7 +338,7 @@ int64_t dgemm_lds_bytes(int bm, int bn, int bk, int elem, int pad_bytes, int buf
 }
 
 int dgemm_kernel_config(int dtype, int layout, int64_t M, int64_t N, int64_t K, char* buf, int64_t len) {
-  if (dtype < 0 || dtype > 3) return DGEMM_ERR_UNSUPPORTED;
+  if (dtype < 0 || dtype > 4) return DGEMM_ERR_UNSUPPORTED;
   const int e = dg::in_elem(dtype);
   const bool nn = layout == DGEMM_NN;
   // Minimal legal, aligned leading dimensions for the description.

@@ -42,6 +42,7 @@ struct OpF16 {
   static constexpr int KI = 16;    // k per MFMA
   static constexpr int FC = 1;     // 16-byte chunks per lane per operand per MFMA
   static constexpr int OE = 2;     // bytes per output element
+  static constexpr bool SCALED = false;  // scale factors applied in the epilogue
   typedef f16x8 Frag;
   __device__ static Frag frag(const char* base, const uint32_t* off) { return *(const Frag*)(base + off[0]); }
   __device__ static f32x16 mma(Frag a, Frag b, f32x16 c) {
@@ -59,6 +60,7 @@ struct OpF16 {
 
 struct OpBF16 {
   static constexpr int ELEM = 2, KI = 16, FC = 1, OE = 2;
+  static constexpr bool SCALED = false;
   typedef bf16x8 Frag;
   __device__ static Frag frag(const char* base, const uint32_t* off) { return *(const Frag*)(base + off[0]); }
   __device__ static f32x16 mma(Frag a, Frag b, f32x16 c) {
@@ -76,6 +78,7 @@ struct OpBF16 {
 
 struct OpFP8 {
   static constexpr int ELEM = 1, KI = 64, FC = 2, OE = 4;
+  static constexpr bool SCALED = false;
   typedef i32x8 Frag;
   // 32 bytes of k per lane, read as two 16-byte (swizzled) chunks.
   __device__ static Frag frag(const char* base, const uint32_t* off) {
@@ -94,6 +97,14 @@ struct OpFP8 {
                                              2, 3, 4, 5, 6, 7);
     return mma(av, bv, c);
   }
+};
+
+// FP8 with per-tensor or per-row scale factors: the same MFMAs, with the
+// FP32 accumulators scaled before the store ("FP8 GEMM Optimization on AMD
+// RDNA 4", section "What Changes at FP8": the factors a quantized kernel
+// carries are applied after the accumulation).
+struct OpFP8S : OpFP8 {
+  static constexpr bool SCALED = true;
 };
 
 // Zero the bytes of a 16-byte chunk at and beyond `valid_bytes` (0..16).
@@ -137,6 +148,49 @@ __device__ __forceinline__ void store4(const GemmArgs& a, int64_t q, int64_t p, 
   }
 }
 
+// Scale factors of one wave's tile (FP8 scaled entry point), applied as the
+// accumulators are converted: D[p][q] = acc * (sp(p) * sq(q)), each product
+// rounded to FP32, where sp(p) = a.sp[p] (a.sp_row) or a.sp[0], and likewise
+// sq.  Lane l stores q = qbase + 32 j + l % 32, whose factors it holds for the
+// whole epilogue, and groups of four consecutive p, whose factors it fetches
+// per group.  Per-row factors are read through buffer descriptors sized to
+// the vectors, so a p or q past the edge reads 0 (never stored).
+template <int TQ>
+struct EpiScale {
+  float fq[TQ];
+  __device__ void init(const GemmArgs& a, int lane, int64_t qbase) {
+    if (a.sq_row) {
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.sq, (uint32_t)(a.Qn * 4));
+#pragma unroll
+      for (int j = 0; j < TQ; ++j)
+        fq[j] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rq, (int)((qbase + 32 * j + (lane & 31)) * 4), 0, 0));
+    } else {
+      const float f = a.sq[0];
+#pragma unroll
+      for (int j = 0; j < TQ; ++j) fq[j] = f;
+    }
+  }
+  __device__ static f32x4 p4(const GemmArgs& a, int64_t p) {
+    if (!a.sp_row) {
+      const float f = a.sp[0];
+      return f32x4{f, f, f, f};
+    }
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.sp, (uint32_t)(a.Pn * 4));
+    f32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      r[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, (int)((p + e) * 4), 0, 0));
+    return r;
+  }
+  __device__ void apply(const f32x4& fp, int j, float& v0, float& v1, float& v2, float& v3) const {
+    v0 *= fp[0] * fq[j];
+    v1 *= fp[1] * fq[j];
+    v2 *= fp[2] * fq[j];
+    v3 *= fp[3] * fq[j];
+  }
+};
+
 // Epilogue D[p][q] -> C[q*ldc + p] for one wave's WTP x WTQ tile, staged
 // through LDS.  Each lane holds four consecutive p of one q per accumulator
 // group, so a direct store writes 8 or 16 bytes into each of 32 different
@@ -161,25 +215,32 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& a, char* reg, co
   static_assert(RB == 256, "staged rows are 256 bytes");
   static_assert(WTQ % 4 == 0, "four rows per read-back instruction");
   const int l32 = lane & 31, h = lane >> 5;
+  [[maybe_unused]] EpiScale<TQ> sc;
+  if constexpr (Op::SCALED) sc.init(a, lane, qbase);
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
 #pragma unroll
     for (int i = 0; i < TPP; ++i)
 #pragma unroll
-      for (int j = 0; j < TQ; ++j)
+      for (int g = 0; g < 4; ++g) {
+        [[maybe_unused]] f32x4 fp;
+        if constexpr (Op::SCALED) fp = EpiScale<TQ>::p4(a, pbase + 32 * (pass * TPP + i) + 8 * g + 4 * h);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int j = 0; j < TQ; ++j) {
           const f32x16& v = acc[pass * TPP + i][j];
+          float v0 = v[4 * g], v1 = v[4 * g + 1], v2 = v[4 * g + 2], v3 = v[4 * g + 3];
+          if constexpr (Op::SCALED) sc.apply(fp, j, v0, v1, v2, v3);
           const int row = 32 * j + l32;
           const int slot = (8 * i + 2 * g + h) ^ (row % NSL);
           char* dst = reg + row * RB + slot * SS;
           if constexpr (OE == 4) {
-            *(f32x4*)dst = f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+            *(f32x4*)dst = f32x4{v0, v1, v2, v3};
           } else {
             typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-            *(u32x2*)dst = u32x2{Op::pack2(v[4 * g], v[4 * g + 1]), Op::pack2(v[4 * g + 2], v[4 * g + 3])};
+            *(u32x2*)dst = u32x2{Op::pack2(v0, v1), Op::pack2(v2, v3)};
           }
         }
+      }
     const int m = lane & 15;                  // 16-byte chunk within a row
 #pragma unroll
     for (int it = 0; it < WTQ / 4; ++it) {

@@ -328,18 +328,27 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     int64_t tp, tq;
     tile_map(a.tiles_p, a.tiles_q, a.group, t, &tp, &tq);
     const int64_t pb = tp * Cfg::BP + wp * Cfg::WTP, qb = tq * Cfg::BQ + wq * Cfg::WTQ;
+    [[maybe_unused]] EpiScale<TQ> sc;
+    if constexpr (Op::SCALED) sc.init(a, lane, qb);
 #pragma unroll
     for (int i = 0; i < TP; ++i)
 #pragma unroll
-      for (int j = 0; j < TQ; ++j) {
-        const int64_t q = qb + 32 * j + l32;
-        if (q >= a.Qn) continue;
+      for (int gg = 0; gg < 4; ++gg) {
+        const int64_t p = pb + 32 * i + 8 * gg + 4 * h;
+        [[maybe_unused]] f32x4 fp;
+        if constexpr (Op::SCALED) fp = EpiScale<TQ>::p4(a, p);
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          const int64_t p = pb + 32 * i + 8 * gg + 4 * h;
-          store4<Op>(a, q, p, acc[i][j][4 * gg + 0], acc[i][j][4 * gg + 1], acc[i][j][4 * gg + 2],
-                     acc[i][j][4 * gg + 3]);
+        for (int j = 0; j < TQ; ++j) {
+          const int64_t q = qb + 32 * j + l32;
+          if (q >= a.Qn) continue;
+          float v0 = acc[i][j][4 * gg + 0], v1 = acc[i][j][4 * gg + 1], v2 = acc[i][j][4 * gg + 2],
+                v3 = acc[i][j][4 * gg + 3];
+          if constexpr (Op::SCALED) sc.apply(fp, j, v0, v1, v2, v3);
+          store4<Op>(a, q, p, v0, v1, v2, v3);
         }
+        // (Keeps the factor loads of later groups from being hoisted here,
+        // where the next tile's fragments already hold most registers.)
+        if constexpr (Op::SCALED) __builtin_amdgcn_sched_barrier(0);
       }
   };
   int g = 0;

@@ -25,7 +25,8 @@
  *
  * Memory and ownership.  A, B and C are DEVICE pointers owned by the caller;
  * the library never allocates, frees or retains them and keeps no mutable
- * global state, so calls are reentrant.  A and B must not overlap C.
+ * global state (beyond a thread-local error code), so calls are reentrant.
+ * A and B must not overlap C.
  * Alignment: A and B must be 16-byte aligned and lda*elem, ldb*elem must be
  * multiples of 16 bytes (elem = bytes per input element); C needs only its
  * element alignment (wider stores are used when C and ldc allow them).
@@ -37,7 +38,8 @@
  * stream) and the call returns without synchronising.  Faults inside the
  * kernel surface at the caller's next synchronisation.
  *
- * Errors.  Each call returns a dgemm_status and never prints or aborts.
+ * Errors.  Each call returns a dgemm_status and never prints or aborts; the
+ * only state kept is the thread-local code of the last HIP failure.
  * Checks, in this order: layout -> DGEMM_ERR_INVALID_LAYOUT; any of M, N, K
  * negative -> DGEMM_ERR_INVALID_DIM; M == 0 or N == 0 -> DGEMM_OK with no
  * work; a NULL A or B (when K > 0) or NULL C -> DGEMM_ERR_NULL_POINTER; a
@@ -84,8 +86,39 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
 int gemm_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
              const uint8_t* B, int64_t ldb, float* C, int64_t ldc, int layout, void* stream);
 
+/*
+ * OCP FP8 E4M3 x E4M3 -> FP32 with scale factors, the per-tensor or per-row
+ * factors a quantized kernel carries on top of the raw FP8 product ("FP8
+ * GEMM Optimization on AMD RDNA 4", section "What Changes at FP8"):
+ *   C_ij = (sum_k A_ik * B_kj) * (sa_i * sb_j)
+ * with the sum accumulated in FP32 as in gemm_fp8 and each of the two
+ * products rounded to FP32 (round-to-nearest-even); IEEE rules apply to
+ * zero, infinite and NaN factors (K == 0 gives 0 * sa_i * sb_j).
+ * scale_a: DEVICE pointer to n_scale_a FP32 values, n_scale_a = 1 (sa_i =
+ *          scale_a[0] for every i) or M (sa_i = scale_a[i], one per row of A);
+ * scale_b: DEVICE pointer to n_scale_b FP32 values, 1 or N (one per column
+ *          of B, whatever the layout).
+ * Both are read by the kernel at run time (stream-ordered like A and B), must
+ * be 4-byte aligned, and are owned by the caller.  Other arguments, layouts
+ * and checks as gemm_fp8; additionally a count other than those above ->
+ * DGEMM_ERR_INVALID_DIM (checked with the dimensions), a NULL factor pointer
+ * -> DGEMM_ERR_NULL_POINTER, a misaligned one -> DGEMM_ERR_MISALIGNED.
+ */
+int gemm_fp8_scaled(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                    const uint8_t* B, int64_t ldb, float* C, int64_t ldc,
+                    const float* scale_a, int64_t n_scale_a, const float* scale_b, int64_t n_scale_b,
+                    int layout, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* gemm_strerror(int status);
+
+/*
+ * dgemm_last_hip_error: the hipError_t code behind the calling thread's most
+ * recent DGEMM_ERR_HIP (0 if there was none); dgemm_hip_error_string: HIP's
+ * static description of such a code.  For diagnostics only.
+ */
+int dgemm_last_hip_error(void);
+const char* dgemm_hip_error_string(int code);
 
 /*
  * Host-side introspection (no GPU work; used by host-only tests and reports).
@@ -105,7 +138,8 @@ const char* gemm_strerror(int status);
  * dgemm_kernel_config: writes a one-line description (kernel name, tile, wave
  * grid, LDS bytes, grid size) of the kernel a call with these arguments would
  * launch into buf (at most len bytes, NUL-terminated).  dtype: 0 f32, 1 f16,
- * 2 bf16, 3 fp8.  Returns 0, or a dgemm_status for invalid arguments.
+ * 2 bf16, 3 fp8, 4 fp8 with scale factors.  Returns 0, or a dgemm_status for
+ * invalid arguments.
  */
 int dgemm_tile_map(int64_t tiles_p, int64_t tiles_q, int64_t group, int64_t pid,
                    int64_t* tile_p, int64_t* tile_q);

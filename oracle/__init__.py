@@ -6,8 +6,9 @@ its Python binding) never imports it, and the two share no code.
 
 The arithmetic lives in ``oracle.cpp`` (built with g++, OpenMP over rows, FP64
 accumulation, one round-to-nearest-even rounding to the output format).  This
-module only builds and loads that library, marshals numpy arrays, and holds
-the acceptance check.
+module only builds and loads that library, marshals numpy arrays, applies
+the FP8 scale factors to the exact sums (``gemm_fp8_scaled``), and holds the
+acceptance check.
 
 Definition followed: "Optimizing GEMM in HIP", section "GEMM fundamentals"
 (C_ij = inner product of row i of A and column j of B); storage layouts from
@@ -112,6 +113,43 @@ def gemm(in_fmt, layout, M, N, K, A, lda, B, ldb, rows=None, threads=0, plain=Fa
     if rc != 0:
         raise ValueError("oracle_gemm rejected its arguments")
     return c, s, sab
+
+
+def scale_vector(scale, n):
+    """A factor vector of length 1 (one factor for all) or n, as FP64 values of n entries."""
+    f = np.asarray(scale, dtype=np.float32).reshape(-1).astype(np.float64)
+    if f.size == 1:
+        return np.full(n, f[0])
+    if f.size != n:
+        raise ValueError("a factor vector holds 1 or %d values" % n)
+    return f
+
+
+def gemm_fp8_scaled(layout, M, N, K, A, lda, B, ldb, scale_a, scale_b, rows=None, threads=0):
+    """E4M3 GEMM with per-tensor or per-row FP32 scale factors.
+
+    The factors a quantized FP8 kernel carries, applied after the sum ("FP8
+    GEMM Optimization on AMD RDNA 4", section "What Changes at FP8"):
+    C_ij = s_ij * sa_i * sb_j, where s_ij is the exact sum from ``gemm``
+    (exact in FP64 for E4M3 operands), sa_i = scale_a[i] (M values) or
+    scale_a[0] (one value), sb_j = scale_b[j] (N values) or scale_b[0].  The
+    product is formed in FP64 (sa_i * sb_j exactly) and rounded once more to
+    FP32 with round-to-nearest-even.  (s_ij * sa_i * sb_j can need more than
+    53 bits, so this is two roundings; they differ from one only when the
+    FP64 value falls exactly on an FP32 tie.)
+
+    Returns (c_bits, sab): FP32 output bits [len(rows) or M][N] and the
+    normaliser S_ij * |sa_i * sb_j| of the acceptance check.
+    """
+    _, s, sab = gemm(E4M3, layout, M, N, K, A, lda, B, ldb, rows=rows, threads=threads)
+    sa = scale_vector(scale_a, M)
+    sb = scale_vector(scale_b, N)
+    if rows is not None:
+        sa = sa[np.asarray(rows, dtype=np.int64)]
+    f = sa[:, None] * sb[None, :]
+    with np.errstate(invalid="ignore", over="ignore"):
+        c = encode(F32, s * f)
+        return c.astype(np.uint32), sab * np.abs(f)
 
 
 def decode(fmt, bits) -> np.ndarray:

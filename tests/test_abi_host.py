@@ -30,7 +30,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     syms = declared_symbols()
-    assert {"gemm_f32", "gemm_f16", "gemm_bf16", "gemm_fp8", "gemm_strerror"} <= set(syms)
+    assert {"gemm_f32", "gemm_f16", "gemm_bf16", "gemm_fp8", "gemm_fp8_scaled", "gemm_strerror"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -79,6 +79,28 @@ def test_argument_validation_order(lib, name, elem):
         oe = 4 if name in ("gemm_f32", "gemm_fp8") else 2
         if oe > 1:
             assert call(lib, name, 4, 4, al, FAKE, al, FAKE, al, FAKE + 1, 4, 1) == 5
+
+
+def scaled(lib, M, N, K, A, lda, B, ldb, C, ldc, sa, na, sb, nb, layout):
+    return lib.gemm_fp8_scaled(M, N, K, A, lda, B, ldb, C, ldc, sa, na, sb, nb, layout, None)
+
+
+def test_scaled_argument_validation(lib):
+    # the factor counts are checked with the dimensions, before the empty case
+    assert scaled(lib, 4, 5, 16, FAKE, 16, FAKE, 16, FAKE, 4, FAKE, 4, FAKE, 5, 9) == 4
+    assert scaled(lib, 4, 5, 16, FAKE, 16, FAKE, 16, FAKE, 4, FAKE, 2, FAKE, 5, 1) == 1
+    assert scaled(lib, 4, 5, 16, FAKE, 16, FAKE, 16, FAKE, 4, FAKE, 4, FAKE, 4, 1) == 1
+    assert scaled(lib, 4, 5, 16, FAKE, 16, FAKE, 16, FAKE, 4, FAKE, 0, FAKE, 1, 1) == 1
+    assert scaled(lib, 0, 5, 16, None, 16, None, 16, None, 4, None, 1, None, 5, 1) == 0
+    assert scaled(lib, 0, 5, 16, None, 16, None, 16, None, 4, None, 3, None, 5, 1) == 1
+    # null and misaligned factor pointers
+    assert scaled(lib, 4, 5, 16, FAKE, 16, FAKE, 16, FAKE, 4, None, 1, FAKE, 5, 1) == 2
+    assert scaled(lib, 4, 5, 16, FAKE, 16, FAKE, 16, FAKE, 4, FAKE, 4, None, 1, 1) == 2
+    assert scaled(lib, 4, 5, 16, FAKE, 16, FAKE, 16, FAKE, 4, FAKE + 2, 1, FAKE, 5, 1) == 5
+    assert scaled(lib, 4, 5, 16, FAKE, 16, FAKE, 16, FAKE, 8, FAKE, 1, FAKE + 1, 1, 0) == 5
+    # the operand checks of gemm_fp8 still apply
+    assert scaled(lib, 4, 5, 16, FAKE, 8, FAKE, 16, FAKE, 4, FAKE, 1, FAKE, 1, 1) == 3
+    assert scaled(lib, 4, 5, 16, FAKE + 4, 16, FAKE, 16, FAKE, 4, FAKE, 1, FAKE, 1, 1) == 5
 
 
 def test_size_limits_unsupported(lib):
@@ -163,10 +185,10 @@ def _kernel(lib, dt, layout, M, N, K):
     (300, 521, 512, "128x128", "256x128"),
 ])
 def test_tile_choice(lib, M, N, K, tile16, tile8nn):
-    for dt in (1, 2, 3):
+    for dt in (1, 2, 3, 4):
         for layout in (0, 1):
             d = _kernel(lib, dt, layout, M, N, K)
-            want = tile8nn if (dt, layout) == (3, 0) else tile16
+            want = tile8nn if dt >= 3 and layout == 0 else tile16
             assert f"_{want}_w4" in d, (dt, layout, d)
     # FP8 TN at 256 x 256 runs persistent workgroups, a multiple of the 8 XCDs.
     assert "persistent" in _kernel(lib, 3, 1, 5120, 5120, 1024)

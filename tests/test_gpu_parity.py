@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from dense_gemm_02_amd import inputs
-from gpu_util import alloc_c, c_host, compare, pad_untouched, run_gpu, say, to_dev
+from gpu_util import alloc_c, c_host, compare, pad_untouched, run_gpu, sample_rows, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +69,7 @@ def kernel_name(dtype, layout, M, N, K):
     import ctypes
     from dense_gemm_02_amd import binding
     buf = ctypes.create_string_buffer(256)
-    code = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}[dtype]
+    code = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3, "fp8s": 4}[dtype]
     assert binding.load_library().dgemm_kernel_config(code, 1 if layout == "tn" else 0, M, N, K, buf, 256) == 0
     return buf.value.decode()
 
@@ -83,7 +83,6 @@ def kernel_name(dtype, layout, M, N, K):
 # tiles per workgroup with its copy stream crossing tiles (rows sampled).
 @pytest.mark.parametrize("dtype,layout", [(d, l) for d in ("f16", "bf16", "fp8") for l in ("tn", "nn")])
 def test_four_wave_kernel(dtype, layout):
-    from gpu_util import sample_rows
     bk = {"f16": 64, "bf16": 64, "fp8": 128}[dtype]
     small = "256x128" if (dtype, layout) == ("fp8", "nn") else "128x128"
     shapes = [(512, 512, 2 * bk, small), (300, 521, 3 * bk, small), (5120, 5120, 3 * bk, "256x256"),
@@ -231,3 +230,97 @@ def test_skinny_split_k_path(dtype):
     p = make_problem(dtype, "tn", 16, 700, 4096, seed=7, dist="pm1")
     cij, _ = c_host(p, run_gpu(p))
     assert compare(p, cij, exact=True)[0]
+
+
+# ---- FP8 with scale factors (gemm_fp8_scaled) --------------------------------
+
+def _factors(rng, n, pow2=False):
+    e = rng.integers(-8, 9, n)
+    m = np.ones(n) if pow2 else rng.uniform(1.0, 2.0, n)
+    return (m * 2.0 ** e * rng.choice([-1.0, 1.0], n)).astype(np.float32)
+
+
+def run_scaled(p, sa, sb):
+    import torch
+    from dense_gemm_02_amd import binding
+    C = alloc_c(p)
+    binding.gemm_scaled(p.layout, p.M, p.N, p.K, to_dev(p.A), p.lda, to_dev(p.B), p.ldb, C, p.ldc,
+                        torch.from_numpy(sa).cuda(), torch.from_numpy(sb).cuda())
+    torch.cuda.synchronize()
+    return C
+
+
+def compare_scaled(p, cij, sa, sb, rows=None, exact=False):
+    from gpu_util import oracle
+    c_ref, sab = oracle.gemm_fp8_scaled(oracle.NN if p.layout == "nn" else oracle.TN, p.M, p.N, p.K, p.A, p.lda,
+                                        p.B, p.ldb, sa, sb, rows=rows)
+    got = cij if rows is None else cij[np.asarray(rows)]
+    if exact:
+        return oracle.bits_equal(got, c_ref, oracle.F32), 0.0
+    ok, err, _ = oracle.check(got, c_ref, sab, oracle.F32, oracle.TOL["fp8"])
+    return ok, err
+
+
+# Every kernel the FP8 path can pick (the eight-wave kernel for ragged K, the
+# four-wave tiles, the persistent 256 x 256 one with 400 tiles), per-tensor
+# and per-row factors, K = 0 (C = 0 * factors).  Tolerance relative to
+# |sa_i sb_j| * sum_k |a b|.
+@pytest.mark.parametrize("layout", ["tn", "nn"])
+@pytest.mark.parametrize("mode", ["tensor", "row"])
+def test_fp8_scaled_against_oracle(layout, mode):
+    rng = np.random.default_rng(6000 + (layout == "nn") + 2 * (mode == "row"))
+    shapes = [(1, 1, 1), (257, 129, 77), (33, 65, 300), (300, 521, 384), (512, 512, 256), (1000, 1100, 1168),
+              (5120, 5120, 384), (70, 90, 0)]
+    for idx, (M, N, K) in enumerate(shapes):
+        p = make_problem("fp8", layout, M, N, K, seed=6100 + idx, pad=idx % 2)
+        sa = _factors(rng, M if mode == "row" else 1)
+        sb = _factors(rng, N if mode == "row" else 1)
+        say(f"case scaled {kernel_name('fp8s', layout, M, N, K)} mode={mode} M={M} N={N} K={K}")
+        cij, pad = c_host(p, run_scaled(p, sa, sb))
+        assert pad_untouched(pad, "fp8")
+        rows = sample_rows(M, seed=idx) if M * N * max(K, 1) > 5e8 else None
+        ok, err = compare_scaled(p, cij, sa, sb, rows=rows)
+        assert ok, f"{layout} {mode} {(M, N, K)}: max err {err:.3e}"
+
+
+# +-1 operands and power-of-two factors: every result is exact, so the
+# output must match the oracle bit for bit; unit factors must reproduce
+# gemm_fp8's own output.
+@pytest.mark.parametrize("layout", ["tn", "nn"])
+def test_fp8_scaled_bit_exact(layout):
+    rng = np.random.default_rng(6200 + (layout == "nn"))
+    for idx, (M, N, K) in enumerate([(260, 300, 2048), (4096, 4096, 512), (77, 50, 100)]):
+        p = make_problem("fp8", layout, M, N, K, seed=6300 + idx, dist="pm1")
+        sa, sb = _factors(rng, M, pow2=True), _factors(rng, N, pow2=True)
+        say(f"case scaled pm1 {layout} M={M} N={N} K={K}")
+        cij, _ = c_host(p, run_scaled(p, sa, sb))
+        rows = sample_rows(M, seed=idx) if M > 1000 else None
+        ok, _ = compare_scaled(p, cij, sa, sb, rows=rows, exact=True)
+        assert ok, f"{(M, N, K)}: not bit-exact"
+        one = np.float32([1.0])
+        c1, _ = c_host(p, run_scaled(p, one, one))
+        c0, _ = c_host(p, run_gpu(p))
+        assert np.array_equal(c1, c0)
+
+
+# The binding must leave one HIP runtime in the process whichever is touched
+# first: a fresh interpreter loads the library before using torch, then runs
+# a small GEMM through it.
+def test_library_loaded_before_torch_use():
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "from dense_gemm_02_amd import binding\n"
+        "binding.load_library()\n"
+        "import torch\n"
+        "a = torch.ones(64, 64, dtype=torch.float32, device='cuda')\n"
+        "c = torch.empty(64, 64, dtype=torch.float32, device='cuda')\n"
+        "binding.gemm('f32', 'nn', 64, 64, 64, a, 64, a, 64, c, 64)\n"
+        "torch.cuda.synchronize()\n"
+        "assert bool((c == 64).all())\n"
+        "print('ok', flush=True)\n")
+    say("case fresh process: library loaded before torch use")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=180)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stdout + r.stderr

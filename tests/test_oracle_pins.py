@@ -18,8 +18,11 @@ what mathematics and library routines fix:
 * FP8 exactness: E4M3 values are multiples of 2^-9, so scaled integer matrix
   products give the exact sum;
 * thread-count independence and equality with the unblocked triple loop;
+* FP8 with scale factors: exact rationals s_ij * sa_i * sb_j rounded once,
+  a rank-one closed form, and reduction to the plain product at unit factors;
 * sensitivity: a transposed operand, a dropped term or a wrong sign each make
-  a pin fail.
+  a pin fail (and for the factors: reversed rows, a lost sign, a missing
+  factor).
 """
 
 from fractions import Fraction
@@ -411,6 +414,89 @@ def test_checker_accepts_and_rejects_as_predicted(oracle_lib):
     # bit equality treats +0 and -0 alike, nothing else
     assert oracle.bits_equal(np.array([0x8000], np.uint16), np.array([0], np.uint16), oracle.BF16)
     assert not oracle.bits_equal(np.array([0x8001], np.uint16), np.array([1], np.uint16), oracle.BF16)
+
+
+# ---- FP8 with scale factors -------------------------------------------------
+
+def _factors(rng, n):
+    """FP32 factors with full 24-bit significands, both signs, spread exponents."""
+    x = rng.uniform(1.0, 2.0, n) * 2.0 ** rng.integers(-8, 9, n) * rng.choice([-1.0, 1.0], n)
+    return x.astype(np.float32)
+
+
+def _scaled(p, sa, sb, rows=None):
+    return oracle.gemm_fp8_scaled(LAY[p.layout], p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, sa, sb, rows=rows)
+
+
+def _check_scaled_exact(p, sa, sb, c, sab):
+    """Bit-exact against exact-rational s_ij * sa_i * sb_j rounded once to FP32."""
+    S, SA = exact_sums(p)
+    for i in range(p.M):
+        for j in range(p.N):
+            fa = Fraction(float(sa[i if sa.size > 1 else 0]))
+            fb = Fraction(float(sb[j if sb.size > 1 else 0]))
+            want = frac_rne(S[i][j] * fa * fb, *FMT_PARAMS["f32"])
+            got = float(oracle.decode(oracle.F32, c[i:i + 1, j])[0])
+            if got != want:
+                return False
+            norm = float(SA[i][j] * abs(fa * fb))
+            assert abs(sab[i, j] - norm) <= 1e-15 * norm
+    return True
+
+
+def test_scaled_unit_factors_reduce_to_plain(oracle_lib):
+    for layout in ("nn", "tn"):
+        p = inputs.make("fp8", layout, 9, 7, 70, 31, "uniform4")
+        c0, _, sab0 = run(p)
+        c, sab = _scaled(p, np.float32([1.0]), np.float32([1.0]))
+        assert np.array_equal(c, c0) and np.array_equal(sab, sab0)
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+@pytest.mark.parametrize("mode", ["tensor", "row"])
+def test_scaled_bruteforce_exact_rationals(oracle_lib, layout, mode):
+    rng = np.random.default_rng(41 + (layout == "nn"))
+    for M, N, K in [(1, 1, 1), (3, 5, 7), (6, 4, 33), (2, 9, 64)]:
+        p = inputs.make("fp8", layout, M, N, K, 50 + K, "uniform4")
+        sa = _factors(rng, M if mode == "row" else 1)
+        sb = _factors(rng, N if mode == "row" else 1)
+        c, sab = _scaled(p, sa, sb)
+        assert _check_scaled_exact(p, sa, sb, c, sab)
+        if mode == "row":
+            # rows subset: the same values for the rows asked for
+            rows = np.array([M - 1, 0], dtype=np.int64)
+            cr, sabr = _scaled(p, sa, sb, rows=rows)
+            assert np.array_equal(cr, c[rows]) and np.array_equal(sabr, sab[rows])
+
+
+def test_scaled_closed_form_rank_one(oracle_lib):
+    # A = 1, B = 1 => C_ij = K * sa_i * sb_j: with power-of-two factors exact
+    # in FP32, and distinct per row / column so that a swapped role shows.
+    for layout in ("nn", "tn"):
+        M, N, K = 5, 3, 48
+        p = inputs.make("fp8", layout, M, N, K, 0, "ones")
+        sa = np.float32([2.0 ** e for e in (-3, 0, 1, 5, -7)])
+        sb = np.float32([-4.0, 0.5, 2.0 ** -10])
+        c, sab = _scaled(p, sa, sb)
+        want = K * np.outer(sa.astype(np.float64), sb.astype(np.float64))
+        assert np.array_equal(oracle.decode(oracle.F32, c), want)
+        assert np.array_equal(sab, np.abs(want))
+    # a zero factor gives an exact zero and a zero normaliser
+    c, sab = _scaled(p, np.float32([0.0]), sb)
+    assert np.all(oracle.decode(oracle.F32, c) == 0) and np.all(sab == 0)
+
+
+def test_scaled_pins_catch_planted_mistakes(oracle_lib):
+    rng = np.random.default_rng(77)
+    p = inputs.make("fp8", "nn", 4, 6, 20, 78, "uniform4")
+    sa, sb = _factors(rng, 4), _factors(rng, 6)
+    assert _check_scaled_exact(p, sa, sb, *_scaled(p, sa, sb))
+    # factors of A applied in reverse row order
+    assert not _check_scaled_exact(p, sa, sb, *_scaled(p, sa[::-1].copy(), sb))
+    # one factor's sign lost
+    assert not _check_scaled_exact(p, sa, sb, *_scaled(p, np.abs(sa), sb))
+    # only one of the two factors applied
+    assert not _check_scaled_exact(p, sa, sb, *_scaled(p, sa, np.float32([1.0])))
 
 
 # ---- sensitivity: planted mistakes must trip a pin ---------------------------
