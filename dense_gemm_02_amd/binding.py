@@ -57,6 +57,8 @@ def load_library():
         fn.restype = ci
     L.gemm_fp8_scaled.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, ci, vp]
     L.gemm_fp8_scaled.restype = ci
+    L.gemm_mxfp8.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, ci, vp]
+    L.gemm_mxfp8.restype = ci
     L.dgemm_last_hip_error.argtypes = []
     L.dgemm_last_hip_error.restype = ci
     L.dgemm_hip_error_string.argtypes = [ci]
@@ -128,6 +130,18 @@ def gemm_fp8_scaled(M, N, K, A, lda, B, ldb, C, ldc, scale_a, n_scale_a, scale_b
         raise DgemmError(st, "gemm_fp8_scaled")
 
 
+def gemm_mxfp8(M, N, K, A, lda, B, ldb, C, ldc, scale_a, ldsa, scale_b, ldsb, layout="tn", stream=None):
+    """Raw-pointer call with E8M0 block scales (device addresses): byte
+    scale_a[i*ldsa + b] scales k block b of row i of A, scale_b[j*ldsb + b]
+    block b of column j of B."""
+    L = load_library()
+    lay = _LAYOUTS.get(layout, layout) if isinstance(layout, str) else layout
+    st = L.gemm_mxfp8(int(M), int(N), int(K), A, int(lda), B, int(ldb), C, int(ldc), scale_a, int(ldsa), scale_b,
+                      int(ldsb), int(lay), _stream_handle(stream))
+    if st != 0:
+        raise DgemmError(st, "gemm_mxfp8")
+
+
 _BY_DTYPE = {"f32": gemm_f32, "f16": gemm_f16, "bf16": gemm_bf16, "fp8": gemm_fp8}
 _ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 
@@ -164,3 +178,18 @@ def gemm_scaled(layout, M, N, K, A, lda, B, ldb, C, ldc, scale_a, scale_b, strea
             raise TypeError("scale factors must be contiguous float32 tensors")
     gemm_fp8_scaled(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, scale_a.data_ptr(),
                     scale_a.numel(), scale_b.data_ptr(), scale_b.numel(), layout, stream)
+
+
+def gemm_mx(layout, M, N, K, A, lda, B, ldb, C, ldc, scale_a, ldsa, scale_b, ldsb, stream=None):
+    """Tensor-level MXFP8 call: A, B hold E4M3 bytes, C FP32 storage,
+    scale_a / scale_b E8M0 bytes (device tensors) with row pitches ldsa / ldsb."""
+    import torch
+    for t in (A, B, C, scale_a, scale_b):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError("A, B, C and the block scales must be device tensors")
+    if A.element_size() != 1 or B.element_size() != 1 or C.element_size() != 4:
+        raise TypeError("fp8 operands need 1-byte elements and a 4-byte output")
+    if scale_a.element_size() != 1 or scale_b.element_size() != 1:
+        raise TypeError("block scales are bytes")
+    gemm_mxfp8(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, scale_a.data_ptr(), ldsa,
+               scale_b.data_ptr(), ldsb, layout, stream)

@@ -126,6 +126,11 @@ struct GemmArgs {
   const float* sp;
   const float* sq;
   int sp_row, sq_row;
+  // E8M0 block scales (MXFP8 entry point only): row p of P has K/32 scale
+  // bytes at msp + p*ldsp, row q of Q at msq + q*ldsq.
+  const uint8_t* msp;
+  const uint8_t* msq;
+  int64_t ldsp, ldsq;
 };
 
 }  // namespace dg

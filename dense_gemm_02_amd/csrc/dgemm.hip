@@ -26,13 +26,16 @@ int hip_failed(hipError_t e) {
   return DGEMM_ERR_HIP;
 }
 
-// DT_FP8S: FP8 with scale factors (gemm_fp8_scaled).
-enum Dtype { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3, DT_FP8S = 4 };
+// DT_FP8S: FP8 with scale factors (gemm_fp8_scaled); DT_MX8: MXFP8 with
+// E8M0 block scales (gemm_mxfp8).
+enum Dtype { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3, DT_FP8S = 4, DT_MX8 = 5 };
+
+bool is_fp8(int dt) { return dt == DT_FP8 || dt == DT_FP8S || dt == DT_MX8; }
 
 constexpr int64_t kMaxDescBytes = (int64_t(1) << 31) - 64;
 
-int in_elem(int dt) { return dt == DT_F32 ? 4 : ((dt == DT_FP8 || dt == DT_FP8S) ? 1 : 2); }
-int out_elem(int dt) { return (dt == DT_F32 || dt == DT_FP8 || dt == DT_FP8S) ? 4 : 2; }
+int in_elem(int dt) { return dt == DT_F32 ? 4 : (is_fp8(dt) ? 1 : 2); }
+int out_elem(int dt) { return (dt == DT_F32 || is_fp8(dt)) ? 4 : 2; }
 
 // A launchable configuration: a kernel symbol plus its tile geometry.
 // Persistent kernels run at most one workgroup per CU and walk the tiles.
@@ -140,6 +143,18 @@ Launch select_skinny(int dt, int64_t M) {
 
 Launch select(int dt, int layout, int64_t M, int64_t N, int64_t K) {
   const bool nn = layout == DGEMM_NN;
+  if (dt == DT_MX8) {
+    // MXFP8 (K a multiple of 32) takes the four-wave kernel; below two
+    // stages only the one-tile-per-workgroup tiles.  K == 0 (C = 0, no
+    // scale is read) goes to the eight-wave kernel's zero fill.
+    if (K == 0) return nn ? mfma_launch<OpFP8, true>("fp8_nn_256x256") : mfma_launch<OpFP8, false>("fp8_tn_256x256");
+    const int64_t Pn = nn ? N : M, Qn = nn ? M : N;
+    if (K < 256) return nn ? tn_launch<OpMX8, true, 256, 128>("mx8_nn_256x128_w4")
+                           : tn_launch<OpMX8, false, 128, 128>("mx8_tn_128x128_w4");
+    static const char* const mxn[3] = {"mx8_nn_256x256_w4_persistent", "mx8_nn_256x128_w4", nullptr};
+    static const char* const mxt[3] = {"mx8_tn_256x256_w4_persistent", nullptr, "mx8_tn_128x128_w4"};
+    return nn ? tn_pick<OpMX8, true>(mxn, Pn, Qn) : tn_pick<OpMX8, false>(mxt, Pn, Qn);
+  }
   // K a whole number of 16-byte chunks and at least two stages: the
   // four-wave kernel (gemm_tn.hpp), tile chosen by shape; NN reads B with
   // transposing LDS reads.
@@ -194,26 +209,42 @@ struct Scales {
   int64_t nb;
 };
 
+// E8M0 block scales of gemm_mxfp8: row i of A has K/32 bytes at sa + i*ldsa,
+// column j of B K/32 bytes at sb + j*ldsb.
+struct MxScales {
+  const uint8_t* sa;
+  int64_t ldsa;
+  const uint8_t* sb;
+  int64_t ldsb;
+};
+
 // Validation in the documented order, then the (P, Q, D) mapping.
 int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-         void* C, int64_t ldc, int layout, Plan* out, bool check_pointers, const Scales* sc = nullptr) {
+         void* C, int64_t ldc, int layout, Plan* out, bool check_pointers, const Scales* sc = nullptr,
+         const MxScales* mx = nullptr) {
   if (layout != DGEMM_NN && layout != DGEMM_TN) return DGEMM_ERR_INVALID_LAYOUT;
   if (M < 0 || N < 0 || K < 0) return DGEMM_ERR_INVALID_DIM;
   if (sc && ((sc->na != 1 && sc->na != M) || (sc->nb != 1 && sc->nb != N))) return DGEMM_ERR_INVALID_DIM;
+  if (dt == DT_MX8 && K % 32 != 0) return DGEMM_ERR_INVALID_DIM;
   if (M == 0 || N == 0) { out->grid = 0; return DGEMM_OK; }
   if (check_pointers && ((K > 0 && (A == nullptr || B == nullptr)) || C == nullptr)) return DGEMM_ERR_NULL_POINTER;
   if (check_pointers && sc && (sc->sa == nullptr || sc->sb == nullptr)) return DGEMM_ERR_NULL_POINTER;
+  if (check_pointers && mx && K > 0 && (mx->sa == nullptr || mx->sb == nullptr)) return DGEMM_ERR_NULL_POINTER;
   const bool nn = layout == DGEMM_NN;
   const int64_t min_lda = K > 0 ? K : 1;
   const int64_t min_ldb = nn ? N : (K > 0 ? K : 1);
   const int64_t min_ldc = nn ? N : M;
   if (lda < min_lda || ldb < min_ldb || ldc < min_ldc) return DGEMM_ERR_INVALID_LD;
+  if (mx && (mx->ldsa < K / 32 || mx->ldsb < K / 32)) return DGEMM_ERR_INVALID_LD;
   const int e = in_elem(dt);
   if (check_pointers && K > 0 &&
       ((((uintptr_t)A) & 15) != 0 || (((uintptr_t)B) & 15) != 0 || ((lda * e) & 15) != 0 || ((ldb * e) & 15) != 0))
     return DGEMM_ERR_MISALIGNED;
   if (((uintptr_t)C) % (uintptr_t)out_elem(dt) != 0) return DGEMM_ERR_MISALIGNED;
   if (sc && ((((uintptr_t)sc->sa) & 3) != 0 || (((uintptr_t)sc->sb) & 3) != 0)) return DGEMM_ERR_MISALIGNED;
+  if (mx && K > 0 &&
+      ((((uintptr_t)mx->sa) & 3) != 0 || (((uintptr_t)mx->sb) & 3) != 0 || (mx->ldsa & 3) != 0 || (mx->ldsb & 3) != 0))
+    return DGEMM_ERR_MISALIGNED;
 
   const bool skinny = use_skinny(dt, layout, M);
   Launch L = skinny ? select_skinny(dt, M) : select(dt, layout, M, N, K);
@@ -234,6 +265,14 @@ int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
     g.sq = nn ? sc->sa : sc->sb;
     g.sq_row = (nn ? sc->na : sc->nb) > 1 ? 1 : 0;
   }
+  if (mx) {
+    // A tile's block scales are addressed through one descriptor in bytes.
+    if (256 * mx->ldsa > kMaxDescBytes || 256 * mx->ldsb > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
+    g.msp = nn ? mx->sb : mx->sa;
+    g.ldsp = nn ? mx->ldsb : mx->ldsa;
+    g.msq = nn ? mx->sa : mx->sb;
+    g.ldsq = nn ? mx->ldsa : mx->ldsb;
+  }
   // Descriptor ranges must stay below 2^31 bytes.
   if ((int64_t)L.bq * g.ldq > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
   if (!L.p_trans && (int64_t)L.bp * g.ldp > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
@@ -253,9 +292,9 @@ int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
 }
 
 int run(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-        void* C, int64_t ldc, int layout, void* stream, const Scales* sc = nullptr) {
+        void* C, int64_t ldc, int layout, void* stream, const Scales* sc = nullptr, const MxScales* mx = nullptr) {
   Plan pl;
-  const int st = plan(dt, M, N, K, A, lda, B, ldb, C, ldc, layout, &pl, true, sc);
+  const int st = plan(dt, M, N, K, A, lda, B, ldb, C, ldc, layout, &pl, true, sc, mx);
   if (st != DGEMM_OK || pl.grid == 0) return st;
   if (pl.L.persistent) {
     // One workgroup per CU, rounded down to a multiple of the XCD count so
@@ -307,6 +346,13 @@ int gemm_fp8_scaled(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t l
   return dg::run(dg::DT_FP8S, M, N, K, A, lda, B, ldb, C, ldc, layout, stream, &sc);
 }
 
+int gemm_mxfp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+               float* C, int64_t ldc, const uint8_t* scale_a, int64_t ldsa, const uint8_t* scale_b, int64_t ldsb,
+               int layout, void* stream) {
+  const dg::MxScales mx{scale_a, ldsa, scale_b, ldsb};
+  return dg::run(dg::DT_MX8, M, N, K, A, lda, B, ldb, C, ldc, layout, stream, nullptr, &mx);
+}
+
 const char* gemm_strerror(int status) {
   switch (status) {
     case DGEMM_OK: return "success";
@@ -338,7 +384,7 @@ int64_t dgemm_lds_bytes(int bm, int bn, int bk, int elem, int pad_bytes, int buf
 }
 
 int dgemm_kernel_config(int dtype, int layout, int64_t M, int64_t N, int64_t K, char* buf, int64_t len) {
-  if (dtype < 0 || dtype > 4) return DGEMM_ERR_UNSUPPORTED;
+  if (dtype < 0 || dtype > 5) return DGEMM_ERR_UNSUPPORTED;
   const int e = dg::in_elem(dtype);
   const bool nn = layout == DGEMM_NN;
   // Minimal legal, aligned leading dimensions for the description.

@@ -43,6 +43,7 @@ struct OpF16 {
   static constexpr int FC = 1;     // 16-byte chunks per lane per operand per MFMA
   static constexpr int OE = 2;     // bytes per output element
   static constexpr bool SCALED = false;  // scale factors applied in the epilogue
+  static constexpr bool MX = false;      // E8M0 block scales fed to the MFMA
   typedef f16x8 Frag;
   __device__ static Frag frag(const char* base, const uint32_t* off) { return *(const Frag*)(base + off[0]); }
   __device__ static f32x16 mma(Frag a, Frag b, f32x16 c) {
@@ -60,7 +61,7 @@ struct OpF16 {
 
 struct OpBF16 {
   static constexpr int ELEM = 2, KI = 16, FC = 1, OE = 2;
-  static constexpr bool SCALED = false;
+  static constexpr bool SCALED = false, MX = false;
   typedef bf16x8 Frag;
   __device__ static Frag frag(const char* base, const uint32_t* off) { return *(const Frag*)(base + off[0]); }
   __device__ static f32x16 mma(Frag a, Frag b, f32x16 c) {
@@ -78,7 +79,7 @@ struct OpBF16 {
 
 struct OpFP8 {
   static constexpr int ELEM = 1, KI = 64, FC = 2, OE = 4;
-  static constexpr bool SCALED = false;
+  static constexpr bool SCALED = false, MX = false;
   typedef i32x8 Frag;
   // 32 bytes of k per lane, read as two 16-byte (swizzled) chunks.
   __device__ static Frag frag(const char* base, const uint32_t* off) {
@@ -105,6 +106,27 @@ struct OpFP8 {
 // carries are applied after the accumulation).
 struct OpFP8S : OpFP8 {
   static constexpr bool SCALED = true;
+};
+
+// MXFP8: E4M3 operands with one E8M0 scale (2^(e - 127)) per 32 consecutive
+// k of each row of A and each column of B, as the block scales of the
+// scaled MFMA take them.  That instruction splits its 64 k into two blocks
+// of 32: lane l (h = l / 32) holds row l % 32 with k 16h .. 16h + 15 in
+// bytes 0-15 and k 32 + 16h .. 32 + 16h + 15 in bytes 16-31, and the scale
+// in lane l applies to k block h of row l % 32 (determined on gfx950 with
+// one-hot operands: every byte position, its output row, its partner in the
+// other operand and the lane whose scale it takes).  opsel picks the byte of
+// the 32-bit scale register.
+struct OpMX8 : OpFP8 {
+  static constexpr bool MX = true;
+  template <int KK>
+  __device__ static f32x16 mma_mx(const u32x4 (&a)[2], const u32x4 (&b)[2], f32x16 c, uint32_t sa, uint32_t sb) {
+    const i32x8 av = __builtin_shufflevector(__builtin_bit_cast(i32x4, a[0]), __builtin_bit_cast(i32x4, a[1]), 0, 1,
+                                             2, 3, 4, 5, 6, 7);
+    const i32x8 bv = __builtin_shufflevector(__builtin_bit_cast(i32x4, b[0]), __builtin_bit_cast(i32x4, b[1]), 0, 1,
+                                             2, 3, 4, 5, 6, 7);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 2 * KK, (int)sa, 2 * KK, (int)sb);
+  }
 };
 
 // Zero the bytes of a 16-byte chunk at and beyond `valid_bytes` (0..16).

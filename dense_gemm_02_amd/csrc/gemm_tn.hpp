@@ -122,6 +122,9 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     const char* q;
     const char* p;
     uint32_t qn, pn;
+    const uint8_t* sq;   // MX: block scales of the tile's q and p rows
+    const uint8_t* sp;
+    uint32_t sqn, spn;
   };
   auto tile_src = [&](int64_t tile) {
     Src r;
@@ -133,18 +136,33 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       const int64_t prows = (a.Pn - p0) < Cfg::BP ? (a.Pn - p0) : Cfg::BP;
       r.q = a.Q + q0 * a.ldq;
       r.qn = (uint32_t)((qrows - 1) * a.ldq) + kbytes16;
+      if constexpr (Op::MX) {
+        // The caller provides rows * ld scale bytes; with K == 0 none at all.
+        r.sq = a.msq + q0 * a.ldsq;
+        r.sqn = K > 0 ? (uint32_t)(qrows * a.ldsq) : 0u;
+        r.sp = a.msp + p0 * a.ldsp;
+        r.spn = K > 0 ? (uint32_t)(prows * a.ldsp) : 0u;
+      }
       if constexpr (!PKM) {
         r.p = a.P + p0 * a.ldp;
         r.pn = (uint32_t)((prows - 1) * a.ldp) + kbytes16;
       } else {
+        // (K == 0 has no rows of P at all: an empty descriptor, not one
+        // whose (K - 1) * ldp term wraps around.)
         r.p = a.P + p0 * E;
-        r.pn = (uint32_t)((K - 1) * a.ldp) + (uint32_t)(((prows * E) + 15) & ~(int64_t)15);
+        r.pn = K > 0 ? (uint32_t)((K - 1) * a.ldp) + (uint32_t)(((prows * E) + 15) & ~(int64_t)15) : 0u;
       }
     } else {
       r.q = a.Q;
       r.p = a.P;
       r.qn = 0;
       r.pn = 0;
+      if constexpr (Op::MX) {
+        r.sq = a.msq;
+        r.sp = a.msp;
+        r.sqn = 0;
+        r.spn = 0;
+      }
     }
     return r;
   };
@@ -202,16 +220,22 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     if (isb || !PKM) {
       const int rr = isb ? r : r - TQ * FC;
       const int tile = rr / FC, f = rr % FC;
-      const uint32_t off = (uint32_t)((((kk * 2 + h) * FC + f) ^ sw_r) << 4);
+      // 16-byte chunk (kk*FC + f)*2 + h of the stage row: for FP8, lane half
+      // h takes chunks h and h + 2 of each 64-k step (the k order of the
+      // MFMA's two scale blocks, see OpMX8).
+      const uint32_t off = (uint32_t)(((((kk * FC + f) * 2 + h)) ^ sw_r) << 4);
       const char* base = sb + (isb ? qf_base : pf_base) + tile * 32 * ROWB;
       const u32x4 v = *(const u32x4*)(base + off);
       if (isb) fb[set][tile][f] = v; else fa[set][tile][f] = v;
     } else {
       const int rr = r - TQ * FC;
       const int tile = rr / Cfg::PRD, q8 = rr % Cfg::PRD;   // which 8-byte piece of the fragment
-      // k of this lane's row: the k-step, the lane half h = tg / 2 (its
-      // block of Op::KI / 2 k), the piece q8 (TRK k each), and tkey.
-      const int krow = kk * Op::KI + (tg >> 1) * (Op::KI / 2) + q8 * TRK + tkey;
+      // k of this lane's row: the k-step, the lane half h = tg / 2, the
+      // piece q8 (TRK k each), and tkey.  16-bit: half h holds k 8h .. 8h+7;
+      // FP8: pieces 0-1 hold k 16h .. 16h+15 and pieces 2-3 k 32+16h ..
+      // (the k order of the MFMA's scale blocks, see OpMX8).
+      const int krow = E == 2 ? kk * Op::KI + (tg >> 1) * (Op::KI / 2) + q8 * TRK + tkey
+                              : kk * Op::KI + (q8 >> 1) * 32 + (tg >> 1) * 16 + (q8 & 1) * 8 + tkey;
       const int unit = (wp * (Cfg::WTP / 32) + tile) ^ tkey;
       const char* src = sb + krow * Cfg::PROWB + unit * Cfg::UB + (tg & 1) * (16 * E) + (ts % (2 * E)) * 8;
       typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -238,9 +262,47 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   };
-  auto mfma_one = [&](int set, int t) {
+  // MX block scales: for the stage in use, lane l holds in scp[i] / scq[j]
+  // the scales of its row of P tile i / Q tile j for k blocks h and h + 2
+  // of the stage in bytes 0 and 2 (a stage is four blocks of 32 k: byte 2kk
+  // serves k-step kk).  The next stage's dwords are loaded into nsp / nsq
+  // one stage ahead, with the copies.
+  [[maybe_unused]] uint32_t scp[TP], scq[TQ], nsp[TP], nsq[TQ];
+  auto load_scales = [&](const Src& src, int t) {
+    if constexpr (Op::MX) {
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc(src.sp, src.spn), rq = make_rsrc(src.sq, src.sqn);
+#pragma unroll
+      for (int i = 0; i < TP; ++i)
+        nsp[i] = __builtin_amdgcn_raw_buffer_load_b32(
+            rp, (int)((wp * Cfg::WTP + 32 * i + l32) * a.ldsp + 4 * t), 0, 0);
+#pragma unroll
+      for (int j = 0; j < TQ; ++j)
+        nsq[j] = __builtin_amdgcn_raw_buffer_load_b32(
+            rq, (int)((wq * Cfg::WTQ + 32 * j + l32) * a.ldsq + 4 * t), 0, 0);
+    }
+  };
+  // Blocks at or past K/32 read as scale byte 0 (their data are zeros; a
+  // stray 255 would be NaN).
+  auto take_scales = [&](int t) {
+    if constexpr (Op::MX) {
+      const int64_t valid = K / 32 - 4 * (int64_t)t;
+      const uint32_t m = valid >= 4 ? ~0u : (valid <= 0 ? 0u : ((1u << (8 * valid)) - 1u));
+#pragma unroll
+      for (int i = 0; i < TP; ++i) scp[i] = (nsp[i] & m) >> (8 * h);
+#pragma unroll
+      for (int j = 0; j < TQ; ++j) scq[j] = (nsq[j] & m) >> (8 * h);
+    }
+  };
+  static_assert(!Op::MX || Cfg::KSTEPS == 2, "two k-steps of 64 per stage");
+  auto mfma_one = [&](int set, int t, int kk) {
     const int i = t / TQ, j = t % TQ;
-    acc[i][j] = Op::mma_parts(fa[set][i], fb[set][j], acc[i][j]);
+    if constexpr (Op::MX) {
+      if (kk == 0) acc[i][j] = Op::template mma_mx<0>(fa[set][i], fb[set][j], acc[i][j], scp[i], scq[j]);
+      else acc[i][j] = Op::template mma_mx<1>(fa[set][i], fb[set][j], acc[i][j], scp[i], scq[j]);
+    } else {
+      (void)kk;
+      acc[i][j] = Op::mma_parts(fa[set][i], fb[set][j], acc[i][j]);
+    }
   };
   auto read_slot = [](int r, int span) { return r * span / NREAD; };
   constexpr int LAST = (Cfg::KSTEPS - 1) & 1;
@@ -260,13 +322,17 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     const Rsrc rq1 = rsrc_at(n1 ? nx.q : cu.q, n1 ? nx.qn : cu.qn, t1, false);
     const Rsrc rp1 = rsrc_at(n1 ? nx.p : cu.p, n1 ? nx.pn : cu.pn, t1, PKM);
     const uint32_t kill1 = kill_at(t1);
+    if constexpr (Op::MX) {
+      take_scales(s);
+      load_scales(n1 ? nx : cu, t1);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk + 1 < Cfg::KSTEPS; ++kk) {
       const int span = kk + 2 == Cfg::KSTEPS ? NMFMA / 2 : NMFMA;
 #pragma unroll
       for (int t = 0; t < NMFMA; ++t) {
-        mfma_one(kk & 1, t);
+        mfma_one(kk & 1, t, kk);
 #pragma unroll
         for (int r = 0; r < NREAD; ++r)
           if (read_slot(r, span) == t) read_one(sb, kk + 1, (kk + 1) & 1, r);
@@ -290,7 +356,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     char* db = smem + b * Cfg::STAGE;
 #pragma unroll
     for (int t = 0; t < NMFMA; ++t) {
-      mfma_one(LAST, t);
+      mfma_one(LAST, t, Cfg::KSTEPS - 1);
 #pragma unroll
       for (int r = 0; r < NREAD; ++r)
         if (read_slot(r, NMFMA) == t) read_one(ob, 0, 0, r);
@@ -308,14 +374,18 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   Src cur = tile_src(tile);
   Src nxt = tile_src(tile + step);
   {
-    // Prologue: stream positions 0 and 1 (nst >= 2, so both are this tile's),
-    // and the part-B copies of position 1 are included.
+    // Prologue: stream positions 0 and 1, both of this tile (persistent
+    // launches have nst >= 2; with one workgroup per tile and nst < 2 the
+    // second position reads zeros that nothing uses), without the part-B
+    // copies of position 1, which stage 0 issues.
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const Rsrc rq = rsrc_at(cur.q, cur.qn, t, false), rp = rsrc_at(cur.p, cur.pn, t, PKM);
       const uint32_t kill = kill_at(t);
 #pragma unroll
       for (int d = 0; d < (t == 0 ? NDMA : NA); ++d) copy_d(rq, rp, kill, smem + t * Cfg::STAGE, d);
+      // MX: stage 0's scales, ahead of the copies the wait below leaves open.
+      if (t == 0) load_scales(cur, 0);
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcntBase | vmcnt_bits(NA));
     __syncthreads();

@@ -26,7 +26,9 @@
  * Memory and ownership.  A, B and C are DEVICE pointers owned by the caller;
  * the library never allocates, frees or retains them and keeps no mutable
  * global state (beyond a thread-local error code), so calls are reentrant.
- * A and B must not overlap C.
+ * A and B must not overlap C, and must be readable over whole rows of
+ * their pitch: A over M*lda elements, B over K*ldb (NN) or N*ldb (TN); the
+ * kernels copy 16-byte pieces and may read the padding of the last row.
  * Alignment: A and B must be 16-byte aligned and lda*elem, ldb*elem must be
  * multiples of 16 bytes (elem = bytes per input element); C needs only its
  * element alignment (wider stores are used when C and ldc allow them).
@@ -109,6 +111,32 @@ int gemm_fp8_scaled(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t l
                     const float* scale_a, int64_t n_scale_a, const float* scale_b, int64_t n_scale_b,
                     int layout, void* stream);
 
+/*
+ * MXFP8: OCP E4M3 x E4M3 -> FP32 with one E8M0 scale per 32 consecutive k of
+ * each row of A and of each column of B (the block scales of the OCP
+ * Microscaling (MX) format, fed to the scale operands of the gfx950 MFMA;
+ * the scaled successor that "FP8 GEMM Optimization on AMD RDNA 4", section
+ * "What Changes at FP8", leaves for later work):
+ *   C_ij = sum over blocks b of 2^(sa_ib - 127) * 2^(sb_jb - 127)
+ *          * sum_{k = 32b}^{32b + 31} A_ik * B_kj
+ * accumulated in FP32.  K must be a multiple of 32 (else
+ * DGEMM_ERR_INVALID_DIM, checked with the dimensions).
+ * scale_a: DEVICE pointer to M*ldsa bytes; sa_ib is scale_a[i*ldsa + b],
+ *          ldsa >= K/32 (the kernels read whole 4-byte groups of a row).
+ * scale_b: DEVICE pointer to N*ldsb bytes; sb_jb is scale_b[j*ldsb + b],
+ *          ldsb >= K/32 (one row of scales per column j of B, in either
+ *          layout).  With K == 0 neither is read (and may be NULL).
+ * Both must be 4-byte aligned with ldsa, ldsb multiples of 4
+ * (else DGEMM_ERR_MISALIGNED); an ld below K/32 -> DGEMM_ERR_INVALID_LD;
+ * 256*ldsa or 256*ldsb at or above 2^31 -> DGEMM_ERR_UNSUPPORTED.  The scale
+ * byte 255 (NaN in the format) is not supported: its result is unspecified.
+ * Other arguments, layouts and checks as gemm_fp8.
+ */
+int gemm_mxfp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+               const uint8_t* B, int64_t ldb, float* C, int64_t ldc,
+               const uint8_t* scale_a, int64_t ldsa, const uint8_t* scale_b, int64_t ldsb,
+               int layout, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* gemm_strerror(int status);
 
@@ -138,8 +166,8 @@ const char* dgemm_hip_error_string(int code);
  * dgemm_kernel_config: writes a one-line description (kernel name, tile, wave
  * grid, LDS bytes, grid size) of the kernel a call with these arguments would
  * launch into buf (at most len bytes, NUL-terminated).  dtype: 0 f32, 1 f16,
- * 2 bf16, 3 fp8, 4 fp8 with scale factors.  Returns 0, or a dgemm_status for
- * invalid arguments.
+ * 2 bf16, 3 fp8, 4 fp8 with scale factors, 5 MXFP8.  Returns 0, or a
+ * dgemm_status for invalid arguments.
  */
 int dgemm_tile_map(int64_t tiles_p, int64_t tiles_q, int64_t group, int64_t pid,
                    int64_t* tile_p, int64_t* tile_q);

@@ -7,8 +7,9 @@ its Python binding) never imports it, and the two share no code.
 The arithmetic lives in ``oracle.cpp`` (built with g++, OpenMP over rows, FP64
 accumulation, one round-to-nearest-even rounding to the output format).  This
 module only builds and loads that library, marshals numpy arrays, applies
-the FP8 scale factors to the exact sums (``gemm_fp8_scaled``), and holds the
-acceptance check.
+the FP8 scale factors to the exact sums (``gemm_fp8_scaled``), computes the
+block-scaled MXFP8 product from per-block library matrix products in FP64
+(``gemm_mxfp8``), and holds the acceptance check.
 
 Definition followed: "Optimizing GEMM in HIP", section "GEMM fundamentals"
 (C_ij = inner product of row i of A and column j of B); storage layouts from
@@ -150,6 +151,65 @@ def gemm_fp8_scaled(layout, M, N, K, A, lda, B, ldb, scale_a, scale_b, rows=None
     with np.errstate(invalid="ignore", over="ignore"):
         c = encode(F32, s * f)
         return c.astype(np.uint32), sab * np.abs(f)
+
+
+def e8m0(bits) -> np.ndarray:
+    """Values of E8M0 scale bytes: 2^(e - 127), and NaN for e = 255 (OCP
+    Microscaling (MX) format, the shared-scale element type)."""
+    e = np.asarray(bits, dtype=np.int64)
+    v = np.ldexp(1.0, e - 127)
+    return np.where(e == 255, np.nan, v)
+
+
+def operands_fp64(in_fmt, layout, M, N, K, A, lda, B, ldb):
+    """a[i][k] and b[k][j] decoded exactly, whatever the storage layout."""
+    A = np.asarray(A).reshape(-1)
+    B = np.asarray(B).reshape(-1)
+    i, j, k = np.arange(M)[:, None], np.arange(N)[None, :], np.arange(K)
+    a = decode(in_fmt, A[i * lda + k[None, :]])                   # A(i,k) = A[i*lda + k]
+    if layout == NN:
+        b = decode(in_fmt, B[k[:, None] * ldb + j])               # B(k,j) = B[k*ldb + j]
+    else:
+        b = decode(in_fmt, B[j * ldb + k[:, None]])               # B(k,j) = B[j*ldb + k]
+    return a.reshape(M, K), b.reshape(K, N)
+
+
+def gemm_mxfp8(layout, M, N, K, A, lda, B, ldb, SA, ldsa, SB, ldsb, rows=None):
+    """MXFP8 GEMM: E4M3 operands with one E8M0 scale per 32 consecutive k of
+    each row of A (SA[i*ldsa + b]) and each column of B (SB[j*ldsb + b]).
+
+    The block-scaled dot product of the OCP Microscaling (MX) format, the
+    scaled variant that "FP8 GEMM Optimization on AMD RDNA 4" (section "What
+    Changes at FP8") leaves for later work:
+        C_ij = sum_b 2^(SA_ib - 127) 2^(SB_jb - 127) sum_{k in block b} a_ik b_kj.
+    Each block's sum is a library matrix product in FP64 and exact (E4M3
+    products are multiples of 2^-18 below 2^18 in magnitude, so 32 of them
+    need under 42 bits), and so is its product with the two powers of two;
+    the sum over blocks is rounded in FP64 (relative error below
+    (K/32) * 2^-53) and then once to FP32 with round-to-nearest-even.
+
+    Returns (c_bits, sab): FP32 output bits [len(rows) or M][N] and the
+    normaliser sum_b 2^.. 2^.. sum_k |a_ik b_kj| of the acceptance check.
+    """
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    nb = K // 32
+    a, b = operands_fp64(E4M3, layout, M, N, K, A, lda, B, ldb)
+    SA = np.asarray(SA).reshape(-1)
+    SB = np.asarray(SB).reshape(-1)
+    ia = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    a = a[ia]
+    sa = e8m0(np.array([[SA[i * ldsa + blk] for blk in range(nb)] for i in ia], dtype=np.int64).reshape(len(ia), nb))
+    sb = e8m0(np.array([[SB[j * ldsb + blk] for blk in range(nb)] for j in range(N)], dtype=np.int64).reshape(N, nb))
+    c = np.zeros((len(ia), N))
+    sab = np.zeros((len(ia), N))
+    with np.errstate(invalid="ignore", over="ignore"):
+        for blk in range(nb):
+            ks = slice(32 * blk, 32 * blk + 32)
+            f = sa[:, blk][:, None] * sb[:, blk][None, :]
+            c += (a[:, ks] @ b[ks, :]) * f
+            sab += (np.abs(a[:, ks]) @ np.abs(b[ks, :])) * f
+        return encode(F32, c).astype(np.uint32), sab
 
 
 def decode(fmt, bits) -> np.ndarray:

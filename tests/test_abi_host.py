@@ -30,7 +30,8 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     syms = declared_symbols()
-    assert {"gemm_f32", "gemm_f16", "gemm_bf16", "gemm_fp8", "gemm_fp8_scaled", "gemm_strerror"} <= set(syms)
+    assert {"gemm_f32", "gemm_f16", "gemm_bf16", "gemm_fp8", "gemm_fp8_scaled", "gemm_mxfp8",
+            "gemm_strerror"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -101,6 +102,29 @@ def test_scaled_argument_validation(lib):
     # the operand checks of gemm_fp8 still apply
     assert scaled(lib, 4, 5, 16, FAKE, 8, FAKE, 16, FAKE, 4, FAKE, 1, FAKE, 1, 1) == 3
     assert scaled(lib, 4, 5, 16, FAKE + 4, 16, FAKE, 16, FAKE, 4, FAKE, 1, FAKE, 1, 1) == 5
+
+
+def mx(lib, M, N, K, A, lda, B, ldb, C, ldc, sa, ldsa, sb, ldsb, layout):
+    return lib.gemm_mxfp8(M, N, K, A, lda, B, ldb, C, ldc, sa, ldsa, sb, ldsb, layout, None)
+
+
+def test_mxfp8_argument_validation(lib):
+    # K must be a whole number of 32-element blocks (checked with the dimensions)
+    assert mx(lib, 4, 5, 48, FAKE, 48, FAKE, 48, FAKE, 4, FAKE, 4, FAKE, 4, 1) == 1
+    assert mx(lib, 0, 5, 48, None, 48, None, 48, None, 4, None, 4, None, 4, 1) == 1
+    assert mx(lib, 0, 5, 64, None, 64, None, 64, None, 4, None, 4, None, 4, 1) == 0
+    assert mx(lib, 4, 5, 64, FAKE, 64, FAKE, 64, FAKE, 4, FAKE, 4, FAKE, 4, 7) == 4
+    # null scale pointers
+    assert mx(lib, 4, 5, 64, FAKE, 64, FAKE, 64, FAKE, 4, None, 4, FAKE, 4, 1) == 2
+    assert mx(lib, 4, 5, 64, FAKE, 64, FAKE, 64, FAKE, 4, FAKE, 4, None, 4, 1) == 2
+    # scale rows shorter than K/32
+    assert mx(lib, 4, 5, 256, FAKE, 256, FAKE, 256, FAKE, 4, FAKE, 4, FAKE, 8, 1) == 3
+    assert mx(lib, 4, 5, 256, FAKE, 256, FAKE, 256, FAKE, 4, FAKE, 8, FAKE, 4, 1) == 3
+    # 4-byte alignment of the scale arrays and their rows
+    assert mx(lib, 4, 5, 64, FAKE, 64, FAKE, 64, FAKE, 4, FAKE + 1, 4, FAKE, 4, 1) == 5
+    assert mx(lib, 4, 5, 64, FAKE, 64, FAKE, 64, FAKE, 4, FAKE, 4, FAKE, 6, 1) == 5
+    # a 256-row block of scales spanning 2^31 bytes
+    assert mx(lib, 4, 5, 64, FAKE, 64, FAKE, 64, FAKE, 4, FAKE, 1 << 23, FAKE, 4, 1) == 6
 
 
 def test_size_limits_unsupported(lib):

@@ -69,7 +69,7 @@ def kernel_name(dtype, layout, M, N, K):
     import ctypes
     from dense_gemm_02_amd import binding
     buf = ctypes.create_string_buffer(256)
-    code = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3, "fp8s": 4}[dtype]
+    code = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3, "fp8s": 4, "mx8": 5}[dtype]
     assert binding.load_library().dgemm_kernel_config(code, 1 if layout == "tn" else 0, M, N, K, buf, 256) == 0
     return buf.value.decode()
 
@@ -324,3 +324,79 @@ def test_library_loaded_before_torch_use():
     say("case fresh process: library loaded before torch use")
     r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=180)
     assert r.returncode == 0 and "ok" in r.stdout, r.stdout + r.stderr
+
+
+# ---- MXFP8 with E8M0 block scales (gemm_mxfp8) -------------------------------
+
+def mx_scales(rng, rows, nb, ld, lo=112, hi=143):
+    """rows x ld scale bytes: nb random E8M0 codes per row, the padding 255
+    (the format's NaN), which no call may read."""
+    s = np.full((max(rows, 1), ld), 255, np.uint8)
+    s[:, :nb] = rng.integers(lo, hi, (max(rows, 1), nb))
+    return s
+
+
+def run_mx(p, SA, ldsa, SB, ldsb):
+    import torch
+    from dense_gemm_02_amd import binding
+    C = alloc_c(p)
+    binding.gemm_mx(p.layout, p.M, p.N, p.K, to_dev(p.A), p.lda, to_dev(p.B), p.ldb, C, p.ldc,
+                    torch.from_numpy(SA.reshape(-1)).cuda(), ldsa, torch.from_numpy(SB.reshape(-1)).cuda(), ldsb)
+    torch.cuda.synchronize()
+    return C
+
+
+def compare_mx(p, cij, SA, ldsa, SB, ldsb, rows=None, exact=False):
+    from gpu_util import oracle
+    c_ref, sab = oracle.gemm_mxfp8(oracle.NN if p.layout == "nn" else oracle.TN, p.M, p.N, p.K, p.A, p.lda, p.B,
+                                   p.ldb, SA.reshape(-1), ldsa, SB.reshape(-1), ldsb, rows=rows)
+    got = cij if rows is None else cij[np.asarray(rows)]
+    if exact:
+        return oracle.bits_equal(got, c_ref, oracle.F32), 0.0
+    ok, err, _ = oracle.check(got, c_ref, sab, oracle.F32, oracle.TOL["fp8"])
+    return ok, err
+
+
+# Every tile the MXFP8 path picks: one or two stages (K < 256, one tile per
+# workgroup), a partial last stage whose scale dword reaches past K/32, the
+# persistent 256 x 256 kernel with 400 tiles, K = 0, padded scale rows full
+# of NaN codes.  Scales 2^-15 .. 2^15.
+@pytest.mark.parametrize("layout", ["tn", "nn"])
+def test_mxfp8_against_oracle(layout):
+    rng = np.random.default_rng(7000 + (layout == "nn"))
+    shapes = [(1, 1, 32), (33, 65, 96), (257, 129, 224), (300, 521, 384), (512, 512, 256), (1000, 1100, 1184),
+              (5120, 5120, 384), (70, 90, 0)]
+    for idx, (M, N, K) in enumerate(shapes):
+        p = make_problem("fp8", layout, M, N, K, seed=7100 + idx, pad=idx % 2)
+        nb = K // 32
+        ld = ((nb + 3) // 4) * 4 + 4 * (idx % 2)
+        SA, SB = mx_scales(rng, M, nb, ld), mx_scales(rng, N, nb, ld)
+        say(f"case mx {kernel_name('mx8', layout, M, N, K)} M={M} N={N} K={K} ld={ld}")
+        cij, pad = c_host(p, run_mx(p, SA, ld, SB, ld))
+        assert pad_untouched(pad, "fp8")
+        rows = sample_rows(M, seed=idx) if M * N * max(K, 1) > 5e8 else None
+        ok, err = compare_mx(p, cij, SA, ld, SB, ld, rows=rows)
+        assert ok, f"{layout} {(M, N, K)}: max err {err:.3e}"
+
+
+# +-1 operands with scales 2^-3 .. 2^3: every partial sum is exact in FP32,
+# so the output matches the oracle bit for bit; unit scales reproduce
+# gemm_fp8 where both take the same four-wave tile.
+@pytest.mark.parametrize("layout", ["tn", "nn"])
+def test_mxfp8_bit_exact(layout):
+    rng = np.random.default_rng(7200 + (layout == "nn"))
+    for idx, (M, N, K) in enumerate([(260, 300, 2048), (4096, 4096, 512), (77, 50, 160)]):
+        p = make_problem("fp8", layout, M, N, K, seed=7300 + idx, dist="pm1")
+        nb = K // 32
+        ld = ((nb + 3) // 4) * 4
+        SA, SB = mx_scales(rng, M, nb, ld, 124, 131), mx_scales(rng, N, nb, ld, 124, 131)
+        say(f"case mx pm1 {layout} M={M} N={N} K={K}")
+        cij, _ = c_host(p, run_mx(p, SA, ld, SB, ld))
+        rows = sample_rows(M, seed=idx) if M > 1000 else None
+        ok, _ = compare_mx(p, cij, SA, ld, SB, ld, rows=rows, exact=True)
+        assert ok, f"{(M, N, K)}: not bit-exact"
+        if K >= 256:
+            one = np.full((max(M, N), ld), 127, np.uint8)
+            c1, _ = c_host(p, run_mx(p, one[:M], ld, one[:N], ld))
+            c0, _ = c_host(p, run_gpu(p))
+            assert np.array_equal(c1, c0)

@@ -20,6 +20,9 @@ what mathematics and library routines fix:
 * thread-count independence and equality with the unblocked triple loop;
 * FP8 with scale factors: exact rationals s_ij * sa_i * sb_j rounded once,
   a rank-one closed form, and reduction to the plain product at unit factors;
+* MXFP8 block scales: E8M0 decoding, exact rationals with per-block powers of
+  two, a closed form that fixes the block width and which operand each
+  scale belongs to, and reduction to the plain product at unit scales;
 * sensitivity: a transposed operand, a dropped term or a wrong sign each make
   a pin fail (and for the factors: reversed rows, a lost sign, a missing
   factor).
@@ -497,6 +500,104 @@ def test_scaled_pins_catch_planted_mistakes(oracle_lib):
     assert not _check_scaled_exact(p, sa, sb, *_scaled(p, np.abs(sa), sb))
     # only one of the two factors applied
     assert not _check_scaled_exact(p, sa, sb, *_scaled(p, sa, np.float32([1.0])))
+
+
+# ---- MXFP8: E8M0 block scales ---------------------------------------------
+
+def _mx(p, SA, ldsa, SB, ldsb, rows=None):
+    return oracle.gemm_mxfp8(LAY[p.layout], p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, SA, ldsa, SB, ldsb, rows=rows)
+
+
+def _check_mx_exact(p, SA, ldsa, SB, ldsb, c):
+    """Bit-exact against the exact-rational block-scaled sum rounded once to FP32."""
+    a = lib_decode("fp8", p.A).reshape(-1)
+    b = lib_decode("fp8", p.B).reshape(-1)
+    for i in range(p.M):
+        for j in range(p.N):
+            acc = Fraction(0)
+            for k in range(p.K):
+                blk = k // 32
+                av = Fraction(float(a[i * p.lda + k]))
+                bv = Fraction(float(b[k * p.ldb + j] if p.layout == "nn" else b[j * p.ldb + k]))
+                acc += av * bv * Fraction(2) ** (int(SA[i * ldsa + blk]) - 127) * \
+                    Fraction(2) ** (int(SB[j * ldsb + blk]) - 127)
+            want = frac_rne(acc, *FMT_PARAMS["f32"])
+            if float(oracle.decode(oracle.F32, c[i:i + 1, j])[0]) != want:
+                return False
+    return True
+
+
+def test_e8m0_values(oracle_lib):
+    e = np.arange(256)
+    v = oracle.e8m0(e)
+    assert v[127] == 1.0 and v[128] == 2.0 and v[0] == 2.0 ** -127 and v[254] == 2.0 ** 127
+    assert np.isnan(v[255]) and np.all(v[:255] == [2.0 ** (x - 127) for x in range(255)])
+
+
+def test_mx_unit_scales_reduce_to_plain(oracle_lib):
+    for layout in ("nn", "tn"):
+        p = inputs.make("fp8", layout, 6, 5, 160, 61, "uniform4")
+        c0, _, sab0 = run(p)
+        c, sab = _mx(p, np.full(6 * 5, 127, np.uint8), 5, np.full(5 * 5, 127, np.uint8), 5)
+        assert np.array_equal(c, c0) and np.array_equal(sab, sab0)
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+def test_mx_bruteforce_exact_rationals(oracle_lib, layout):
+    rng = np.random.default_rng(90 + (layout == "nn"))
+    for M, N, K in [(1, 1, 32), (3, 4, 64), (4, 3, 96)]:
+        p = inputs.make("fp8", layout, M, N, K, 70 + K, "uniform4")
+        nb = K // 32
+        ldsa, ldsb = nb + 1, nb + 3          # padded rows; the padding holds NaN codes
+        SA = np.full(M * ldsa, 255, np.uint8)
+        SB = np.full(N * ldsb, 255, np.uint8)
+        for i in range(M):
+            SA[i * ldsa:i * ldsa + nb] = rng.integers(112, 143, nb)
+        for j in range(N):
+            SB[j * ldsb:j * ldsb + nb] = rng.integers(112, 143, nb)
+        c, sab = _mx(p, SA, ldsa, SB, ldsb)
+        assert _check_mx_exact(p, SA, ldsa, SB, ldsb, c)
+        assert np.all(np.isfinite(sab))
+        rows = np.array([M - 1, 0], dtype=np.int64)
+        cr, _ = _mx(p, SA, ldsa, SB, ldsb, rows=rows)
+        assert np.array_equal(cr, c[rows])
+
+
+def test_mx_closed_form(oracle_lib):
+    # A = B = 1, SA[i][b] = 127 + b, SB[j][b] = 127 + j:
+    # C_ij = 32 * 2^j * (2^nb - 1).  Blocks of any other width than 32, or
+    # the two operands' scales exchanged, give other values.
+    for layout in ("nn", "tn"):
+        M, N, K = 3, 4, 160
+        nb = K // 32
+        p = inputs.make("fp8", layout, M, N, K, 0, "ones")
+        SA = np.array([127 + blk for _ in range(M) for blk in range(nb)], np.uint8)
+        SB = np.array([127 + j for j in range(N) for _ in range(nb)], np.uint8)
+        c, sab = _mx(p, SA, nb, SB, nb)
+        want = np.array([[32.0 * 2.0 ** j * (2.0 ** nb - 1) for j in range(N)] for _ in range(M)])
+        assert np.array_equal(oracle.decode(oracle.F32, c), want) and np.array_equal(sab, want)
+    # a NaN scale (code 255) makes its outputs NaN
+    SA2 = SA.copy()
+    SA2[0] = 255
+    c, _ = _mx(p, SA2, nb, SB, nb)
+    assert np.all(np.isnan(oracle.decode(oracle.F32, c[0]))) and not np.any(np.isnan(oracle.decode(oracle.F32, c[1:])))
+
+
+def test_mx_pins_catch_planted_mistakes(oracle_lib):
+    rng = np.random.default_rng(95)
+    p = inputs.make("fp8", "tn", 3, 4, 96, 96, "uniform4")
+    SA = rng.integers(118, 137, 3 * 3).astype(np.uint8)
+    SB = rng.integers(118, 137, 4 * 3).astype(np.uint8)
+    assert _check_mx_exact(p, SA, 3, SB, 3, _mx(p, SA, 3, SB, 3)[0])
+    # scale blocks of A's rows in reverse order
+    rev = SA.reshape(3, 3)[:, ::-1].reshape(-1).copy()
+    assert not _check_mx_exact(p, SA, 3, SB, 3, _mx(p, rev, 3, SB, 3)[0])
+    # A's and B's scales exchanged (first three rows)
+    assert not _check_mx_exact(p, SA, 3, SB, 3, _mx(p, SB[:9].copy(), 3, np.concatenate([SA, SA[:3]]), 3)[0])
+    # one scale off by one
+    off = SB.copy()
+    off[5] += 1
+    assert not _check_mx_exact(p, SA, 3, SB, 3, _mx(p, SA, 3, off, 3)[0])
 
 
 # ---- sensitivity: planted mistakes must trip a pin ---------------------------
