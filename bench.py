@@ -43,6 +43,9 @@ WORKLOADS = {
 # Other workload configurations, timed with --workload (not part of the
 # default line).  The skinny BF16 case is HBM-bound: B is rotated over
 # ROTATE copies (> 256 MB Infinity Cache + L2) so each launch reads it from HBM.
+# An eighth field selects a variant of the FP8 call: "scaled" (per-row FP32
+# factors for A and B, gemm_fp8_scaled) or "mx" (E8M0 block scales,
+# gemm_mxfp8).
 EXTRA = {
     "bf16_tn_16x8192x8192": ("bf16", "tn", 16, 8192, 8192, 4, "normal"),
     "bf16_tn_4096x14336x4096": ("bf16", "tn", 4096, 14336, 4096, 4, "normal"),
@@ -53,6 +56,13 @@ EXTRA = {
     "fp8_tn_8192x28672x8192": ("fp8", "tn", 8192, 28672, 8192, 5, "uniform4"),
     "f32_nn_4096x4096x4096": ("f32", "nn", 4096, 4096, 4096, 1, "uniform"),
     "f32_nn_256x256x256": ("f32", "nn", 256, 256, 256, 0, "uniform"),
+    "bf16_nn_8192x8192x8192": ("bf16", "nn", 8192, 8192, 8192, 4, "normal"),
+    "fp8_nn_8192x8192x8192": ("fp8", "nn", 8192, 8192, 8192, 5, "uniform4"),
+    "fp8_tn_8192x8192x8192_scaled": ("fp8", "tn", 8192, 8192, 8192, 5, "uniform4", "scaled"),
+    "fp8_tn_8192x8192x8192_mx": ("fp8", "tn", 8192, 8192, 8192, 5, "uniform4", "mx"),
+    "bf16_tn_2048x2048x2048": ("bf16", "tn", 2048, 2048, 2048, 4, "normal"),
+    "bf16_tn_3072x4096x8192": ("bf16", "tn", 3072, 4096, 8192, 4, "normal"),
+    "bf16_tn_8192x10240x8192": ("bf16", "tn", 8192, 10240, 8192, 4, "normal"),
 }
 ROTATE = 4
 DTYPE_NAME = {"f16": "f16", "bf16": "bf16", "fp8": "fp8 (e4m3) x fp8 -> f32", "f32": "f32"}
@@ -85,7 +95,7 @@ def load_traffic(workload: str):
 def make_inputs(dtype, spec=None):
     import torch
     from dense_gemm_02_amd import inputs
-    dt, layout, M, N, K, seed, dist = spec or WORKLOADS[dtype]
+    dt, layout, M, N, K, seed, dist = (spec or WORKLOADS[dtype])[:7]
     p = inputs.make(dt, layout, M, N, K, seed, dist)
 
     def dev(x):
@@ -107,11 +117,27 @@ def time_gemm(dtype, steps, warmup, spec=None, rotate=1):
     Bs = [B] + [B.clone() for _ in range(rotate - 1)]
     stream = torch.cuda.current_stream()
     it = [0]
+    variant = spec[7] if spec is not None and len(spec) > 7 else None
+    rng = np.random.default_rng(11)
+    if variant == "scaled":
+        # per-row factors in [0.5, 2)
+        sa = torch.from_numpy(rng.uniform(0.5, 2.0, p.M).astype(np.float32)).cuda()
+        sb = torch.from_numpy(rng.uniform(0.5, 2.0, p.N).astype(np.float32)).cuda()
+    elif variant == "mx":
+        # E8M0 codes 2^-7 .. 2^7, K/32 per row
+        ld = ((p.K // 32 + 3) // 4) * 4
+        sa = torch.from_numpy(rng.integers(120, 135, (p.M, ld)).astype(np.uint8)).cuda()
+        sb = torch.from_numpy(rng.integers(120, 135, (p.N, ld)).astype(np.uint8)).cuda()
 
     def step():
         b = Bs[it[0] % len(Bs)]
         it[0] += 1
-        binding.gemm(p.dtype, p.layout, p.M, p.N, p.K, A, p.lda, b, p.ldb, C, p.ldc, stream=stream)
+        if variant == "scaled":
+            binding.gemm_scaled(p.layout, p.M, p.N, p.K, A, p.lda, b, p.ldb, C, p.ldc, sa, sb, stream=stream)
+        elif variant == "mx":
+            binding.gemm_mx(p.layout, p.M, p.N, p.K, A, p.lda, b, p.ldb, C, p.ldc, sa, ld, sb, ld, stream=stream)
+        else:
+            binding.gemm(p.dtype, p.layout, p.M, p.N, p.K, A, p.lda, b, p.ldb, C, p.ldc, stream=stream)
 
     for _ in range(warmup):
         step()

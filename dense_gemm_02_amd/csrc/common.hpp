@@ -67,6 +67,16 @@ __device__ __forceinline__ void copy16_lds(i32x4 desc, uint32_t voff, const void
                : "memory", "m0");
 }
 
+// The same with 4 bytes per lane (buffer_load_dword ... lds): lane l lands
+// at M0 + 4*l.
+__device__ __forceinline__ void copy4_lds(i32x4 desc, uint32_t voff, const void* lds_dst) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_dst;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(desc), "s"(m0)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
 }

@@ -34,7 +34,13 @@ struct TnCfg {
   static constexpr int BK = ROWB / E;             // k per stage
   static constexpr int CPE = 16 / E;              // elements per 16-byte chunk
   static constexpr int P_LDS = BP * ROWB;
-  static constexpr int STAGE = (BP + BQ) * ROWB;  // 64 KiB
+  // MX: after the tiles, each stage holds the stage's four scale bytes of
+  // every P row, then of every Q row (one dword per row).
+  static constexpr int SC_LDS = (BP + BQ) * ROWB;
+  static constexpr int SC_ROWS = Op::MX ? BP + BQ : 0;
+  static constexpr int SC_INST = SC_ROWS / 64;                  // 64-row copies per stage
+  static constexpr int SC_MIN = SC_INST / 4;                    // the fewest any wave issues
+  static constexpr int STAGE = (BP + BQ) * ROWB + 4 * SC_ROWS;  // 64 KiB (+2 KiB with MX)
   static constexpr int QSEG = BQ / 8 / NW, PSEG = BP / 8 / NW;
   static constexpr int NDMA = QSEG + PSEG;        // copy instructions per wave per stage
   static constexpr int WTP = BP / WP, WTQ = BQ / WQ;
@@ -265,32 +271,50 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   // MX block scales: for the stage in use, lane l holds in scp[i] / scq[j]
   // the scales of its row of P tile i / Q tile j for k blocks h and h + 2
   // of the stage in bytes 0 and 2 (a stage is four blocks of 32 k: byte 2kk
-  // serves k-step kk).  The next stage's dwords are loaded into nsp / nsq
-  // one stage ahead, with the copies.
+  // serves k-step kk).  A stream position's scale dwords travel with its
+  // copies into its LDS stage (4-byte copies, 64 rows each, spread over the
+  // waves), are read into nsp / nsq in the second half of the stage before
+  // (with its first fragments), and taken at the start of their stage.
   [[maybe_unused]] uint32_t scp[TP], scq[TQ], nsp[TP], nsq[TQ];
-  auto load_scales = [&](const Src& src, int t) {
+  auto copy_scales = [&](const Src& src, int t, char* stage_lds) {
     if constexpr (Op::MX) {
-      const __amdgpu_buffer_rsrc_t rp = make_rsrc(src.sp, src.spn), rq = make_rsrc(src.sq, src.sqn);
+#pragma unroll
+      for (int u0 = 0; u0 < Cfg::SC_INST; u0 += NW) {
+        const int u = u0 + wave_u;
+        if (u0 + NW > Cfg::SC_INST && u >= Cfg::SC_INST) break;
+        const bool isp = 64 * u < Cfg::BP;
+        const int row = isp ? 64 * u + lane : 64 * u - Cfg::BP + lane;
+        const uint32_t voff = (uint32_t)(row * (isp ? a.ldsp : a.ldsq) + 4 * t);
+        char* dst = stage_lds + Cfg::SC_LDS + 256 * u;
+        if constexpr (PKM) {
+          copy4_lds(isp ? make_desc(src.sp, src.spn) : make_desc(src.sq, src.sqn), voff, dst);
+        } else {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(isp ? make_rsrc(src.sp, src.spn) : make_rsrc(src.sq, src.sqn),
+                                                   (__attribute__((address_space(3))) void*)dst, 4, voff, 0, 0, 0);
+        }
+      }
+    }
+  };
+  auto read_scales = [&](const char* stage_lds) {
+    if constexpr (Op::MX) {
 #pragma unroll
       for (int i = 0; i < TP; ++i)
-        nsp[i] = __builtin_amdgcn_raw_buffer_load_b32(
-            rp, (int)((wp * Cfg::WTP + 32 * i + l32) * a.ldsp + 4 * t), 0, 0);
+        nsp[i] = *(const uint32_t*)(stage_lds + Cfg::SC_LDS + 4 * (wp * Cfg::WTP + 32 * i + l32));
 #pragma unroll
       for (int j = 0; j < TQ; ++j)
-        nsq[j] = __builtin_amdgcn_raw_buffer_load_b32(
-            rq, (int)((wq * Cfg::WTQ + 32 * j + l32) * a.ldsq + 4 * t), 0, 0);
+        nsq[j] = *(const uint32_t*)(stage_lds + Cfg::SC_LDS + 4 * (Cfg::BP + wq * Cfg::WTQ + 32 * j + l32));
     }
   };
   // Blocks at or past K/32 read as scale byte 0 (their data are zeros; a
   // stray 255 would be NaN).
-  auto take_scales = [&](int t) {
+  auto take_scales = [&](int t, const uint32_t(&sp)[TP], const uint32_t(&sq)[TQ]) {
     if constexpr (Op::MX) {
       const int64_t valid = K / 32 - 4 * (int64_t)t;
       const uint32_t m = valid >= 4 ? ~0u : (valid <= 0 ? 0u : ((1u << (8 * valid)) - 1u));
 #pragma unroll
-      for (int i = 0; i < TP; ++i) scp[i] = (nsp[i] & m) >> (8 * h);
+      for (int i = 0; i < TP; ++i) scp[i] = (sp[i] & m) >> (8 * h);
 #pragma unroll
-      for (int j = 0; j < TQ; ++j) scq[j] = (nsq[j] & m) >> (8 * h);
+      for (int j = 0; j < TQ; ++j) scq[j] = (sq[j] & m) >> (8 * h);
     }
   };
   static_assert(!Op::MX || Cfg::KSTEPS == 2, "two k-steps of 64 per stage");
@@ -322,10 +346,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     const Rsrc rq1 = rsrc_at(n1 ? nx.q : cu.q, n1 ? nx.qn : cu.qn, t1, false);
     const Rsrc rp1 = rsrc_at(n1 ? nx.p : cu.p, n1 ? nx.pn : cu.pn, t1, PKM);
     const uint32_t kill1 = kill_at(t1);
-    if constexpr (Op::MX) {
-      take_scales(s);
-      load_scales(n1 ? nx : cu, t1);
-    }
+    if constexpr (Op::MX) take_scales(s, nsp, nsq);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk + 1 < Cfg::KSTEPS; ++kk) {
@@ -346,6 +367,8 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
+    // MX: the next stage's scales, first of the reads from its buffer.
+    if constexpr (Op::MX) read_scales(ob);
     __builtin_amdgcn_sched_barrier(0);
     // stream position g + 2
     const bool n2 = s + 2 >= nst;
@@ -354,6 +377,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     const Rsrc rp2 = rsrc_at(n2 ? nx.p : cu.p, n2 ? nx.pn : cu.pn, t2, PKM);
     const uint32_t kill2 = kill_at(t2);
     char* db = smem + b * Cfg::STAGE;
+    if constexpr (Op::MX) copy_scales(n2 ? nx : cu, t2, db);
 #pragma unroll
     for (int t = 0; t < NMFMA; ++t) {
       mfma_one(LAST, t, Cfg::KSTEPS - 1);
@@ -384,11 +408,12 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       const uint32_t kill = kill_at(t);
 #pragma unroll
       for (int d = 0; d < (t == 0 ? NDMA : NA); ++d) copy_d(rq, rp, kill, smem + t * Cfg::STAGE, d);
-      // MX: stage 0's scales, ahead of the copies the wait below leaves open.
-      if (t == 0) load_scales(cur, 0);
+      copy_scales(cur, t, smem + t * Cfg::STAGE);
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVmcntBase | vmcnt_bits(NA));
+    // Position 0 has landed once at most the position-1 copies are open.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcntBase | vmcnt_bits(NA + Cfg::SC_MIN));
     __syncthreads();
+    if constexpr (Op::MX) read_scales(smem);
 #pragma unroll
     for (int r = 0; r < NREAD; ++r) read_one(smem, 0, 0, r);
   }
