@@ -425,26 +425,32 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     const int64_t pb = tp * Cfg::BP + wp * Cfg::WTP, qb = tq * Cfg::BQ + wq * Cfg::WTQ;
     [[maybe_unused]] EpiScale<TQ> sc;
     if constexpr (Op::SCALED) sc.init(a, lane, qb);
+    // Column by column: a lane's four stores into one column of C follow
+    // each other, so each 128-byte line is written whole while it is open.
 #pragma unroll
-    for (int i = 0; i < TP; ++i)
+    for (int i = 0; i < TP; ++i) {
+      [[maybe_unused]] f32x4 fp[4];
+      if constexpr (Op::SCALED) {
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const int64_t p = pb + 32 * i + 8 * gg + 4 * h;
-        [[maybe_unused]] f32x4 fp;
-        if constexpr (Op::SCALED) fp = EpiScale<TQ>::p4(a, p);
+        for (int gg = 0; gg < 4; ++gg) fp[gg] = EpiScale<TQ>::p4(a, pb + 32 * i + 8 * gg + 4 * h);
+      }
 #pragma unroll
-        for (int j = 0; j < TQ; ++j) {
-          const int64_t q = qb + 32 * j + l32;
-          if (q >= a.Qn) continue;
+      for (int j = 0; j < TQ; ++j) {
+        const int64_t q = qb + 32 * j + l32;
+        if (q >= a.Qn) continue;
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int64_t p = pb + 32 * i + 8 * gg + 4 * h;
           float v0 = acc[i][j][4 * gg + 0], v1 = acc[i][j][4 * gg + 1], v2 = acc[i][j][4 * gg + 2],
                 v3 = acc[i][j][4 * gg + 3];
-          if constexpr (Op::SCALED) sc.apply(fp, j, v0, v1, v2, v3);
+          if constexpr (Op::SCALED) sc.apply(fp[gg], j, v0, v1, v2, v3);
           store4<Op>(a, q, p, v0, v1, v2, v3);
         }
-        // (Keeps the factor loads of later groups from being hoisted here,
-        // where the next tile's fragments already hold most registers.)
-        if constexpr (Op::SCALED) __builtin_amdgcn_sched_barrier(0);
       }
+      // (Keeps the factor loads of later row tiles from being hoisted here,
+      // where the next tile's fragments already hold most registers.)
+      if constexpr (Op::SCALED) __builtin_amdgcn_sched_barrier(0);
+    }
   };
   int g = 0;
   for (;;) {
