@@ -64,11 +64,11 @@ Launch mfma_launch(const char* name) {
 // Four-wave kernel (gemm_tn.hpp).  256 x 256 FP8, whose FP32 output is twice
 // as large, runs persistently so that each tile's stores drain under the next
 // tile's stages; every other shape runs one tile per workgroup.
-template <class Op, bool PKM, int BP, int BQ>
+template <class Op, bool PKM, int BP, int BQ, int NS = 2>
 Launch tn_launch(const char* name) {
-  using Cfg = TnCfg<Op, PKM, BP, BQ>;
+  using Cfg = TnCfg<Op, PKM, BP, BQ, NS>;
   constexpr bool P = Op::ELEM == 1 && BP == 256 && BQ == 256;
-  return Launch{(const void*)&gemm_tn_kernel<Op, P, PKM, BP, BQ>, name, BP, BQ, Cfg::NT, 2 * Cfg::STAGE, PKM, P};
+  return Launch{(const void*)&gemm_tn_kernel<Op, P, PKM, BP, BQ, NS>, name, BP, BQ, Cfg::NT, NS * Cfg::STAGE, PKM, P};
 }
 
 // Block tiles of the four-wave kernel and their throughput relative to the
@@ -78,6 +78,13 @@ Launch tn_launch(const char* name) {
 // fragment read, but fill the CUs when the problem has few tiles. With these
 // rates 128 x 128 never loses to 256 x 128, so the latter serves only FP8
 // with p-contiguous P, whose transposing-read swizzle needs 256-byte rows.
+// 128 x 128 comes twice: two workgroups per CU with two LDS stages, or one
+// with four stages, whose copies run three stages ahead.  The four-stage
+// tile is only taken when all its tiles fit one round (at most one per CU):
+// there it beats the two-stage one (bf16 2048^3: 678 against 563 TF/s,
+// 1536 x 1536 x 8192: 586 against 453), with more rounds it loses (bf16
+// 4352 x 4352 x 1024: 550 against 649; 8192^3 forced: 926 against 1012).
+// Its rate is the one measured at one round.
 // The choice minimises ceil(tiles / slots) * tile work / rate, i.e. the
 // number of rounds of workgroups times the time of one round ("FP16 GEMM
 // Optimization on AMD RDNA 3 and RDNA 4", Where That Leaves Us: no single
@@ -85,19 +92,23 @@ Launch tn_launch(const char* name) {
 struct TileChoice {
   int bp, bq, per_cu;   // tile, workgroups resident per CU
   double rate;          // CU throughput relative to 256 x 256
+  int max_rounds;       // 0: any number of rounds
 };
-constexpr TileChoice kTiles[3] = {{256, 256, 1, 1.00}, {256, 128, 1, 0.76}, {128, 128, 2, 0.78}};
+constexpr int kNumTiles = 4;
+constexpr TileChoice kTiles[kNumTiles] = {
+    {256, 256, 1, 1.00, 0}, {256, 128, 1, 0.76, 0}, {128, 128, 2, 0.78, 0}, {128, 128, 1, 0.47, 1}};
 constexpr int kPlanCus = 256;  // MI355X CUs, for the tile choice only
 
 int pick_tile(int64_t Pn, int64_t Qn, unsigned allowed) {
   int best = -1;
   double best_t = 0.0;
-  for (int i = 0; i < 3; ++i) {
+  for (int i = 0; i < kNumTiles; ++i) {
     if (!(allowed >> i & 1u)) continue;
     const TileChoice& c = kTiles[i];
     const int64_t tiles = ((Pn + c.bp - 1) / c.bp) * ((Qn + c.bq - 1) / c.bq);
     const int64_t slots = (int64_t)kPlanCus * c.per_cu;
     const double rounds = (double)((tiles + slots - 1) / slots);
+    if (c.max_rounds > 0 && rounds > c.max_rounds) continue;
     const double t = rounds * (double)c.bp * c.bq * c.per_cu / c.rate;
     if (best < 0 || t < best_t) { best = i; best_t = t; }
   }
@@ -105,15 +116,18 @@ int pick_tile(int64_t Pn, int64_t Qn, unsigned allowed) {
 }
 
 template <class Op, bool PKM>
-Launch tn_pick(const char* const names[3], int64_t Pn, int64_t Qn) {
+Launch tn_pick(const char* const names[kNumTiles], int64_t Pn, int64_t Qn) {
   // p-contiguous FP8 P keeps 256-wide rows (the transposing-read swizzle
   // needs eight 32-byte units per row).
   if constexpr (PKM && Op::ELEM == 1) {
-    if (pick_tile(Pn, Qn, 0b011) == 1) return tn_launch<Op, PKM, 256, 128>(names[1]);
+    if (pick_tile(Pn, Qn, 0b0011) == 1) return tn_launch<Op, PKM, 256, 128>(names[1]);
     return tn_launch<Op, PKM, 256, 256>(names[0]);
   } else {
-    if (pick_tile(Pn, Qn, 0b101) == 2) return tn_launch<Op, PKM, 128, 128>(names[2]);
-    return tn_launch<Op, PKM, 256, 256>(names[0]);
+    switch (pick_tile(Pn, Qn, 0b1101)) {
+      case 2: return tn_launch<Op, PKM, 128, 128>(names[2]);
+      case 3: return tn_launch<Op, PKM, 128, 128, 4>(names[3]);
+      default: return tn_launch<Op, PKM, 256, 256>(names[0]);
+    }
   }
 }
 
@@ -151,8 +165,9 @@ Launch select(int dt, int layout, int64_t M, int64_t N, int64_t K) {
     const int64_t Pn = nn ? N : M, Qn = nn ? M : N;
     if (K < 256) return nn ? tn_launch<OpMX8, true, 256, 128>("mx8_nn_256x128_w4")
                            : tn_launch<OpMX8, false, 128, 128>("mx8_tn_128x128_w4");
-    static const char* const mxn[3] = {"mx8_nn_256x256_w4_persistent", "mx8_nn_256x128_w4", nullptr};
-    static const char* const mxt[3] = {"mx8_tn_256x256_w4_persistent", nullptr, "mx8_tn_128x128_w4"};
+    static const char* const mxn[kNumTiles] = {"mx8_nn_256x256_w4_persistent", "mx8_nn_256x128_w4", nullptr, nullptr};
+    static const char* const mxt[kNumTiles] = {"mx8_tn_256x256_w4_persistent", nullptr, "mx8_tn_128x128_w4",
+                                               "mx8_tn_128x128_w4_s4"};
     return nn ? tn_pick<OpMX8, true>(mxn, Pn, Qn) : tn_pick<OpMX8, false>(mxt, Pn, Qn);
   }
   // K a whole number of 16-byte chunks and at least two stages: the
@@ -162,14 +177,22 @@ Launch select(int dt, int layout, int64_t M, int64_t N, int64_t K) {
     const int e = in_elem(dt);
     if (K % (16 / e) == 0 && K >= 2 * (128 / e)) {
       const int64_t Pn = nn ? N : M, Qn = nn ? M : N;
-      static const char* const f16n[3] = {"f16_nn_256x256_w4", nullptr, "f16_nn_128x128_w4"};
-      static const char* const bf16n[3] = {"bf16_nn_256x256_w4", nullptr, "bf16_nn_128x128_w4"};
-      static const char* const fp8n[3] = {"fp8_nn_256x256_w4_persistent", "fp8_nn_256x128_w4", nullptr};
-      static const char* const f16t[3] = {"f16_tn_256x256_w4", nullptr, "f16_tn_128x128_w4"};
-      static const char* const bf16t[3] = {"bf16_tn_256x256_w4", nullptr, "bf16_tn_128x128_w4"};
-      static const char* const fp8t[3] = {"fp8_tn_256x256_w4_persistent", nullptr, "fp8_tn_128x128_w4"};
-      static const char* const fp8sn[3] = {"fp8s_nn_256x256_w4_persistent", "fp8s_nn_256x128_w4", nullptr};
-      static const char* const fp8st[3] = {"fp8s_tn_256x256_w4_persistent", nullptr, "fp8s_tn_128x128_w4"};
+      static const char* const f16n[kNumTiles] = {"f16_nn_256x256_w4", nullptr, "f16_nn_128x128_w4",
+                                                 "f16_nn_128x128_w4_s4"};
+      static const char* const bf16n[kNumTiles] = {"bf16_nn_256x256_w4", nullptr, "bf16_nn_128x128_w4",
+                                                 "bf16_nn_128x128_w4_s4"};
+      static const char* const fp8n[kNumTiles] = {"fp8_nn_256x256_w4_persistent", "fp8_nn_256x128_w4", nullptr,
+                                                  nullptr};
+      static const char* const f16t[kNumTiles] = {"f16_tn_256x256_w4", nullptr, "f16_tn_128x128_w4",
+                                                 "f16_tn_128x128_w4_s4"};
+      static const char* const bf16t[kNumTiles] = {"bf16_tn_256x256_w4", nullptr, "bf16_tn_128x128_w4",
+                                                 "bf16_tn_128x128_w4_s4"};
+      static const char* const fp8t[kNumTiles] = {"fp8_tn_256x256_w4_persistent", nullptr, "fp8_tn_128x128_w4",
+                                                  "fp8_tn_128x128_w4_s4"};
+      static const char* const fp8sn[kNumTiles] = {"fp8s_nn_256x256_w4_persistent", "fp8s_nn_256x128_w4", nullptr,
+                                                   nullptr};
+      static const char* const fp8st[kNumTiles] = {"fp8s_tn_256x256_w4_persistent", nullptr, "fp8s_tn_128x128_w4",
+                                                   "fp8s_tn_128x128_w4_s4"};
       if (nn) {
         switch (dt) {
           case DT_F16: return tn_pick<OpF16, true>(f16n, Pn, Qn);

@@ -17,6 +17,9 @@
 //  * Copies of a stage are split: NA go out right after the barrier two
 //    stages ahead, the other NDMA - NA over the first KB k-steps of the stage
 //    before, so the texture unit sees them spread out.
+//  * NS LDS stages: with NS > 2 (small tiles, one workgroup per CU) every
+//    copy goes out NS stages ahead, so a stage's copy latency hides behind
+//    NS - 1 stages of MFMAs.
 #pragma once
 
 #include <type_traits>
@@ -26,9 +29,11 @@
 
 namespace dg {
 
-template <class Op, bool PKM, int BP_ = 256, int BQ_ = 256>
+template <class Op, bool PKM, int BP_ = 256, int BQ_ = 256, int NS_ = 2>
 struct TnCfg {
   static constexpr int BP = BP_, BQ = BQ_, WP = 2, WQ = 2, NW = 4, NT = 256;
+  static constexpr int NS = NS_;                  // LDS stages (a power of two)
+  static_assert(NS == 2 || NS == 4, "two or four stages");
   static constexpr int E = Op::ELEM, FC = Op::FC;
   static constexpr int ROWB = 128;                // bytes of k per LDS row per stage
   static constexpr int BK = ROWB / E;             // k per stage
@@ -61,28 +66,32 @@ struct TnCfg {
   // Copy split: FP16/BF16 issue half of a stage's copies after the barrier
   // two stages ahead and the rest over the first two k-steps of the stage
   // before; FP8 (two k-steps per stage) issues them all after the barrier.
-  static constexpr int NA = Op::ELEM == 2 ? NDMA / 2 : NDMA;
+  static constexpr int NA = (Op::ELEM == 2 && NS == 2) ? NDMA / 2 : NDMA;
   static constexpr int NB = NDMA - NA;
   static constexpr int KB = KSTEPS > 2 ? 2 : KSTEPS - 1;
   static_assert(NB == 0 || KB >= 1, "part-B copies need k-steps before the barrier");
-  static_assert(2 * STAGE <= kLdsLimit, "LDS budget");
+  static_assert(NS * STAGE <= kLdsLimit, "LDS budget");
+  // Copies in flight when a stage's data must have landed: those of the
+  // NS - 2 later stream positions (each wave issues at least SC_MIN scale
+  // copies per position).
+  static constexpr int VM_MID = (NS - 2) * (NDMA + SC_MIN);
   static_assert(!PKM || PROWB / UB >= KEYM, "swizzle keys stay within a row of P");
   // The LDS-staged epilogue needs 256-byte staged rows; smaller wave tiles
   // store straight from the accumulators.
   static constexpr bool STAGED_EPI = (TP / (Op::OE == 4 ? 2 : 1)) * 32 * Op::OE == 256;
   // Waves per SIMD the kernel is compiled for: a 64x64 wave tile is small
   // enough for two (two workgroups per CU).
-  static constexpr int WPE = TP * TQ <= 4 ? 2 : 1;
+  static constexpr int WPE = TP * TQ <= 4 && NS == 2 ? 2 : 1;
 };
 
-template <class Op, bool PERSIST, bool PKM, int BP, int BQ>
+template <class Op, bool PERSIST, bool PKM, int BP, int BQ, int NS>
 __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
-  using Cfg = TnCfg<Op, PKM, BP, BQ>;
+  using Cfg = TnCfg<Op, PKM, BP, BQ, NS>;
   constexpr int NW = Cfg::NW, E = Cfg::E, FC = Cfg::FC, ROWB = Cfg::ROWB, BK = Cfg::BK, CPE = Cfg::CPE;
   constexpr int TP = Cfg::TP, TQ = Cfg::TQ, QSEG = Cfg::QSEG, NDMA = Cfg::NDMA;
   constexpr int NREAD = Cfg::NREAD, NMFMA = Cfg::NMFMA, NA = Cfg::NA, NB = Cfg::NB, KB = Cfg::KB;
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * Cfg::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[NS * Cfg::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -332,14 +341,15 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   constexpr int LAST = (Cfg::KSTEPS - 1) & 1;
 
   // ---- one stage ----
-  // Global stage g (buffer g % 2) is stage s of the current tile.  Copies
-  // issued here belong to the stream position g + 2 (after the barrier; NA
-  // of them) and g + 1 (before it; NB of them), which may already be stages
-  // of the next tile `nx`.
+  // Global stage g (buffer g % NS) is stage s of the current tile.  Copies
+  // issued here belong to the stream position g + NS (after the barrier; NA
+  // of them) and g + 1 (before it; NB of them, two stages only), which may
+  // already be stages of the next tile `nx` (persistent launches have
+  // nst >= NS).
   auto stage = [&](int g, int s, const Src& cu, const Src& nx) {
-    const int b = g & 1;
+    const int b = g & (NS - 1);
     const char* sb = smem + b * Cfg::STAGE;
-    char* ob = smem + (b ^ 1) * Cfg::STAGE;
+    char* ob = smem + ((g + 1) & (NS - 1)) * Cfg::STAGE;
     // stream position g + 1
     const bool n1 = s + 1 >= nst;
     const int t1 = n1 ? s + 1 - nst : s + 1;
@@ -365,14 +375,16 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    // Stream position g + 1 has landed (later positions may still be in flight).
+    if constexpr (NS == 2) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    else __builtin_amdgcn_s_waitcnt(kWaitVmcntBase | vmcnt_bits(Cfg::VM_MID));
     __syncthreads();
     // MX: the next stage's scales, first of the reads from its buffer.
     if constexpr (Op::MX) read_scales(ob);
     __builtin_amdgcn_sched_barrier(0);
-    // stream position g + 2
-    const bool n2 = s + 2 >= nst;
-    const int t2 = n2 ? s + 2 - nst : s + 2;
+    // stream position g + NS
+    const bool n2 = s + NS >= nst;
+    const int t2 = n2 ? s + NS - nst : s + NS;
     const Rsrc rq2 = rsrc_at(n2 ? nx.q : cu.q, n2 ? nx.qn : cu.qn, t2, false);
     const Rsrc rp2 = rsrc_at(n2 ? nx.p : cu.p, n2 ? nx.pn : cu.pn, t2, PKM);
     const uint32_t kill2 = kill_at(t2);
@@ -403,15 +415,16 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     // second position reads zeros that nothing uses), without the part-B
     // copies of position 1, which stage 0 issues.
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < NS; ++t) {
       const Rsrc rq = rsrc_at(cur.q, cur.qn, t, false), rp = rsrc_at(cur.p, cur.pn, t, PKM);
       const uint32_t kill = kill_at(t);
 #pragma unroll
-      for (int d = 0; d < (t == 0 ? NDMA : NA); ++d) copy_d(rq, rp, kill, smem + t * Cfg::STAGE, d);
+      for (int d = 0; d < (t == NS - 1 ? NA : NDMA); ++d) copy_d(rq, rp, kill, smem + t * Cfg::STAGE, d);
       copy_scales(cur, t, smem + t * Cfg::STAGE);
     }
-    // Position 0 has landed once at most the position-1 copies are open.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcntBase | vmcnt_bits(NA + Cfg::SC_MIN));
+    // Position 0 has landed once at most the copies of positions 1 .. NS-1
+    // are open.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcntBase | vmcnt_bits(Cfg::VM_MID + NA + Cfg::SC_MIN));
     __syncthreads();
     if constexpr (Op::MX) read_scales(smem);
 #pragma unroll
@@ -483,11 +496,11 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   }
 }
 
-template <class Op, bool PERSIST, bool PKM, int BP, int BQ>
+template <class Op, bool PERSIST, bool PKM, int BP, int BQ, int NS>
 __global__ void __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(TnCfg<Op, PKM, BP, BQ>::WPE, TnCfg<Op, PKM, BP, BQ>::WPE)))
+__attribute__((amdgpu_waves_per_eu(TnCfg<Op, PKM, BP, BQ, NS>::WPE, TnCfg<Op, PKM, BP, BQ, NS>::WPE)))
 gemm_tn_kernel(const GemmArgs a) {
-  gemm_tn_body<Op, PERSIST, PKM, BP, BQ>(a);
+  gemm_tn_body<Op, PERSIST, PKM, BP, BQ, NS>(a);
 }
 
 }  // namespace dg

@@ -76,7 +76,8 @@ def kernel_name(dtype, layout, M, N, K):
 
 # The four-wave kernel (K a multiple of the 16-byte chunk, at least two
 # 128-byte stages; NN reads B through transposing LDS reads), with each block
-# tile the shape table picks: exactly two stages, an odd stage count with edge
+# tile the shape table picks (and 128 x 128 with two and with four LDS
+# stages, the latter also with fewer stages than buffers): exactly two stages, an odd stage count with edge
 # tiles (N not a multiple of 8 in NN, so B's rows are padded and the last p
 # tile reads past the row end), a partial last stage, and 400 tiles of
 # 256 x 256, more than the CUs, so the persistent FP8 variant walks several
@@ -84,12 +85,16 @@ def kernel_name(dtype, layout, M, N, K):
 @pytest.mark.parametrize("dtype,layout", [(d, l) for d in ("f16", "bf16", "fp8") for l in ("tn", "nn")])
 def test_four_wave_kernel(dtype, layout):
     bk = {"f16": 64, "bf16": 64, "fp8": 128}[dtype]
-    small = "256x128" if (dtype, layout) == ("fp8", "nn") else "128x128"
-    shapes = [(512, 512, 2 * bk, small), (300, 521, 3 * bk, small), (5120, 5120, 3 * bk, "256x256"),
-              (1000, 1100, 9 * bk + 16, small), (2048, 1800, 2 * bk + 16, small)]
+    fp8nn = (dtype, layout) == ("fp8", "nn")
+    small = "256x128_w4" if fp8nn else "128x128_w4_s4"
+    mid = "256x128_w4" if fp8nn else "128x128_w4"
+    shapes = [(512, 512, 2 * bk, small), (300, 521, 3 * bk, small), (5120, 5120, 3 * bk, "256x256_w4"),
+              (1000, 1100, 9 * bk + 16, small), (2048, 1800, 2 * bk + 16, small), (2560, 2304, 3 * bk, mid),
+              (129, 77, 5 * bk + 16, small)]
     for idx, (M, N, K, tile) in enumerate(shapes):
         name = kernel_name(dtype, layout, M, N, K)
-        assert f"_{tile}_w4" in name, name
+        k = name.split()[0]
+        assert k.endswith(tile) or k.endswith(tile + "_persistent"), name
         p = make_problem(dtype, layout, M, N, K, seed=5000 + idx, pad=idx % 2)
         say(f"case w4 {name} M={M} N={N} K={K}")
         cij, pad = c_host(p, run_gpu(p))
