@@ -99,7 +99,7 @@ constexpr TileChoice kTiles[kNumTiles] = {
     {256, 256, 1, 1.00, 0}, {256, 128, 1, 0.76, 0}, {128, 128, 2, 0.78, 0}, {128, 128, 1, 0.47, 1}};
 constexpr int kPlanCus = 256;  // MI355X CUs, for the tile choice only
 
-int pick_tile(int64_t Pn, int64_t Qn, unsigned allowed) {
+int pick_tile(int64_t Pn, int64_t Qn, unsigned allowed, double* cost = nullptr) {
   int best = -1;
   double best_t = 0.0;
   for (int i = 0; i < kNumTiles; ++i) {
@@ -112,18 +112,22 @@ int pick_tile(int64_t Pn, int64_t Qn, unsigned allowed) {
     const double t = rounds * (double)c.bp * c.bq * c.per_cu / c.rate;
     if (best < 0 || t < best_t) { best = i; best_t = t; }
   }
+  if (cost) *cost = best_t;
   return best;
 }
 
+// Tiles a four-wave variant allows: p-contiguous FP8 P keeps 256-wide rows
+// (the transposing-read swizzle needs eight 32-byte units per row).
+unsigned tile_mask(int dt, bool nn) { return (nn && is_fp8(dt)) ? 0b0011u : 0b1101u; }
+
+// The four-wave launch of kTiles entry `idx` (one tile_mask allows).
 template <class Op, bool PKM>
-Launch tn_pick(const char* const names[kNumTiles], int64_t Pn, int64_t Qn) {
-  // p-contiguous FP8 P keeps 256-wide rows (the transposing-read swizzle
-  // needs eight 32-byte units per row).
+Launch tn_make(const char* const names[kNumTiles], int idx) {
   if constexpr (PKM && Op::ELEM == 1) {
-    if (pick_tile(Pn, Qn, 0b0011) == 1) return tn_launch<Op, PKM, 256, 128>(names[1]);
+    if (idx == 1) return tn_launch<Op, PKM, 256, 128>(names[1]);
     return tn_launch<Op, PKM, 256, 256>(names[0]);
   } else {
-    switch (pick_tile(Pn, Qn, 0b1101)) {
+    switch (idx) {
       case 2: return tn_launch<Op, PKM, 128, 128>(names[2]);
       case 3: return tn_launch<Op, PKM, 128, 128, 4>(names[3]);
       default: return tn_launch<Op, PKM, 256, 256>(names[0]);
@@ -155,73 +159,130 @@ Launch select_skinny(int dt, int64_t M) {
   return M <= 16 ? skinny_launch<OpBF16, 1>("bf16_tn_skinny16") : skinny_launch<OpBF16, 2>("bf16_tn_skinny32");
 }
 
-Launch select(int dt, int layout, int64_t M, int64_t N, int64_t K) {
+Launch four_wave(int dt, bool nn, int idx) {
+  static const char* const f16n[kNumTiles] = {"f16_nn_256x256_w4", nullptr, "f16_nn_128x128_w4",
+                                             "f16_nn_128x128_w4_s4"};
+  static const char* const bf16n[kNumTiles] = {"bf16_nn_256x256_w4", nullptr, "bf16_nn_128x128_w4",
+                                              "bf16_nn_128x128_w4_s4"};
+  static const char* const fp8n[kNumTiles] = {"fp8_nn_256x256_w4_persistent", "fp8_nn_256x128_w4", nullptr,
+                                              nullptr};
+  static const char* const fp8sn[kNumTiles] = {"fp8s_nn_256x256_w4_persistent", "fp8s_nn_256x128_w4", nullptr,
+                                               nullptr};
+  static const char* const mxn[kNumTiles] = {"mx8_nn_256x256_w4_persistent", "mx8_nn_256x128_w4", nullptr, nullptr};
+  static const char* const f16t[kNumTiles] = {"f16_tn_256x256_w4", nullptr, "f16_tn_128x128_w4",
+                                             "f16_tn_128x128_w4_s4"};
+  static const char* const bf16t[kNumTiles] = {"bf16_tn_256x256_w4", nullptr, "bf16_tn_128x128_w4",
+                                              "bf16_tn_128x128_w4_s4"};
+  static const char* const fp8t[kNumTiles] = {"fp8_tn_256x256_w4_persistent", nullptr, "fp8_tn_128x128_w4",
+                                              "fp8_tn_128x128_w4_s4"};
+  static const char* const fp8st[kNumTiles] = {"fp8s_tn_256x256_w4_persistent", nullptr, "fp8s_tn_128x128_w4",
+                                               "fp8s_tn_128x128_w4_s4"};
+  static const char* const mxt[kNumTiles] = {"mx8_tn_256x256_w4_persistent", nullptr, "mx8_tn_128x128_w4",
+                                             "mx8_tn_128x128_w4_s4"};
+  if (nn) {
+    switch (dt) {
+      case DT_F16: return tn_make<OpF16, true>(f16n, idx);
+      case DT_BF16: return tn_make<OpBF16, true>(bf16n, idx);
+      case DT_FP8S: return tn_make<OpFP8S, true>(fp8sn, idx);
+      case DT_MX8: return tn_make<OpMX8, true>(mxn, idx);
+      default: return tn_make<OpFP8, true>(fp8n, idx);
+    }
+  }
+  switch (dt) {
+    case DT_F16: return tn_make<OpF16, false>(f16t, idx);
+    case DT_BF16: return tn_make<OpBF16, false>(bf16t, idx);
+    case DT_FP8S: return tn_make<OpFP8S, false>(fp8st, idx);
+    case DT_MX8: return tn_make<OpMX8, false>(mxt, idx);
+    default: return tn_make<OpFP8, false>(fp8t, idx);
+  }
+}
+
+// The kernels of one call: a main launch, and optionally a second one over
+// the rest of one axis, p >= at (split_p) or q >= at.
+struct Choice {
+  Launch L;
+  bool split;
+  bool split_p;
+  int64_t at;
+  Launch T;
+};
+
+// When the 256 x 256 grid ends in a partial round, the call can run the
+// whole rounds with 256 x 256 tiles over the first part of the p or the q
+// range and the rest as a second launch with the tile the table picks for
+// it (e.g. bf16 6144^2 x 4096: 1032 -> 1157 TF/s, fp8 8192 x 5120 x 8192:
+// 2287 -> 2540 TF/s).  Taken when the cost model (rounds x round time, as
+// pick_tile) gains at least 5%.
+Choice choose(int dt, int layout, int64_t M, int64_t N, int64_t K) {
   const bool nn = layout == DGEMM_NN;
+  const int64_t Pn = nn ? N : M, Qn = nn ? M : N;
+  Choice c{};
   if (dt == DT_MX8) {
     // MXFP8 (K a multiple of 32) takes the four-wave kernel; below two
     // stages only the one-tile-per-workgroup tiles.  K == 0 (C = 0, no
     // scale is read) goes to the eight-wave kernel's zero fill.
-    if (K == 0) return nn ? mfma_launch<OpFP8, true>("fp8_nn_256x256") : mfma_launch<OpFP8, false>("fp8_tn_256x256");
-    const int64_t Pn = nn ? N : M, Qn = nn ? M : N;
-    if (K < 256) return nn ? tn_launch<OpMX8, true, 256, 128>("mx8_nn_256x128_w4")
-                           : tn_launch<OpMX8, false, 128, 128>("mx8_tn_128x128_w4");
-    static const char* const mxn[kNumTiles] = {"mx8_nn_256x256_w4_persistent", "mx8_nn_256x128_w4", nullptr, nullptr};
-    static const char* const mxt[kNumTiles] = {"mx8_tn_256x256_w4_persistent", nullptr, "mx8_tn_128x128_w4",
-                                               "mx8_tn_128x128_w4_s4"};
-    return nn ? tn_pick<OpMX8, true>(mxn, Pn, Qn) : tn_pick<OpMX8, false>(mxt, Pn, Qn);
+    if (K == 0) {
+      c.L = nn ? mfma_launch<OpFP8, true>("fp8_nn_256x256") : mfma_launch<OpFP8, false>("fp8_tn_256x256");
+      return c;
+    }
+    if (K < 256) {
+      c.L = nn ? tn_launch<OpMX8, true, 256, 128>("mx8_nn_256x128_w4")
+               : tn_launch<OpMX8, false, 128, 128>("mx8_tn_128x128_w4");
+      return c;
+    }
   }
   // K a whole number of 16-byte chunks and at least two stages: the
   // four-wave kernel (gemm_tn.hpp), tile chosen by shape; NN reads B with
   // transposing LDS reads.
-  if (dt != DT_F32) {
-    const int e = in_elem(dt);
-    if (K % (16 / e) == 0 && K >= 2 * (128 / e)) {
-      const int64_t Pn = nn ? N : M, Qn = nn ? M : N;
-      static const char* const f16n[kNumTiles] = {"f16_nn_256x256_w4", nullptr, "f16_nn_128x128_w4",
-                                                 "f16_nn_128x128_w4_s4"};
-      static const char* const bf16n[kNumTiles] = {"bf16_nn_256x256_w4", nullptr, "bf16_nn_128x128_w4",
-                                                 "bf16_nn_128x128_w4_s4"};
-      static const char* const fp8n[kNumTiles] = {"fp8_nn_256x256_w4_persistent", "fp8_nn_256x128_w4", nullptr,
-                                                  nullptr};
-      static const char* const f16t[kNumTiles] = {"f16_tn_256x256_w4", nullptr, "f16_tn_128x128_w4",
-                                                 "f16_tn_128x128_w4_s4"};
-      static const char* const bf16t[kNumTiles] = {"bf16_tn_256x256_w4", nullptr, "bf16_tn_128x128_w4",
-                                                 "bf16_tn_128x128_w4_s4"};
-      static const char* const fp8t[kNumTiles] = {"fp8_tn_256x256_w4_persistent", nullptr, "fp8_tn_128x128_w4",
-                                                  "fp8_tn_128x128_w4_s4"};
-      static const char* const fp8sn[kNumTiles] = {"fp8s_nn_256x256_w4_persistent", "fp8s_nn_256x128_w4", nullptr,
-                                                   nullptr};
-      static const char* const fp8st[kNumTiles] = {"fp8s_tn_256x256_w4_persistent", nullptr, "fp8s_tn_128x128_w4",
-                                                   "fp8s_tn_128x128_w4_s4"};
-      if (nn) {
-        switch (dt) {
-          case DT_F16: return tn_pick<OpF16, true>(f16n, Pn, Qn);
-          case DT_BF16: return tn_pick<OpBF16, true>(bf16n, Pn, Qn);
-          case DT_FP8S: return tn_pick<OpFP8S, true>(fp8sn, Pn, Qn);
-          default: return tn_pick<OpFP8, true>(fp8n, Pn, Qn);
-        }
-      }
-      switch (dt) {
-        case DT_F16: return tn_pick<OpF16, false>(f16t, Pn, Qn);
-        case DT_BF16: return tn_pick<OpBF16, false>(bf16t, Pn, Qn);
-        case DT_FP8S: return tn_pick<OpFP8S, false>(fp8st, Pn, Qn);
-        default: return tn_pick<OpFP8, false>(fp8t, Pn, Qn);
+  const int e = in_elem(dt);
+  if (dt == DT_MX8 || (dt != DT_F32 && K % (16 / e) == 0 && K >= 2 * (128 / e))) {
+    const unsigned mask = tile_mask(dt, nn);
+    double whole = 0.0;
+    const int idx = pick_tile(Pn, Qn, mask, &whole);
+    c.L = four_wave(dt, nn, idx);
+    const int64_t slots = kPlanCus;
+    const int64_t tp = (Pn + 255) / 256, tq = (Qn + 255) / 256, tiles = tp * tq;
+    double best = 0.95 * whole;
+    for (int axis = 0; axis < 2 && tiles % slots != 0; ++axis) {
+      // axis 0 splits q, axis 1 splits p: n1 whole tiles of the split axis
+      // fit the full rounds.
+      const int64_t across = axis == 0 ? tp : tq, along = axis == 0 ? tq : tp;
+      const int64_t n1 = (tiles / slots) * slots / across;
+      if (n1 < 1 || n1 >= along) continue;
+      double tail = 0.0;
+      const int tidx = axis == 0 ? pick_tile(Pn, Qn - 256 * n1, mask, &tail)
+                                 : pick_tile(Pn - 256 * n1, Qn, mask, &tail);
+      const double cost = (double)((across * n1 + slots - 1) / slots) * 65536.0 + tail;
+      if (cost < best) {
+        best = cost;
+        c.L = four_wave(dt, nn, 0);
+        c.split = true;
+        c.split_p = axis == 1;
+        c.at = 256 * n1;
+        c.T = four_wave(dt, nn, tidx);
       }
     }
+    return c;
   }
   switch (dt) {
-    case DT_F32:  return nn ? f32_launch<true>("f32_nn_128x128") : f32_launch<false>("f32_tn_128x128");
-    case DT_F16:  return nn ? mfma_launch<OpF16, true>("f16_nn_256x256") : mfma_launch<OpF16, false>("f16_tn_256x256");
-    case DT_BF16: return nn ? mfma_launch<OpBF16, true>("bf16_nn_256x256") : mfma_launch<OpBF16, false>("bf16_tn_256x256");
-    case DT_FP8S: return nn ? mfma_launch<OpFP8S, true>("fp8s_nn_256x256") : mfma_launch<OpFP8S, false>("fp8s_tn_256x256");
-    default:      return nn ? mfma_launch<OpFP8, true>("fp8_nn_256x256") : mfma_launch<OpFP8, false>("fp8_tn_256x256");
+    case DT_F32:  c.L = nn ? f32_launch<true>("f32_nn_128x128") : f32_launch<false>("f32_tn_128x128"); break;
+    case DT_F16:  c.L = nn ? mfma_launch<OpF16, true>("f16_nn_256x256") : mfma_launch<OpF16, false>("f16_tn_256x256"); break;
+    case DT_BF16: c.L = nn ? mfma_launch<OpBF16, true>("bf16_nn_256x256") : mfma_launch<OpBF16, false>("bf16_tn_256x256"); break;
+    case DT_FP8S: c.L = nn ? mfma_launch<OpFP8S, true>("fp8s_nn_256x256") : mfma_launch<OpFP8S, false>("fp8s_tn_256x256"); break;
+    default:      c.L = nn ? mfma_launch<OpFP8, true>("fp8_nn_256x256") : mfma_launch<OpFP8, false>("fp8_tn_256x256"); break;
   }
+  return c;
 }
 
 struct Plan {
   Launch L;
   GemmArgs g;
   int64_t grid;
+  bool split;      // a second launch over p or q >= the split point
+  bool split_p;
+  Launch L2;
+  GemmArgs g2;
+  int64_t grid2;
 };
 
 // Scale factors of gemm_fp8_scaled: na values at sa (1 or M), nb at sb (1 or N).
@@ -249,6 +310,7 @@ int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
   if (M < 0 || N < 0 || K < 0) return DGEMM_ERR_INVALID_DIM;
   if (sc && ((sc->na != 1 && sc->na != M) || (sc->nb != 1 && sc->nb != N))) return DGEMM_ERR_INVALID_DIM;
   if (dt == DT_MX8 && K % 32 != 0) return DGEMM_ERR_INVALID_DIM;
+  out->split = false;
   if (M == 0 || N == 0) { out->grid = 0; return DGEMM_OK; }
   if (check_pointers && ((K > 0 && (A == nullptr || B == nullptr)) || C == nullptr)) return DGEMM_ERR_NULL_POINTER;
   if (check_pointers && sc && (sc->sa == nullptr || sc->sb == nullptr)) return DGEMM_ERR_NULL_POINTER;
@@ -270,7 +332,10 @@ int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
     return DGEMM_ERR_MISALIGNED;
 
   const bool skinny = use_skinny(dt, layout, M);
-  Launch L = skinny ? select_skinny(dt, M) : select(dt, layout, M, N, K);
+  Choice ch{};
+  if (skinny) ch.L = select_skinny(dt, M);
+  else ch = choose(dt, layout, M, N, K);
+  const Launch L = ch.L;
   GemmArgs g{};
   if (!nn) {
     g.P = (const char*)A; g.ldp = lda * e; g.Pn = M;
@@ -297,20 +362,73 @@ int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
     g.ldsq = nn ? mx->ldsa : mx->ldsb;
   }
   // Descriptor ranges must stay below 2^31 bytes.
-  if ((int64_t)L.bq * g.ldq > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
-  if (!L.p_trans && (int64_t)L.bp * g.ldp > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
-  if (L.p_trans && K * g.ldp > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
+  for (const Launch* l : {&ch.L, &ch.T}) {
+    if (l == &ch.T && !ch.split) break;
+    if ((int64_t)l->bq * g.ldq > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
+    if (!l->p_trans && (int64_t)l->bp * g.ldp > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
+    if (l->p_trans && K * g.ldp > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
+  }
   if (K * e > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
-  g.tiles_p = skinny ? 1 : (g.Pn + L.bp - 1) / L.bp;
-  g.tiles_q = (g.Qn + L.bq - 1) / L.bq;
   g.group = 8;
   const int oe = out_elem(dt);
   g.vec_store = ((((uintptr_t)C) % (uintptr_t)(4 * oe)) == 0 && ((ldc * oe) % (4 * oe)) == 0) ? 1 : 0;
   g.vec16 = ((((uintptr_t)C) % 16) == 0 && ((ldc * oe) % 16) == 0) ? 1 : 0;
+  if (ch.split) {
+    // The second launch covers q >= at (rows of Q and of the factor / scale
+    // arrays along q, columns of D) or p >= at (rows of P -- for
+    // p-contiguous P its columns --, factors along p, rows of D).
+    GemmArgs g2 = g;
+    const int64_t x0 = ch.at;
+    if (!ch.split_p) {
+      g2.Q = g.Q + x0 * g.ldq;
+      g2.C = (char*)C + x0 * ldc * oe;
+      g2.Qn = g.Qn - x0;
+      if (g.sq && g.sq_row) g2.sq = g.sq + x0;
+      if (g.msq) g2.msq = g.msq + x0 * g.ldsq;
+      g.Qn = x0;
+    } else {
+      g2.P = g.P + (ch.L.p_trans ? x0 * e : x0 * g.ldp);
+      g2.C = (char*)C + x0 * oe;
+      g2.Pn = g.Pn - x0;
+      if (g.sp && g.sp_row) g2.sp = g.sp + x0;
+      if (g.msp) g2.msp = g.msp + x0 * g.ldsp;
+      g.Pn = x0;
+    }
+    g2.tiles_p = (g2.Pn + ch.T.bp - 1) / ch.T.bp;
+    g2.tiles_q = (g2.Qn + ch.T.bq - 1) / ch.T.bq;
+    out->split = true;
+    out->split_p = ch.split_p;
+    out->L2 = ch.T;
+    out->g2 = g2;
+    out->grid2 = g2.tiles_p * g2.tiles_q;
+    if (out->grid2 > 0x7fffffff) return DGEMM_ERR_UNSUPPORTED;
+  }
+  g.tiles_p = skinny ? 1 : (g.Pn + L.bp - 1) / L.bp;
+  g.tiles_q = (g.Qn + L.bq - 1) / L.bq;
   out->L = L;
   out->g = g;
   out->grid = g.tiles_p * g.tiles_q;
   if (out->grid > 0x7fffffff) return DGEMM_ERR_UNSUPPORTED;
+  return DGEMM_OK;
+}
+
+// One launch on the caller's stream.  Persistent kernels run one workgroup
+// per CU, rounded down to a multiple of the XCD count so that every tile of
+// a workgroup maps to the workgroup's own XCD.
+int launch(const Launch& L, const GemmArgs& g, int64_t grid, void* stream) {
+  if (L.persistent) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_failed(e);
+    if (cus <= 0) return hip_failed(hipErrorInvalidValue);
+    if (cus >= kXcds) cus -= cus % kXcds;
+    if (grid > cus) grid = cus;
+  }
+  GemmArgs arg = g;
+  void* args[] = {(void*)&arg};
+  const hipError_t err = hipLaunchKernel(L.fn, dim3((unsigned)grid), dim3(L.threads), args, 0, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_failed(err);
   return DGEMM_OK;
 }
 
@@ -319,22 +437,9 @@ int run(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
   Plan pl;
   const int st = plan(dt, M, N, K, A, lda, B, ldb, C, ldc, layout, &pl, true, sc, mx);
   if (st != DGEMM_OK || pl.grid == 0) return st;
-  if (pl.L.persistent) {
-    // One workgroup per CU, rounded down to a multiple of the XCD count so
-    // that every tile of a workgroup maps to the workgroup's own XCD.
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return hip_failed(e);
-    if (cus <= 0) return hip_failed(hipErrorInvalidValue);
-    if (cus >= kXcds) cus -= cus % kXcds;
-    if (pl.grid > cus) pl.grid = cus;
-  }
-  void* args[] = {(void*)&pl.g};
-  const hipError_t err = hipLaunchKernel(pl.L.fn, dim3((unsigned)pl.grid), dim3(pl.L.threads), args, 0,
-                                         (hipStream_t)stream);
-  if (err != hipSuccess) return hip_failed(err);
-  return DGEMM_OK;
+  const int r = launch(pl.L, pl.g, pl.grid, stream);
+  if (r != DGEMM_OK || !pl.split) return r;
+  return launch(pl.L2, pl.g2, pl.grid2, stream);
 }
 
 }  // namespace
@@ -421,10 +526,18 @@ int dgemm_kernel_config(int dtype, int layout, int64_t M, int64_t N, int64_t K, 
   if (buf && len > 0) {
     if (pl.grid == 0)
       snprintf(buf, (size_t)len, "none (empty output)");
-    else
+    else if (!pl.split)
       snprintf(buf, (size_t)len, "%s tile=%dx%d threads=%d lds=%d grid=%lld tiles=%lldx%lld group=%lld",
                pl.L.name, pl.L.bp, pl.L.bq, pl.L.threads, pl.L.lds, (long long)pl.grid, (long long)pl.g.tiles_p,
                (long long)pl.g.tiles_q, (long long)pl.g.group);
+    else
+      snprintf(buf, (size_t)len,
+               "%s tile=%dx%d threads=%d lds=%d grid=%lld tiles=%lldx%lld group=%lld"
+               " + %s tile=%dx%d lds=%d grid=%lld tiles=%lldx%lld from %c=%lld",
+               pl.L.name, pl.L.bp, pl.L.bq, pl.L.threads, pl.L.lds, (long long)pl.grid, (long long)pl.g.tiles_p,
+               (long long)pl.g.tiles_q, (long long)pl.g.group, pl.L2.name, pl.L2.bp, pl.L2.bq, pl.L2.lds,
+               (long long)pl.grid2, (long long)pl.g2.tiles_p, (long long)pl.g2.tiles_q, pl.split_p ? 'p' : 'q',
+               (long long)(pl.split_p ? pl.g.Pn : pl.g.Qn));
   }
   return DGEMM_OK;
 }

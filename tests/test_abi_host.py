@@ -205,17 +205,46 @@ def _kernel(lib, dt, layout, M, N, K):
     (4096, 4096, 4096, "256x256_w4", "256x256_w4"),    # one full round vs two
     (3072, 4096, 8192, "256x256_w4", "256x256_w4"),    # 192 tiles: one round vs two
     (5120, 5120, 1024, "256x256_w4", "256x256_w4"),    # 400 tiles: 2 rounds (2) vs 4 (2.56)
-    (4352, 4352, 1024, "128x128_w4", "256x128_w4"),    # 289 tiles: 2 rounds (2) vs 3 (1.92)
     (2560, 2304, 4096, "128x128_w4", "256x128_w4"),    # 360 tiles of 128 x 128: one round at two per CU
     (2048, 2048, 2048, "128x128_w4_s4", "256x128_w4"),  # 256 tiles of 128 x 128, one per CU
     (300, 521, 512, "128x128_w4_s4", "256x128_w4"),
 ])
 def test_tile_choice(lib, M, N, K, tile16, tile8nn):
-    for dt in (1, 2, 3, 4):
+    for dt in (1, 2, 3, 4, 5):
         for layout in (0, 1):
-            d = _kernel(lib, dt, layout, M, N, K).split()[0]
+            full = _kernel(lib, dt, layout, M, N, K)
+            d = full.split()[0]
             want = tile8nn if dt >= 3 and layout == 0 else tile16
-            assert d.endswith(want) or d.endswith(want + "_persistent"), (dt, layout, d)
+            assert d.endswith(want) or d.endswith(want + "_persistent"), (dt, layout, full)
+            assert " + " not in full, full
+
+
+# A 256 x 256 grid that ends in a partial round: its whole rounds run as one
+# launch over the first part of q (TN: columns of C) or p, the rest as a
+# second launch with the tile the table picks for it.
+@pytest.mark.parametrize("dt,layout,M,N,K,axis,at,tail", [
+    (2, 1, 4096, 14336, 4096, "q", 12288, "bf16_tn_128x128_w4"),    # 896 tiles: 3 rounds + 4096 x 2048
+    (3, 1, 4096, 14336, 4096, "q", 12288, "fp8_tn_128x128_w4"),
+    (5, 1, 4096, 14336, 4096, "q", 12288, "mx8_tn_128x128_w4"),
+    (2, 0, 4096, 14336, 4096, "p", 12288, "bf16_nn_128x128_w4"),    # NN: p runs along N
+    (3, 0, 4096, 14336, 4096, "p", 12288, "fp8_nn_256x128_w4"),
+    (2, 1, 14336, 4096, 4096, "p", 12288, "bf16_tn_128x128_w4"),
+    (1, 1, 6144, 6144, 4096, "q", 5376, "f16_tn_128x128_w4"),        # 576 tiles: 504 + 48 x 6 of 128
+    (2, 1, 4352, 4352, 1024, "q", 3840, "bf16_tn_128x128_w4_s4"),    # 289 tiles: 255 + 136 of 128, one per CU
+    (4, 1, 2560, 14336, 8192, "q", 13056, "fp8s_tn_128x128_w4_s4"),
+])
+def test_split_choice(lib, dt, layout, M, N, K, axis, at, tail):
+    full = _kernel(lib, dt, layout, M, N, K)
+    main, rest = full.split(" + ")
+    assert "256x256_w4" in main.split()[0], full
+    assert rest.split()[0] == tail, full
+    assert rest.endswith(f"from {axis}={at}"), full
+
+
+@pytest.mark.parametrize("M,N,K", [(8192, 8192, 8192), (3584, 8192, 8192), (8191, 8190, 8200), (3072, 4096, 8192)])
+def test_no_split_when_rounds_are_whole_or_it_does_not_pay(lib, M, N, K):
+    for dt in (1, 2, 3):
+        assert " + " not in _kernel(lib, dt, 1, M, N, K)
     # FP8 TN at 256 x 256 runs persistent workgroups, a multiple of the 8 XCDs.
     assert "persistent" in _kernel(lib, 3, 1, 5120, 5120, 1024)
     # K not a whole number of 16-byte chunks: the eight-wave kernel.

@@ -88,13 +88,18 @@ def test_four_wave_kernel(dtype, layout):
     fp8nn = (dtype, layout) == ("fp8", "nn")
     small = "256x128_w4" if fp8nn else "128x128_w4_s4"
     mid = "256x128_w4" if fp8nn else "128x128_w4"
+    # the last two split into whole 256 x 256 rounds plus a second launch
+    # (along q, then along p)
+    psplit = (14336, 4096) if layout == "tn" else (4096, 14336)
     shapes = [(512, 512, 2 * bk, small), (300, 521, 3 * bk, small), (5120, 5120, 3 * bk, "256x256_w4"),
               (1000, 1100, 9 * bk + 16, small), (2048, 1800, 2 * bk + 16, small), (2560, 2304, 3 * bk, mid),
-              (129, 77, 5 * bk + 16, small)]
+              (129, 77, 5 * bk + 16, small), (4352, 4352, 3 * bk, "256x256_w4"),
+              (psplit[0], psplit[1], 3 * bk, "256x256_w4")]
     for idx, (M, N, K, tile) in enumerate(shapes):
         name = kernel_name(dtype, layout, M, N, K)
         k = name.split()[0]
         assert k.endswith(tile) or k.endswith(tile + "_persistent"), name
+        assert (" + " in name) == (idx >= 7), name
         p = make_problem(dtype, layout, M, N, K, seed=5000 + idx, pad=idx % 2)
         say(f"case w4 {name} M={M} N={N} K={K}")
         cij, pad = c_host(p, run_gpu(p))
@@ -275,7 +280,8 @@ def compare_scaled(p, cij, sa, sb, rows=None, exact=False):
 def test_fp8_scaled_against_oracle(layout, mode):
     rng = np.random.default_rng(6000 + (layout == "nn") + 2 * (mode == "row"))
     shapes = [(1, 1, 1), (257, 129, 77), (33, 65, 300), (300, 521, 384), (512, 512, 256), (1000, 1100, 1168),
-              (5120, 5120, 384), (70, 90, 0)]
+              (5120, 5120, 384), (70, 90, 0), (4352, 4352, 384), (14336, 4096, 384) if layout == "tn" else
+              (4096, 14336, 384)]
     for idx, (M, N, K) in enumerate(shapes):
         p = make_problem("fp8", layout, M, N, K, seed=6100 + idx, pad=idx % 2)
         sa = _factors(rng, M if mode == "row" else 1)
@@ -370,7 +376,8 @@ def compare_mx(p, cij, SA, ldsa, SB, ldsb, rows=None, exact=False):
 def test_mxfp8_against_oracle(layout):
     rng = np.random.default_rng(7000 + (layout == "nn"))
     shapes = [(1, 1, 32), (33, 65, 96), (257, 129, 224), (300, 521, 384), (512, 512, 256), (1000, 1100, 1184),
-              (5120, 5120, 384), (70, 90, 0)]
+              (5120, 5120, 384), (70, 90, 0), (4352, 4352, 384), (14336, 4096, 384) if layout == "tn" else
+              (4096, 14336, 384)]
     for idx, (M, N, K) in enumerate(shapes):
         p = make_problem("fp8", layout, M, N, K, seed=7100 + idx, pad=idx % 2)
         nb = K // 32
