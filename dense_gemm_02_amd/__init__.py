@@ -6,5 +6,5 @@ arguments to it (``dense_gemm_02_amd.binding``).  Importing the package does
 not load the library; the first call does, and fails loudly if it is missing.
 """
 
-from .binding import (gemm, gemm_f32, gemm_f16, gemm_bf16, gemm_fp8, gemm_strerror,  # noqa: F401
-                      DgemmError, library_path, load_library)
+from .binding import (gemm, gemm_f32, gemm_f16, gemm_bf16, gemm_fp8, gemm_fp8_scaled, gemm_mxfp8,  # noqa: F401
+                      gemm_scaled, gemm_mx, matmul, gemm_strerror, DgemmError, library_path, load_library)

@@ -193,3 +193,72 @@ def gemm_mx(layout, M, N, K, A, lda, B, ldb, C, ldc, scale_a, ldsa, scale_b, lds
         raise TypeError("block scales are bytes")
     gemm_mxfp8(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, scale_a.data_ptr(), ldsa,
                scale_b.data_ptr(), ldsb, layout, stream)
+
+
+_TORCH_DT = None
+
+
+def _dtype_name(t):
+    import torch
+    global _TORCH_DT
+    if _TORCH_DT is None:
+        _TORCH_DT = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16",
+                     torch.float8_e4m3fn: "fp8"}
+    if t.dtype not in _TORCH_DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _TORCH_DT[t.dtype]
+
+
+def matmul(a, b, out=None, scale_a=None, scale_b=None, stream=None):
+    """C = A x B for device tensors, the layout read from the strides.
+
+    a: M x K row-major (stride(1) == 1).  b: K x N, either row-major (NN) or
+    column-major (stride(0) == 1, TN: e.g. ``bt.t()`` of an N x K row-major
+    tensor).  The result has the layout the library writes: row-major M x N
+    for NN, column-major M x N (a transposed N x M tensor) for TN.  FP8
+    (``torch.float8_e4m3fn``) returns float32; ``scale_a`` / ``scale_b``
+    (float32 tensors of 1 or M / 1 or N values) select gemm_fp8_scaled.
+    ``out`` may be given with the same layout and dtype.
+    """
+    import torch
+    for t in (a, b):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError("a and b must be device tensors")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError(f"shapes {tuple(a.shape)} and {tuple(b.shape)} do not chain")
+    dt = _dtype_name(a)
+    if _dtype_name(b) != dt:
+        raise TypeError("a and b must share a dtype")
+    M, K = a.shape
+    N = b.shape[1]
+    if a.stride(1) != 1 and M * K > 1:
+        raise ValueError("a must be row-major (stride(1) == 1)")
+    lda = a.stride(0) if M > 1 else max(K, 1)
+    if b.stride(1) == 1 and (b.stride(0) != 1 or N == 1):
+        layout, ldb = "nn", (b.stride(0) if K > 1 else max(N, 1))
+    elif b.stride(0) == 1:
+        layout, ldb = "tn", (b.stride(1) if N > 1 else max(K, 1))
+    else:
+        raise ValueError("b must be row-major or column-major")
+    odt = torch.float32 if dt in ("f32", "fp8") else a.dtype
+    if out is None:
+        out = (torch.empty((M, N), dtype=odt, device=a.device) if layout == "nn"
+               else torch.empty((N, M), dtype=odt, device=a.device).t())
+    if out.shape != (M, N) or out.dtype != odt or not out.is_cuda:
+        raise ValueError("out must be a device tensor of shape (M, N) and the output dtype")
+    if layout == "nn":
+        if out.stride(1) != 1 and M * N > 1:
+            raise ValueError("NN writes a row-major C")
+        ldc = out.stride(0) if M > 1 else max(N, 1)
+    else:
+        if out.stride(0) != 1 and M * N > 1:
+            raise ValueError("TN writes a column-major C")
+        ldc = out.stride(1) if N > 1 else max(M, 1)
+    if scale_a is not None or scale_b is not None:
+        if dt != "fp8" or scale_a is None or scale_b is None:
+            raise ValueError("scale factors go with fp8 operands, both of them")
+        gemm_fp8_scaled(M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, scale_a.data_ptr(),
+                        scale_a.numel(), scale_b.data_ptr(), scale_b.numel(), layout, stream)
+    else:
+        _raw("gemm_" + dt, M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, layout, stream)
+    return out

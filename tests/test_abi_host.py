@@ -249,3 +249,12 @@ def test_no_split_when_rounds_are_whole_or_it_does_not_pay(lib, M, N, K):
     assert "persistent" in _kernel(lib, 3, 1, 5120, 5120, 1024)
     # K not a whole number of 16-byte chunks: the eight-wave kernel.
     assert "_w4" not in _kernel(lib, 2, 1, 4096, 4096, 4100)
+
+
+def test_matmul_rejects_host_and_mismatched_tensors():
+    import torch
+    from dense_gemm_02_amd import matmul
+    with pytest.raises(TypeError):
+        matmul(torch.ones(2, 3), torch.ones(3, 4))
+    with pytest.raises(TypeError):
+        matmul(np.ones((2, 3)), np.ones((3, 4)))

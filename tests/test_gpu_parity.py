@@ -412,3 +412,37 @@ def test_mxfp8_bit_exact(layout):
             c1, _ = c_host(p, run_mx(p, one[:M], ld, one[:N], ld))
             c0, _ = c_host(p, run_gpu(p))
             assert np.array_equal(c1, c0)
+
+
+# The tensor-level face: layouts read from strides, against the oracle.
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "fp8"])
+def test_matmul_tensor_api(dtype):
+    import torch
+    from dense_gemm_02_amd import matmul
+    from gpu_util import oracle
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[dtype]
+    for layout in ("nn", "tn"):
+        M, N, K = 200, 136, 320
+        p = make_problem(dtype, layout, M, N, K, seed=8000 + (layout == "tn"))
+        A = to_dev(p.A).view(tdt) if dtype != "fp8" else to_dev(p.A).view(tdt)
+        B = to_dev(p.B).view(tdt)
+        a = A.view(-1)[: M * p.lda].view(M, p.lda)[:, :K]
+        if layout == "nn":
+            b = B.view(-1)[: K * p.ldb].view(K, p.ldb)[:, :N]
+        else:
+            b = B.view(-1)[: N * p.ldb].view(N, p.ldb)[:, :K].t()
+        say(f"case matmul {dtype} {layout}")
+        c = matmul(a, b)
+        torch.cuda.synchronize()
+        assert c.shape == (M, N)
+        bits = c.contiguous().view(torch.int32 if c.element_size() == 4 else torch.int16).cpu().numpy()
+        cij = bits.view(np.uint32) if c.element_size() == 4 else bits.view(np.uint16)
+        ok, err, nbad = compare(p, np.ascontiguousarray(cij))
+        assert ok, f"{dtype} {layout}: max err {err:.3e}"
+    # scale factors through the same face
+    if dtype == "fp8":
+        sa = torch.full((M,), 0.5, device="cuda")
+        sb = torch.full((N,), 4.0, device="cuda")
+        c2 = matmul(a, b, scale_a=sa, scale_b=sb)
+        torch.cuda.synchronize()
+        assert torch.equal(c2, 2.0 * matmul(a, b))
