@@ -446,3 +446,41 @@ def test_matmul_tensor_api(dtype):
         c2 = matmul(a, b, scale_a=sa, scale_b=sb)
         torch.cuda.synchronize()
         assert torch.equal(c2, 2.0 * matmul(a, b))
+
+
+# Maximum sizes: leading dimensions at the 32-bit descriptor limit (the bytes
+# one block tile spans stay below 2^31), operands placed in the first K (NN B:
+# N) columns of huge device rows; the oracle sees the compact problem.
+@pytest.mark.parametrize("dtype,layout", [("bf16", "tn"), ("fp8", "tn"), ("bf16", "nn"), ("fp8", "nn")])
+def test_leading_dimensions_at_the_descriptor_limit(dtype, layout):
+    import torch
+    from dense_gemm_02_amd import binding
+    e = {"bf16": 2, "fp8": 1}[dtype]
+    bk = 128 // e
+    M, N, K = 300, 280, 3 * bk
+    p = make_problem(dtype, layout, M, N, K, seed=8100)
+    limit = (1 << 31) - 64
+    al = 16 // e
+    big_q = ((limit // (256 * e)) // al) * al               # K-contiguous operand: 256 rows per block
+    lda = big_q
+    ldb = big_q if layout == "tn" else ((limit // (K * e)) // al) * al   # NN B: K rows per block
+    assert 256 * lda * e <= limit and (256 * ldb * e <= limit if layout == "tn" else K * ldb * e <= limit)
+    tdt = torch.uint8 if e == 1 else torch.int16
+    A = torch.zeros((M, lda), dtype=tdt, device="cuda")
+    A[:, :K] = to_dev(p.A).view(M, p.lda)[:, :K]
+    if layout == "tn":
+        B = torch.zeros((N, ldb), dtype=tdt, device="cuda")
+        B[:, :K] = to_dev(p.B).view(N, p.ldb)[:, :K]
+    else:
+        B = torch.zeros((K, ldb), dtype=tdt, device="cuda")
+        B[:, :N] = to_dev(p.B).view(K, p.ldb)[:, :N]
+    C = alloc_c(p)
+    say(f"case limit {dtype} {layout} lda={lda} ldb={ldb}")
+    binding.gemm(dtype, layout, M, N, K, A, lda, B, ldb, C, p.ldc)
+    torch.cuda.synchronize()
+    cij, pad = c_host(p, C)
+    assert pad_untouched(pad, dtype)
+    ok, err, nbad = compare(p, cij)
+    assert ok, f"max err {err:.3e}, {nbad} bad"
+    del A, B
+    torch.cuda.empty_cache()
