@@ -125,7 +125,7 @@ def time_gemm(dtype, steps, warmup, spec=None, rotate=1):
         sb = torch.from_numpy(rng.uniform(0.5, 2.0, p.N).astype(np.float32)).cuda()
     elif variant == "mx":
         # E8M0 codes 2^-7 .. 2^7, K/32 per row
-        ld = ((p.K // 32 + 3) // 4) * 4
+        ld = ((p.K // 32 + 15) // 16) * 16
         sa = torch.from_numpy(rng.integers(120, 135, (p.M, ld)).astype(np.uint8)).cuda()
         sb = torch.from_numpy(rng.integers(120, 135, (p.N, ld)).astype(np.uint8)).cuda()
 

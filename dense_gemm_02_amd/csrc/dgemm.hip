@@ -68,7 +68,7 @@ template <class Op, bool PKM, int BP, int BQ, int NS = 2>
 Launch tn_launch(const char* name) {
   using Cfg = TnCfg<Op, PKM, BP, BQ, NS>;
   constexpr bool P = Op::ELEM == 1 && BP == 256 && BQ == 256;
-  return Launch{(const void*)&gemm_tn_kernel<Op, P, PKM, BP, BQ, NS>, name, BP, BQ, Cfg::NT, NS * Cfg::STAGE, PKM, P};
+  return Launch{(const void*)&gemm_tn_kernel<Op, P, PKM, BP, BQ, NS>, name, BP, BQ, Cfg::NT, Cfg::LDS, PKM, P};
 }
 
 // Block tiles of the four-wave kernel and their throughput relative to the
@@ -118,7 +118,12 @@ int pick_tile(int64_t Pn, int64_t Qn, unsigned allowed, double* cost = nullptr) 
 
 // Tiles a four-wave variant allows: p-contiguous FP8 P keeps 256-wide rows
 // (the transposing-read swizzle needs eight 32-byte units per row).
-unsigned tile_mask(int dt, bool nn) { return (nn && is_fp8(dt)) ? 0b0011u : 0b1101u; }
+// MXFP8's scale ring needs two LDS stages, so it leaves out the four-stage
+// tile.
+unsigned tile_mask(int dt, bool nn) {
+  if (nn && is_fp8(dt)) return 0b0011u;
+  return dt == DT_MX8 ? 0b0101u : 0b1101u;
+}
 
 // The four-wave launch of kTiles entry `idx` (one tile_mask allows).
 template <class Op, bool PKM>
@@ -129,7 +134,9 @@ Launch tn_make(const char* const names[kNumTiles], int idx) {
   } else {
     switch (idx) {
       case 2: return tn_launch<Op, PKM, 128, 128>(names[2]);
-      case 3: return tn_launch<Op, PKM, 128, 128, 4>(names[3]);
+      case 3:
+        if constexpr (!Op::MX) return tn_launch<Op, PKM, 128, 128, 4>(names[3]);
+        [[fallthrough]];
       default: return tn_launch<Op, PKM, 256, 256>(names[0]);
     }
   }
@@ -177,8 +184,7 @@ Launch four_wave(int dt, bool nn, int idx) {
                                               "fp8_tn_128x128_w4_s4"};
   static const char* const fp8st[kNumTiles] = {"fp8s_tn_256x256_w4_persistent", nullptr, "fp8s_tn_128x128_w4",
                                                "fp8s_tn_128x128_w4_s4"};
-  static const char* const mxt[kNumTiles] = {"mx8_tn_256x256_w4_persistent", nullptr, "mx8_tn_128x128_w4",
-                                             "mx8_tn_128x128_w4_s4"};
+  static const char* const mxt[kNumTiles] = {"mx8_tn_256x256_w4_persistent", nullptr, "mx8_tn_128x128_w4", nullptr};
   if (nn) {
     switch (dt) {
       case DT_F16: return tn_make<OpF16, true>(f16n, idx);
@@ -328,7 +334,8 @@ int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
   if (((uintptr_t)C) % (uintptr_t)out_elem(dt) != 0) return DGEMM_ERR_MISALIGNED;
   if (sc && ((((uintptr_t)sc->sa) & 3) != 0 || (((uintptr_t)sc->sb) & 3) != 0)) return DGEMM_ERR_MISALIGNED;
   if (mx && K > 0 &&
-      ((((uintptr_t)mx->sa) & 3) != 0 || (((uintptr_t)mx->sb) & 3) != 0 || (mx->ldsa & 3) != 0 || (mx->ldsb & 3) != 0))
+      ((((uintptr_t)mx->sa) & 15) != 0 || (((uintptr_t)mx->sb) & 15) != 0 || (mx->ldsa & 15) != 0 ||
+       (mx->ldsb & 15) != 0))
     return DGEMM_ERR_MISALIGNED;
 
   const bool skinny = use_skinny(dt, layout, M);

@@ -39,13 +39,15 @@ struct TnCfg {
   static constexpr int BK = ROWB / E;             // k per stage
   static constexpr int CPE = 16 / E;              // elements per 16-byte chunk
   static constexpr int P_LDS = BP * ROWB;
-  // MX: after the tiles, each stage holds the stage's four scale bytes of
-  // every P row, then of every Q row (one dword per row).
-  static constexpr int SC_LDS = (BP + BQ) * ROWB;
+  static constexpr int STAGE = (BP + BQ) * ROWB;  // 64 KiB
+  // MX: after the NS stages, a ring of two scale groups; a group holds four
+  // stages' block scales (16 bytes, 16 blocks of 32 k) of every P row, then
+  // of every Q row.
   static constexpr int SC_ROWS = Op::MX ? BP + BQ : 0;
-  static constexpr int SC_INST = SC_ROWS / 64;                  // 64-row copies per stage
-  static constexpr int SC_MIN = SC_INST / 4;                    // the fewest any wave issues
-  static constexpr int STAGE = (BP + BQ) * ROWB + 4 * SC_ROWS;  // 64 KiB (+2 KiB with MX)
+  static constexpr int SG_STAGES = 4;             // stages per scale group
+  static constexpr int SG_BYTES = 16 * SC_ROWS;
+  static constexpr int SC_INST = SC_ROWS / 64;    // 64-row copies per group
+  static constexpr int LDS = NS * STAGE + 2 * SG_BYTES;
   static constexpr int QSEG = BQ / 8 / NW, PSEG = BP / 8 / NW;
   static constexpr int NDMA = QSEG + PSEG;        // copy instructions per wave per stage
   static constexpr int WTP = BP / WP, WTQ = BQ / WQ;
@@ -70,11 +72,12 @@ struct TnCfg {
   static constexpr int NB = NDMA - NA;
   static constexpr int KB = KSTEPS > 2 ? 2 : KSTEPS - 1;
   static_assert(NB == 0 || KB >= 1, "part-B copies need k-steps before the barrier");
-  static_assert(NS * STAGE <= kLdsLimit, "LDS budget");
+  static_assert(LDS <= kLdsLimit, "LDS budget");
+  // The scale ring relies on every mid-stage wait draining all copies.
+  static_assert(!Op::MX || NS == 2, "MX scale groups need two stages");
   // Copies in flight when a stage's data must have landed: those of the
-  // NS - 2 later stream positions (each wave issues at least SC_MIN scale
-  // copies per position).
-  static constexpr int VM_MID = (NS - 2) * (NDMA + SC_MIN);
+  // NS - 2 later stream positions.
+  static constexpr int VM_MID = (NS - 2) * NDMA;
   static_assert(!PKM || PROWB / UB >= KEYM, "swizzle keys stay within a row of P");
   // The LDS-staged epilogue needs 256-byte staged rows; smaller wave tiles
   // store straight from the accumulators.
@@ -91,7 +94,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   constexpr int TP = Cfg::TP, TQ = Cfg::TQ, QSEG = Cfg::QSEG, NDMA = Cfg::NDMA;
   constexpr int NREAD = Cfg::NREAD, NMFMA = Cfg::NMFMA, NA = Cfg::NA, NB = Cfg::NB, KB = Cfg::KB;
 
-  __shared__ __attribute__((aligned(1024))) char smem[NS * Cfg::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[Cfg::LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -280,12 +283,23 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   // MX block scales: for the stage in use, lane l holds in scp[i] / scq[j]
   // the scales of its row of P tile i / Q tile j for k blocks h and h + 2
   // of the stage in bytes 0 and 2 (a stage is four blocks of 32 k: byte 2kk
-  // serves k-step kk).  A stream position's scale dwords travel with its
-  // copies into its LDS stage (4-byte copies, 64 rows each, spread over the
-  // waves), are read into nsp / nsq in the second half of the stage before
-  // (with its first fragments), and taken at the start of their stage.
+  // serves k-step kk).  Scale group G of a tile (stages 4G .. 4G+3) travels
+  // as one 16-byte copy per row (64 rows per instruction, spread over the
+  // waves) into ring buffer gam % 2, gam counting groups along the stream of
+  // stages.  The last stage of a group picks (without branching) the group
+  // two ahead; the next stage copies it first thing, into the buffer of the
+  // group just finished, which every wave is done with since that stage's
+  // barrier; its own barrier drains the copy before any stage reads it.  (A
+  // branch among the MFMAs would let the compiler sink them past it.)  A
+  // stage's dword is read in the second half of the stage before, and taken
+  // at its start.
+  char* const sring = smem + NS * Cfg::STAGE;
   [[maybe_unused]] uint32_t scp[TP], scq[TQ], nsp[TP], nsq[TQ];
-  auto copy_scales = [&](const Src& src, int t, char* stage_lds) {
+  [[maybe_unused]] int gam = 0;
+  [[maybe_unused]] bool gpend = false;   // a group copy for the next stage to issue
+  [[maybe_unused]] int gpend_g = 0, gpend_buf = 0;
+  [[maybe_unused]] Src gpend_src{};
+  auto copy_group = [&](const Src& src, int G, int buf) {
     if constexpr (Op::MX) {
 #pragma unroll
       for (int u0 = 0; u0 < Cfg::SC_INST; u0 += NW) {
@@ -293,25 +307,24 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
         if (u0 + NW > Cfg::SC_INST && u >= Cfg::SC_INST) break;
         const bool isp = 64 * u < Cfg::BP;
         const int row = isp ? 64 * u + lane : 64 * u - Cfg::BP + lane;
-        const uint32_t voff = (uint32_t)(row * (isp ? a.ldsp : a.ldsq) + 4 * t);
-        char* dst = stage_lds + Cfg::SC_LDS + 256 * u;
+        const uint32_t voff = (uint32_t)(row * (isp ? a.ldsp : a.ldsq) + 16 * G);
+        char* dst = sring + buf * Cfg::SG_BYTES + 1024 * u;
         if constexpr (PKM) {
-          copy4_lds(isp ? make_desc(src.sp, src.spn) : make_desc(src.sq, src.sqn), voff, dst);
+          copy16_lds(isp ? make_desc(src.sp, src.spn) : make_desc(src.sq, src.sqn), voff, dst);
         } else {
           __builtin_amdgcn_raw_ptr_buffer_load_lds(isp ? make_rsrc(src.sp, src.spn) : make_rsrc(src.sq, src.sqn),
-                                                   (__attribute__((address_space(3))) void*)dst, 4, voff, 0, 0, 0);
+                                                   (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
         }
       }
     }
   };
-  auto read_scales = [&](const char* stage_lds) {
+  auto read_scales = [&](int buf, int slot) {
     if constexpr (Op::MX) {
+      const char* g0 = sring + buf * Cfg::SG_BYTES + 4 * slot;
 #pragma unroll
-      for (int i = 0; i < TP; ++i)
-        nsp[i] = *(const uint32_t*)(stage_lds + Cfg::SC_LDS + 4 * (wp * Cfg::WTP + 32 * i + l32));
+      for (int i = 0; i < TP; ++i) nsp[i] = *(const uint32_t*)(g0 + 16 * (wp * Cfg::WTP + 32 * i + l32));
 #pragma unroll
-      for (int j = 0; j < TQ; ++j)
-        nsq[j] = *(const uint32_t*)(stage_lds + Cfg::SC_LDS + 4 * (Cfg::BP + wq * Cfg::WTQ + 32 * j + l32));
+      for (int j = 0; j < TQ; ++j) nsq[j] = *(const uint32_t*)(g0 + 16 * (Cfg::BP + wq * Cfg::WTQ + 32 * j + l32));
     }
   };
   // Blocks at or past K/32 read as scale byte 0 (their data are zeros; a
@@ -346,7 +359,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   // of them) and g + 1 (before it; NB of them, two stages only), which may
   // already be stages of the next tile `nx` (persistent launches have
   // nst >= NS).
-  auto stage = [&](int g, int s, const Src& cu, const Src& nx) {
+  auto stage = [&](int g, int s, const Src& cu, const Src& nx, const Src& nx2) {
     const int b = g & (NS - 1);
     const char* sb = smem + b * Cfg::STAGE;
     char* ob = smem + ((g + 1) & (NS - 1)) * Cfg::STAGE;
@@ -356,7 +369,10 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     const Rsrc rq1 = rsrc_at(n1 ? nx.q : cu.q, n1 ? nx.qn : cu.qn, t1, false);
     const Rsrc rp1 = rsrc_at(n1 ? nx.p : cu.p, n1 ? nx.pn : cu.pn, t1, PKM);
     const uint32_t kill1 = kill_at(t1);
-    if constexpr (Op::MX) take_scales(s, nsp, nsq);
+    if constexpr (Op::MX) {
+      if (gpend) copy_group(gpend_src, gpend_g, gpend_buf);
+      take_scales(s, nsp, nsq);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk + 1 < Cfg::KSTEPS; ++kk) {
@@ -376,11 +392,14 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       }
     }
     // Stream position g + 1 has landed (later positions may still be in flight).
+    [[maybe_unused]] const int snext = s + 1 >= nst ? 0 : s + 1;
+    [[maybe_unused]] const bool opens = snext % Cfg::SG_STAGES == 0;
     if constexpr (NS == 2) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     else __builtin_amdgcn_s_waitcnt(kWaitVmcntBase | vmcnt_bits(Cfg::VM_MID));
     __syncthreads();
-    // MX: the next stage's scales, first of the reads from its buffer.
-    if constexpr (Op::MX) read_scales(ob);
+    // MX: the next stage's scales, first of the reads: it opens a group (its
+    // tile's stage 0 or a multiple of four) or continues this one.
+    if constexpr (Op::MX) read_scales((gam + (opens ? 1 : 0)) & 1, snext % Cfg::SG_STAGES);
     __builtin_amdgcn_sched_barrier(0);
     // stream position g + NS
     const bool n2 = s + NS >= nst;
@@ -389,7 +408,6 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     const Rsrc rp2 = rsrc_at(n2 ? nx.p : cu.p, n2 ? nx.pn : cu.pn, t2, PKM);
     const uint32_t kill2 = kill_at(t2);
     char* db = smem + b * Cfg::STAGE;
-    if constexpr (Op::MX) copy_scales(n2 ? nx : cu, t2, db);
 #pragma unroll
     for (int t = 0; t < NMFMA; ++t) {
       mfma_one(LAST, t, Cfg::KSTEPS - 1);
@@ -401,6 +419,21 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
         if (d * NMFMA / NA == t) copy_d(rq2, rp2, kill2, db, d);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (Op::MX) {
+      // When this stage ends group gam, its buffer takes group gam + 2, the
+      // group after the one the next stage opens: the next group of this
+      // tile, or the first or second of the next tile, or the first of the
+      // tile after it (tiles of one group).
+      const int Gn = snext / Cfg::SG_STAGES;
+      const bool in_tile = s + 1 < nst;
+      const bool cu_more = (Gn + 1) * Cfg::SG_STAGES < nst;
+      const bool nx_more = Cfg::SG_STAGES < nst;
+      gpend = opens;
+      gpend_buf = gam & 1;
+      gpend_g = in_tile ? (cu_more ? Gn + 1 : 0) : (nx_more ? 1 : 0);
+      gpend_src = in_tile ? (cu_more ? cu : nx) : (nx_more ? nx : nx2);
+      gam += opens ? 1 : 0;
+    }
   };
 
   // ---- tiles ----
@@ -409,6 +442,9 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   const int64_t step = PERSIST ? (int64_t)gridDim.x : ntiles;
   Src cur = tile_src(tile);
   Src nxt = tile_src(tile + step);
+  // MX with one scale group per tile copies groups two tiles ahead.
+  [[maybe_unused]] Src nx2{};
+  if constexpr (Op::MX) nx2 = tile_src(tile + 2 * step);
   {
     // Prologue: stream positions 0 and 1, both of this tile (persistent
     // launches have nst >= 2; with one workgroup per tile and nst < 2 the
@@ -420,13 +456,19 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       const uint32_t kill = kill_at(t);
 #pragma unroll
       for (int d = 0; d < (t == NS - 1 ? NA : NDMA); ++d) copy_d(rq, rp, kill, smem + t * Cfg::STAGE, d);
-      copy_scales(cur, t, smem + t * Cfg::STAGE);
+      if (t == 0) {
+        // MX: the first two scale groups of the stream, ahead of the copies
+        // the wait below leaves open.
+        copy_group(cur, 0, 0);
+        if (Cfg::SG_STAGES < nst) copy_group(cur, 1, 1);
+        else copy_group(nxt, 0, 1);
+      }
     }
     // Position 0 has landed once at most the copies of positions 1 .. NS-1
     // are open.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcntBase | vmcnt_bits(Cfg::VM_MID + NA + Cfg::SC_MIN));
+    __builtin_amdgcn_s_waitcnt(kWaitVmcntBase | vmcnt_bits(Cfg::VM_MID + NA));
     __syncthreads();
-    if constexpr (Op::MX) read_scales(smem);
+    if constexpr (Op::MX) read_scales(0, 0);
 #pragma unroll
     for (int r = 0; r < NREAD; ++r) read_one(smem, 0, 0, r);
   }
@@ -468,7 +510,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   int g = 0;
   for (;;) {
     zero_acc();
-    for (int s = 0; s < nst; ++s, ++g) stage(g, s, cur, nxt);
+    for (int s = 0; s < nst; ++s, ++g) stage(g, s, cur, nxt, nx2);
     if constexpr (!PERSIST) break;
     // Persistent: the stores drain while the next tile's stages (already
     // copied) run.
@@ -476,7 +518,12 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     tile += step;
     if (tile >= ntiles) break;
     cur = nxt;
-    nxt = tile_src(tile + step);
+    if constexpr (Op::MX) {
+      nxt = nx2;
+      nx2 = tile_src(tile + 2 * step);
+    } else {
+      nxt = tile_src(tile + step);
+    }
   }
   // Copies issued past the last tile read zeros; let them land before exit.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);

@@ -122,11 +122,11 @@ int gemm_fp8_scaled(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t l
  * accumulated in FP32.  K must be a multiple of 32 (else
  * DGEMM_ERR_INVALID_DIM, checked with the dimensions).
  * scale_a: DEVICE pointer to M*ldsa bytes; sa_ib is scale_a[i*ldsa + b],
- *          ldsa >= K/32 (the kernels read whole 4-byte groups of a row).
+ *          ldsa >= K/32 (the kernels read whole 16-byte groups of a row).
  * scale_b: DEVICE pointer to N*ldsb bytes; sb_jb is scale_b[j*ldsb + b],
  *          ldsb >= K/32 (one row of scales per column j of B, in either
  *          layout).  With K == 0 neither is read (and may be NULL).
- * Both must be 4-byte aligned with ldsa, ldsb multiples of 4
+ * Both must be 16-byte aligned with ldsa, ldsb multiples of 16
  * (else DGEMM_ERR_MISALIGNED); an ld below K/32 -> DGEMM_ERR_INVALID_LD;
  * 256*ldsa or 256*ldsb at or above 2^31 -> DGEMM_ERR_UNSUPPORTED.  The scale
  * byte 255 (NaN in the format) is not supported: its result is unspecified.

@@ -370,18 +370,20 @@ def compare_mx(p, cij, SA, ldsa, SB, ldsb, rows=None, exact=False):
 
 # Every tile the MXFP8 path picks: one or two stages (K < 256, one tile per
 # workgroup), a partial last stage whose scale dword reaches past K/32, the
-# persistent 256 x 256 kernel with 400 tiles, K = 0, padded scale rows full
-# of NaN codes.  Scales 2^-15 .. 2^15.
+# persistent 256 x 256 kernel with 400 tiles (and with tiles of one scale
+# group, K = 384, whose next-but-one tile's group is copied at tile ends),
+# K = 0, padded scale rows full of NaN codes, launches split along q and p.
+# Scales 2^-15 .. 2^15.
 @pytest.mark.parametrize("layout", ["tn", "nn"])
 def test_mxfp8_against_oracle(layout):
     rng = np.random.default_rng(7000 + (layout == "nn"))
     shapes = [(1, 1, 32), (33, 65, 96), (257, 129, 224), (300, 521, 384), (512, 512, 256), (1000, 1100, 1184),
               (5120, 5120, 384), (70, 90, 0), (4352, 4352, 384), (14336, 4096, 384) if layout == "tn" else
-              (4096, 14336, 384)]
+              (4096, 14336, 384), (5120, 5120, 1184)]
     for idx, (M, N, K) in enumerate(shapes):
         p = make_problem("fp8", layout, M, N, K, seed=7100 + idx, pad=idx % 2)
         nb = K // 32
-        ld = ((nb + 3) // 4) * 4 + 4 * (idx % 2)
+        ld = ((nb + 15) // 16) * 16 + 16 * (idx % 2)
         SA, SB = mx_scales(rng, M, nb, ld), mx_scales(rng, N, nb, ld)
         say(f"case mx {kernel_name('mx8', layout, M, N, K)} M={M} N={N} K={K} ld={ld}")
         cij, pad = c_host(p, run_mx(p, SA, ld, SB, ld))
@@ -400,7 +402,7 @@ def test_mxfp8_bit_exact(layout):
     for idx, (M, N, K) in enumerate([(260, 300, 2048), (4096, 4096, 512), (77, 50, 160)]):
         p = make_problem("fp8", layout, M, N, K, seed=7300 + idx, dist="pm1")
         nb = K // 32
-        ld = ((nb + 3) // 4) * 4
+        ld = ((nb + 15) // 16) * 16
         SA, SB = mx_scales(rng, M, nb, ld, 124, 131), mx_scales(rng, N, nb, ld, 124, 131)
         say(f"case mx pm1 {layout} M={M} N={N} K={K}")
         cij, _ = c_host(p, run_mx(p, SA, ld, SB, ld))
