@@ -78,7 +78,7 @@ struct TnCfg {
   // Copies in flight when a stage's data must have landed: those of the
   // NS - 2 later stream positions.
   static constexpr int VM_MID = (NS - 2) * NDMA;
-  static_assert(!PKM || PROWB / UB >= KEYM, "swizzle keys stay within a row of P");
+  static_assert(!PKM || (PROWB / UB) % KEYM == 0, "swizzle keys stay within a row of P");
   // The LDS-staged epilogue needs 256-byte staged rows; smaller wave tiles
   // store straight from the accumulators.
   static constexpr bool STAGED_EPI = (TP / (Op::OE == 4 ? 2 : 1)) * 32 * Op::OE == 256;
