@@ -63,13 +63,21 @@ Launch mfma_launch(const char* name) {
 
 // Four-wave kernel (gemm_tn.hpp).  256 x 256 FP8, whose FP32 output is twice
 // as large, runs persistently so that each tile's stores drain under the next
-// tile's stages; every other shape runs one tile per workgroup.
+// tile's stages; every other shape runs one tile per workgroup.  `kt`: K is
+// not a whole number of stages, so the copies need tail masks (a separate
+// instantiation: without a tail they cost nothing).
 template <class Op, bool PKM, int BP, int BQ, int NS = 2>
-Launch tn_launch(const char* name) {
+Launch tn_launch(const char* name, bool kt) {
   using Cfg = TnCfg<Op, PKM, BP, BQ, NS>;
   constexpr bool P = Op::ELEM == 1 && BP == 256 && BQ == 256;
-  return Launch{(const void*)&gemm_tn_kernel<Op, P, PKM, BP, BQ, NS>, name, BP, BQ, Cfg::NT, Cfg::LDS, PKM, P};
+  const void* fn = kt ? (const void*)&gemm_tn_kernel<Op, P, PKM, BP, BQ, NS, true>
+                      : (const void*)&gemm_tn_kernel<Op, P, PKM, BP, BQ, NS, false>;
+  return Launch{fn, name, BP, BQ, Cfg::NT, Cfg::LDS, PKM, P};
 }
+
+// Whether K ends inside a stage of the four-wave kernel (stages of 128 bytes
+// of k).
+bool k_tail(int dt, int64_t K) { return K % (128 / in_elem(dt)) != 0; }
 
 // Block tiles of the four-wave kernel and their throughput relative to the
 // 256 x 256 tile when every CU is busy, measured on MI355X at 8192^3 class
@@ -127,17 +135,17 @@ unsigned tile_mask(int dt, bool nn) {
 
 // The four-wave launch of kTiles entry `idx` (one tile_mask allows).
 template <class Op, bool PKM>
-Launch tn_make(const char* const names[kNumTiles], int idx) {
+Launch tn_make(const char* const names[kNumTiles], int idx, bool kt) {
   if constexpr (PKM && Op::ELEM == 1) {
-    if (idx == 1) return tn_launch<Op, PKM, 256, 128>(names[1]);
-    return tn_launch<Op, PKM, 256, 256>(names[0]);
+    if (idx == 1) return tn_launch<Op, PKM, 256, 128>(names[1], kt);
+    return tn_launch<Op, PKM, 256, 256>(names[0], kt);
   } else {
     switch (idx) {
-      case 2: return tn_launch<Op, PKM, 128, 128>(names[2]);
+      case 2: return tn_launch<Op, PKM, 128, 128>(names[2], kt);
       case 3:
-        if constexpr (!Op::MX) return tn_launch<Op, PKM, 128, 128, 4>(names[3]);
+        if constexpr (!Op::MX) return tn_launch<Op, PKM, 128, 128, 4>(names[3], kt);
         [[fallthrough]];
-      default: return tn_launch<Op, PKM, 256, 256>(names[0]);
+      default: return tn_launch<Op, PKM, 256, 256>(names[0], kt);
     }
   }
 }
@@ -166,7 +174,7 @@ Launch select_skinny(int dt, int64_t M) {
   return M <= 16 ? skinny_launch<OpBF16, 1>("bf16_tn_skinny16") : skinny_launch<OpBF16, 2>("bf16_tn_skinny32");
 }
 
-Launch four_wave(int dt, bool nn, int idx) {
+Launch four_wave(int dt, bool nn, int idx, bool kt) {
   static const char* const f16n[kNumTiles] = {"f16_nn_256x256_w4", nullptr, "f16_nn_128x128_w4",
                                              "f16_nn_128x128_w4_s4"};
   static const char* const bf16n[kNumTiles] = {"bf16_nn_256x256_w4", nullptr, "bf16_nn_128x128_w4",
@@ -187,19 +195,19 @@ Launch four_wave(int dt, bool nn, int idx) {
   static const char* const mxt[kNumTiles] = {"mx8_tn_256x256_w4_persistent", nullptr, "mx8_tn_128x128_w4", nullptr};
   if (nn) {
     switch (dt) {
-      case DT_F16: return tn_make<OpF16, true>(f16n, idx);
-      case DT_BF16: return tn_make<OpBF16, true>(bf16n, idx);
-      case DT_FP8S: return tn_make<OpFP8S, true>(fp8sn, idx);
-      case DT_MX8: return tn_make<OpMX8, true>(mxn, idx);
-      default: return tn_make<OpFP8, true>(fp8n, idx);
+      case DT_F16: return tn_make<OpF16, true>(f16n, idx, kt);
+      case DT_BF16: return tn_make<OpBF16, true>(bf16n, idx, kt);
+      case DT_FP8S: return tn_make<OpFP8S, true>(fp8sn, idx, kt);
+      case DT_MX8: return tn_make<OpMX8, true>(mxn, idx, kt);
+      default: return tn_make<OpFP8, true>(fp8n, idx, kt);
     }
   }
   switch (dt) {
-    case DT_F16: return tn_make<OpF16, false>(f16t, idx);
-    case DT_BF16: return tn_make<OpBF16, false>(bf16t, idx);
-    case DT_FP8S: return tn_make<OpFP8S, false>(fp8st, idx);
-    case DT_MX8: return tn_make<OpMX8, false>(mxt, idx);
-    default: return tn_make<OpFP8, false>(fp8t, idx);
+    case DT_F16: return tn_make<OpF16, false>(f16t, idx, kt);
+    case DT_BF16: return tn_make<OpBF16, false>(bf16t, idx, kt);
+    case DT_FP8S: return tn_make<OpFP8S, false>(fp8st, idx, kt);
+    case DT_MX8: return tn_make<OpMX8, false>(mxt, idx, kt);
+    default: return tn_make<OpFP8, false>(fp8t, idx, kt);
   }
 }
 
@@ -232,8 +240,8 @@ Choice choose(int dt, int layout, int64_t M, int64_t N, int64_t K) {
       return c;
     }
     if (K < 256) {
-      c.L = nn ? tn_launch<OpMX8, true, 256, 128>("mx8_nn_256x128_w4")
-               : tn_launch<OpMX8, false, 128, 128>("mx8_tn_128x128_w4");
+      c.L = nn ? tn_launch<OpMX8, true, 256, 128>("mx8_nn_256x128_w4", k_tail(dt, K))
+               : tn_launch<OpMX8, false, 128, 128>("mx8_tn_128x128_w4", k_tail(dt, K));
       return c;
     }
   }
@@ -245,7 +253,7 @@ Choice choose(int dt, int layout, int64_t M, int64_t N, int64_t K) {
     const unsigned mask = tile_mask(dt, nn);
     double whole = 0.0;
     const int idx = pick_tile(Pn, Qn, mask, &whole);
-    c.L = four_wave(dt, nn, idx);
+    c.L = four_wave(dt, nn, idx, k_tail(dt, K));
     const int64_t slots = kPlanCus;
     const int64_t tp = (Pn + 255) / 256, tq = (Qn + 255) / 256, tiles = tp * tq;
     double best = 0.95 * whole;
@@ -261,11 +269,11 @@ Choice choose(int dt, int layout, int64_t M, int64_t N, int64_t K) {
       const double cost = (double)((across * n1 + slots - 1) / slots) * 65536.0 + tail;
       if (cost < best) {
         best = cost;
-        c.L = four_wave(dt, nn, 0);
+        c.L = four_wave(dt, nn, 0, k_tail(dt, K));
         c.split = true;
         c.split_p = axis == 1;
         c.at = 256 * n1;
-        c.T = four_wave(dt, nn, tidx);
+        c.T = four_wave(dt, nn, tidx, k_tail(dt, K));
       }
     }
     return c;

@@ -87,7 +87,7 @@ struct TnCfg {
   static constexpr int WPE = TP * TQ <= 4 && NS == 2 ? 2 : 1;
 };
 
-template <class Op, bool PERSIST, bool PKM, int BP, int BQ, int NS>
+template <class Op, bool PERSIST, bool PKM, int BP, int BQ, int NS, bool KT>
 __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   using Cfg = TnCfg<Op, PKM, BP, BQ, NS>;
   constexpr int NW = Cfg::NW, E = Cfg::E, FC = Cfg::FC, ROWB = Cfg::ROWB, BK = Cfg::BK, CPE = Cfg::CPE;
@@ -184,26 +184,45 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     }
     return r;
   };
-  // Descriptor advanced to stage t: K-contiguous operands move along the
-  // row, p-contiguous P moves down BK rows.
   // With p-contiguous P the copies go through inline assembly (see
   // copy16_lds), which takes the descriptor as four dwords.
   using Rsrc = std::conditional_t<PKM, i32x4, __amdgpu_buffer_rsrc_t>;
-  auto rsrc_at = [&](const char* blk, uint32_t nrec, int t, bool pkm_p) -> Rsrc {
-    const uint32_t adv = pkm_p ? (uint32_t)((int64_t)t * BK * a.ldp) : (uint32_t)t * ROWB;
-    // (readfirstlane keeps the clamped count in a scalar register: a vector
-    // select here would force a per-lane loop around every copy.)
-    const uint32_t left = (uint32_t)__builtin_amdgcn_readfirstlane((int)(adv < nrec ? nrec - adv : 0u));
-    if constexpr (PKM) return make_desc(blk + adv, left);
-    else return make_rsrc(blk + adv, left);
+  auto rsrc = [](const char* base, uint32_t nrec) -> Rsrc {
+    if constexpr (PKM) return make_desc(base, nrec);
+    else return make_rsrc(base, nrec);
   };
   // Chunks at or past K read zero: bit 31 puts the offset past num_records.
-  auto kill_at = [&](int t) {
-    const int64_t rem64 = K - (int64_t)t * BK;
-    const int rem = (int)(rem64 < BK ? rem64 : BK);
-    return dk0 >= rem ? kOobOffset : 0u;
+  // Only a stage that ends inside K has such chunks (KT).
+  auto kill_at = [&](int t) -> uint32_t {
+    if constexpr (!KT) {
+      (void)t;
+      return 0u;
+    } else {
+      const int64_t rem64 = K - (int64_t)t * BK;
+      const int rem = (int)(rem64 < BK ? rem64 : BK);
+      return dk0 >= rem ? kOobOffset : 0u;
+    }
   };
-  auto copy_d = [&](Rsrc rq, Rsrc rp, uint32_t kill, char* stage_lds, int d) {
+  // Copy source of stream position t of a tile: descriptors advanced to
+  // stage t (K-contiguous operands move along the row, p-contiguous P down
+  // BK rows) and the tail mask.  An invalid position (a stage past the
+  // tile's end, or of no tile) gets empty descriptors and reads zeros.  A
+  // valid one keeps records left, as every stage of a tile starts inside
+  // the descriptor's range; the count is a plain scalar select (a
+  // saturating subtract would go through vector registers).
+  struct Pos {
+    Rsrc q, p;
+    uint32_t kill;
+  };
+  auto pos_at = [&](const Src& src, int t, bool valid) -> Pos {
+    const uint32_t aq = (uint32_t)t * ROWB;
+    const uint32_t ap = PKM ? (uint32_t)((int64_t)t * BK * a.ldp) : aq;
+    return Pos{rsrc(src.q + aq, valid ? src.qn - aq : 0u), rsrc(src.p + ap, valid ? src.pn - ap : 0u), kill_at(t)};
+  };
+  auto copy_d = [&](const Pos& ps, char* stage_lds, int d) {
+    const Rsrc& rq = ps.q;
+    const Rsrc& rp = ps.p;
+    const uint32_t kill = ps.kill;
     if constexpr (PKM) {
       if (d < QSEG) copy16_lds(rq, qvo[d] | kill, stage_lds + Cfg::P_LDS + (d * NW + wave_u) * 1024);
       else copy16_lds(rp, pvo[d - QSEG], stage_lds + ((d - QSEG) * NW + wave_u) * 1024);
@@ -358,17 +377,13 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   // issued here belong to the stream position g + NS (after the barrier; NA
   // of them) and g + 1 (before it; NB of them, two stages only), which may
   // already be stages of the next tile `nx` (persistent launches have
-  // nst >= NS).
-  auto stage = [&](int g, int s, const Src& cu, const Src& nx, const Src& nx2) {
+  // nst >= NS; with one tile per workgroup, positions past the tile read
+  // zeros).  `p1` holds position g + 1 on entry and g + NS on return: with
+  // two stages that is the next stage's g + 1.
+  auto stage = [&](int g, int s, const Src& cu, const Src& nx, const Src& nx2, Pos& p1) {
     const int b = g & (NS - 1);
     const char* sb = smem + b * Cfg::STAGE;
     char* ob = smem + ((g + 1) & (NS - 1)) * Cfg::STAGE;
-    // stream position g + 1
-    const bool n1 = s + 1 >= nst;
-    const int t1 = n1 ? s + 1 - nst : s + 1;
-    const Rsrc rq1 = rsrc_at(n1 ? nx.q : cu.q, n1 ? nx.qn : cu.qn, t1, false);
-    const Rsrc rp1 = rsrc_at(n1 ? nx.p : cu.p, n1 ? nx.pn : cu.pn, t1, PKM);
-    const uint32_t kill1 = kill_at(t1);
     if constexpr (Op::MX) {
       if (gpend) copy_group(gpend_src, gpend_g, gpend_buf);
       take_scales(s, nsp, nsq);
@@ -386,7 +401,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
         if constexpr (NB > 0) {
 #pragma unroll
           for (int j = 0; j < NB; ++j)
-            if (j * (KB * NMFMA) / NB == kk * NMFMA + t) copy_d(rq1, rp1, kill1, ob, NA + j);
+            if (j * (KB * NMFMA) / NB == kk * NMFMA + t) copy_d(p1, ob, NA + j);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -402,11 +417,15 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     if constexpr (Op::MX) read_scales((gam + (opens ? 1 : 0)) & 1, snext % Cfg::SG_STAGES);
     __builtin_amdgcn_sched_barrier(0);
     // stream position g + NS
-    const bool n2 = s + NS >= nst;
-    const int t2 = n2 ? s + NS - nst : s + NS;
-    const Rsrc rq2 = rsrc_at(n2 ? nx.q : cu.q, n2 ? nx.qn : cu.qn, t2, false);
-    const Rsrc rp2 = rsrc_at(n2 ? nx.p : cu.p, n2 ? nx.pn : cu.pn, t2, PKM);
-    const uint32_t kill2 = kill_at(t2);
+    Pos p2;
+    if constexpr (PERSIST) {
+      const bool n2 = s + NS >= nst;
+      const Src& src = n2 ? nx : cu;
+      p2 = pos_at(src, n2 ? s + NS - nst : s + NS, src.qn != 0);
+    } else {
+      (void)nx;
+      p2 = pos_at(cu, s + NS, s + NS < nst);
+    }
     char* db = smem + b * Cfg::STAGE;
 #pragma unroll
     for (int t = 0; t < NMFMA; ++t) {
@@ -416,7 +435,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
         if (read_slot(r, NMFMA) == t) read_one(ob, 0, 0, r);
 #pragma unroll
       for (int d = 0; d < NA; ++d)
-        if (d * NMFMA / NA == t) copy_d(rq2, rp2, kill2, db, d);
+        if (d * NMFMA / NA == t) copy_d(p2, db, d);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (Op::MX) {
@@ -434,6 +453,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       gpend_src = in_tile ? (cu_more ? cu : nx) : (nx_more ? nx : nx2);
       gam += opens ? 1 : 0;
     }
+    p1 = p2;
   };
 
   // ---- tiles ----
@@ -445,17 +465,18 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   // MX with one scale group per tile copies groups two tiles ahead.
   [[maybe_unused]] Src nx2{};
   if constexpr (Op::MX) nx2 = tile_src(tile + 2 * step);
+  Pos p1;   // the stream position after the current stage's
   {
-    // Prologue: stream positions 0 and 1, both of this tile (persistent
-    // launches have nst >= 2; with one workgroup per tile and nst < 2 the
-    // second position reads zeros that nothing uses), without the part-B
+    // Prologue: stream positions 0 .. NS-1, all of this tile (persistent
+    // launches have nst >= NS; with one workgroup per tile and nst < NS the
+    // later positions read zeros that nothing uses), without the part-B
     // copies of position 1, which stage 0 issues.
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
-      const Rsrc rq = rsrc_at(cur.q, cur.qn, t, false), rp = rsrc_at(cur.p, cur.pn, t, PKM);
-      const uint32_t kill = kill_at(t);
+      const Pos ps = pos_at(cur, t, t < nst);
+      if (t == 1) p1 = ps;
 #pragma unroll
-      for (int d = 0; d < (t == NS - 1 ? NA : NDMA); ++d) copy_d(rq, rp, kill, smem + t * Cfg::STAGE, d);
+      for (int d = 0; d < (t == NS - 1 ? NA : NDMA); ++d) copy_d(ps, smem + t * Cfg::STAGE, d);
       if (t == 0) {
         // MX: the first two scale groups of the stream, ahead of the copies
         // the wait below leaves open.
@@ -510,7 +531,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   int g = 0;
   for (;;) {
     zero_acc();
-    for (int s = 0; s < nst; ++s, ++g) stage(g, s, cur, nxt, nx2);
+    for (int s = 0; s < nst; ++s, ++g) stage(g, s, cur, nxt, nx2, p1);
     if constexpr (!PERSIST) break;
     // Persistent: the stores drain while the next tile's stages (already
     // copied) run.
@@ -543,11 +564,13 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   }
 }
 
-template <class Op, bool PERSIST, bool PKM, int BP, int BQ, int NS>
+// KT: some stage ends inside K (K not a multiple of the stage depth), so
+// the copies carry per-lane tail masks.
+template <class Op, bool PERSIST, bool PKM, int BP, int BQ, int NS, bool KT>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(TnCfg<Op, PKM, BP, BQ, NS>::WPE, TnCfg<Op, PKM, BP, BQ, NS>::WPE)))
 gemm_tn_kernel(const GemmArgs a) {
-  gemm_tn_body<Op, PERSIST, PKM, BP, BQ, NS>(a);
+  gemm_tn_body<Op, PERSIST, PKM, BP, BQ, NS, KT>(a);
 }
 
 }  // namespace dg

@@ -81,7 +81,8 @@ def kernel_name(dtype, layout, M, N, K):
 # tiles (N not a multiple of 8 in NN, so B's rows are padded and the last p
 # tile reads past the row end), a partial last stage, and 400 tiles of
 # 256 x 256, more than the CUs, so the persistent FP8 variant walks several
-# tiles per workgroup with its copy stream crossing tiles (rows sampled).
+# tiles per workgroup with its copy stream crossing tiles (rows sampled),
+# also with a partial last stage (the kernels built with tail masks).
 @pytest.mark.parametrize("dtype,layout", [(d, l) for d in ("f16", "bf16", "fp8") for l in ("tn", "nn")])
 def test_four_wave_kernel(dtype, layout):
     bk = {"f16": 64, "bf16": 64, "fp8": 128}[dtype]
@@ -93,13 +94,13 @@ def test_four_wave_kernel(dtype, layout):
     psplit = (14336, 4096) if layout == "tn" else (4096, 14336)
     shapes = [(512, 512, 2 * bk, small), (300, 521, 3 * bk, small), (5120, 5120, 3 * bk, "256x256_w4"),
               (1000, 1100, 9 * bk + 16, small), (2048, 1800, 2 * bk + 16, small), (2560, 2304, 3 * bk, mid),
-              (129, 77, 5 * bk + 16, small), (4352, 4352, 3 * bk, "256x256_w4"),
-              (psplit[0], psplit[1], 3 * bk, "256x256_w4")]
+              (129, 77, 5 * bk + 16, small), (5120, 5120, 3 * bk + 16, "256x256_w4"),
+              (4352, 4352, 3 * bk, "256x256_w4"), (psplit[0], psplit[1], 3 * bk + 16, "256x256_w4")]
     for idx, (M, N, K, tile) in enumerate(shapes):
         name = kernel_name(dtype, layout, M, N, K)
         k = name.split()[0]
         assert k.endswith(tile) or k.endswith(tile + "_persistent"), name
-        assert (" + " in name) == (idx >= 7), name
+        assert (" + " in name) == (idx >= 8), name
         p = make_problem(dtype, layout, M, N, K, seed=5000 + idx, pad=idx % 2)
         say(f"case w4 {name} M={M} N={N} K={K}")
         cij, pad = c_host(p, run_gpu(p))
@@ -280,8 +281,8 @@ def compare_scaled(p, cij, sa, sb, rows=None, exact=False):
 def test_fp8_scaled_against_oracle(layout, mode):
     rng = np.random.default_rng(6000 + (layout == "nn") + 2 * (mode == "row"))
     shapes = [(1, 1, 1), (257, 129, 77), (33, 65, 300), (300, 521, 384), (512, 512, 256), (1000, 1100, 1168),
-              (5120, 5120, 384), (70, 90, 0), (4352, 4352, 384), (14336, 4096, 384) if layout == "tn" else
-              (4096, 14336, 384)]
+              (5120, 5120, 384), (5120, 5120, 400), (70, 90, 0), (4352, 4352, 384), (14336, 4096, 384)
+              if layout == "tn" else (4096, 14336, 384)]
     for idx, (M, N, K) in enumerate(shapes):
         p = make_problem("fp8", layout, M, N, K, seed=6100 + idx, pad=idx % 2)
         sa = _factors(rng, M if mode == "row" else 1)
