@@ -57,6 +57,13 @@ struct OpF16 {
   __device__ static f32x16 mma_parts(const u32x4 (&a)[1], const u32x4 (&b)[1], f32x16 c) {
     return mma(__builtin_bit_cast(Frag, a[0]), __builtin_bit_cast(Frag, b[0]), c);
   }
+  // The 16 x 16 x 32 MFMA (the four-wave kernel): lane l holds row l % 16
+  // of A and column l % 16 of B, each with 8 k (lanes 16g .. 16g + 15 the
+  // same k); D holds rows 4 (l / 16) .. 4 (l / 16) + 3 of column l % 16.
+  __device__ static f32x4 mma16(const u32x4 (&a)[1], const u32x4 (&b)[1], f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(Frag, a[0]), __builtin_bit_cast(Frag, b[0]), c, 0,
+                                                   0, 0);
+  }
 };
 
 struct OpBF16 {
@@ -74,6 +81,10 @@ struct OpBF16 {
   __device__ static uint16_t one(float x) { const __bf16 h = (__bf16)x; return __builtin_bit_cast(uint16_t, h); }
   __device__ static f32x16 mma_parts(const u32x4 (&a)[1], const u32x4 (&b)[1], f32x16 c) {
     return mma(__builtin_bit_cast(Frag, a[0]), __builtin_bit_cast(Frag, b[0]), c);
+  }
+  __device__ static f32x4 mma16(const u32x4 (&a)[1], const u32x4 (&b)[1], f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(Frag, a[0]), __builtin_bit_cast(Frag, b[0]), c,
+                                                    0, 0, 0);
   }
 };
 
@@ -215,28 +226,38 @@ struct EpiScale {
 
 // Epilogue D[p][q] -> C[q*ldc + p] for one wave's WTP x WTQ tile, staged
 // through LDS.  Each lane holds four consecutive p of one q per accumulator
-// group, so a direct store writes 8 or 16 bytes into each of 32 different
-// columns of C.  Instead the wave converts its tile into its own LDS region
-// `reg` (WTQ rows of 256 bytes, [q][p]) and reads it back as 16-byte chunks:
-// one store instruction then covers four columns with 256 contiguous bytes
-// each ("An Educational GEMM Ladder for Helios GPUs", the LDS-staged
-// epilogue).  Slots of four p are XOR-swizzled by the row so that both the
-// scattered writes and the row-wise reads are free of bank conflicts.  FP32
-// output needs twice the space and goes in two passes over p.  The caller
-// makes sure no other wave still uses `reg`.
-template <class Op, int WTP, int WTQ, int TP, int TQ>
-__device__ __forceinline__ void staged_epilogue(const GemmArgs& a, char* reg, const f32x16 (&acc)[TP][TQ], int lane,
+// group, so a direct store writes 8 or 16 bytes into each of 32 (16)
+// different columns of C.  Instead the wave converts its tile into its own
+// LDS region `reg` (WTQ rows of 256 bytes, [q][p]) and reads it back as
+// 16-byte chunks: one store instruction then covers four columns with 256
+// contiguous bytes each ("An Educational GEMM Ladder for Helios GPUs", the
+// LDS-staged epilogue).  Slots of four p are XOR-swizzled by the row so that
+// both the scattered writes and the row-wise reads are free of bank
+// conflicts.  FP32 output needs twice the space and goes in two passes over
+// p.  The caller makes sure no other wave still uses `reg`.
+//
+// MT is the MFMA tile: 32 x 32 accumulators (lane l: q = 32 j + l % 32,
+// p = 32 i + 8 g + 4 (l / 32) + 0..3 for register group g) or 16 x 16
+// (lane l: q = 16 j + l % 16, p = 16 i + 4 (l / 16) + 0..3).  With 16 x 16
+// one write instruction covers 16 rows and four slots of each; the key
+// 2 (row mod 16) (8-byte slots) or row mod 16 (16-byte slots) spreads them
+// over all banks and keeps 8-byte slot pairs aligned.
+template <class Op, int WTP, int WTQ, int TP, int TQ, int MT = 32, class AccT = f32x16>
+__device__ __forceinline__ void staged_epilogue(const GemmArgs& a, char* reg, const AccT (&acc)[TP][TQ], int lane,
                                                 int64_t pbase, int64_t qbase) {
   constexpr int OE = Op::OE;
   constexpr int PASSES = OE == 4 ? 2 : 1;
   constexpr int TPP = TP / PASSES;            // accumulator tiles along p per pass
-  constexpr int RB = TPP * 32 * OE;           // bytes of one staged row (one q)
+  constexpr int RB = TPP * MT * OE;           // bytes of one staged row (one q)
   constexpr int SS = 4 * OE;                  // bytes of one slot (four p)
   constexpr int NSL = RB / SS;                // slots per row
   constexpr int EPC = 16 / OE;                // elements per 16-byte chunk
+  constexpr int NG = MT * MT / 256;           // register groups of four per accumulator tile
   static_assert(RB == 256, "staged rows are 256 bytes");
   static_assert(WTQ % 4 == 0, "four rows per read-back instruction");
-  const int l32 = lane & 31, h = lane >> 5;
+  static_assert(MT == 32 || !Op::SCALED, "scale factors follow the 32 x 32 layout");
+  auto key = [](int row) { return MT == 32 ? row % NSL : (OE == 2 ? 2 * (row % 16) : row % 16); };
+  const int lr = lane % MT, lg = lane / MT;
   [[maybe_unused]] EpiScale<TQ> sc;
   if constexpr (Op::SCALED) sc.init(a, lane, qbase);
 #pragma unroll
@@ -244,16 +265,17 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& a, char* reg, co
 #pragma unroll
     for (int i = 0; i < TPP; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < NG; ++g) {
         [[maybe_unused]] f32x4 fp;
-        if constexpr (Op::SCALED) fp = EpiScale<TQ>::p4(a, pbase + 32 * (pass * TPP + i) + 8 * g + 4 * h);
+        if constexpr (Op::SCALED) fp = EpiScale<TQ>::p4(a, pbase + 32 * (pass * TPP + i) + 8 * g + 4 * lg);
 #pragma unroll
         for (int j = 0; j < TQ; ++j) {
-          const f32x16& v = acc[pass * TPP + i][j];
+          const AccT& v = acc[pass * TPP + i][j];
           float v0 = v[4 * g], v1 = v[4 * g + 1], v2 = v[4 * g + 2], v3 = v[4 * g + 3];
           if constexpr (Op::SCALED) sc.apply(fp, j, v0, v1, v2, v3);
-          const int row = 32 * j + l32;
-          const int slot = (8 * i + 2 * g + h) ^ (row % NSL);
+          const int row = MT * j + lr;
+          // slot of p = MT i + 8 g + 4 lg (32 x 32) or MT i + 4 lg (16 x 16)
+          const int slot = ((MT / 4) * i + 2 * g + lg) ^ key(row);
           char* dst = reg + row * RB + slot * SS;
           if constexpr (OE == 4) {
             *(f32x4*)dst = f32x4{v0, v1, v2, v3};
@@ -267,18 +289,18 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& a, char* reg, co
 #pragma unroll
     for (int it = 0; it < WTQ / 4; ++it) {
       const int row = 4 * it + (lane >> 4);
+      const int kr = key(row);
       u32x4 d;
       if constexpr (OE == 4) {
-        d = *(const u32x4*)(reg + row * RB + ((m ^ (row % NSL)) * 16));
+        d = *(const u32x4*)(reg + row * RB + ((m ^ kr) * 16));
       } else {
         // Chunk m holds slots 2m and 2m+1, which the swizzle keeps in one
         // aligned pair but swaps when the key is odd.
-        const int key = row % NSL;
-        const u32x4 raw = *(const u32x4*)(reg + row * RB + ((((2 * m) ^ key) & ~1) * SS));
-        d = (key & 1) ? u32x4{raw[2], raw[3], raw[0], raw[1]} : raw;
+        const u32x4 raw = *(const u32x4*)(reg + row * RB + ((((2 * m) ^ kr) & ~1) * SS));
+        d = (kr & 1) ? u32x4{raw[2], raw[3], raw[0], raw[1]} : raw;
       }
       const int64_t q = qbase + row;
-      const int64_t p = pbase + pass * TPP * 32 + m * EPC;
+      const int64_t p = pbase + pass * TPP * MT + m * EPC;
       if (q >= a.Qn) continue;
       char* c = (char*)a.C + (q * a.ldc + p) * OE;
       if (a.vec16 && p + EPC <= a.Pn) {

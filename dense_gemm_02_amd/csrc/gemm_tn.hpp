@@ -51,27 +51,38 @@ struct TnCfg {
   static constexpr int QSEG = BQ / 8 / NW, PSEG = BP / 8 / NW;
   static constexpr int NDMA = QSEG + PSEG;        // copy instructions per wave per stage
   static constexpr int WTP = BP / WP, WTQ = BQ / WQ;
-  static constexpr int TP = WTP / 32, TQ = WTQ / 32;
-  static constexpr int KSTEPS = BK / Op::KI;
+  // MFMA tile: 16 x 16 x 32 for FP16/BF16, which sustains about 12% more
+  // throughput than 32 x 32 x 16 on the same wave tile once the chip runs
+  // at its power limit (random operands; equal at zero data), and
+  // 32 x 32 x 64 for FP8.
+  static constexpr int MT = E == 2 ? 16 : 32;
+  static constexpr int KI = E == 2 ? 32 : Op::KI;  // k per MFMA
+  static constexpr int ACC = MT * MT / 64;         // accumulator registers per tile
+  using Acc = std::conditional_t<MT == 16, f32x4, f32x16>;
+  static constexpr int TP = WTP / MT, TQ = WTQ / MT;
+  static constexpr int KSTEPS = BK / KI;
+  static constexpr int CPK = KI * E / 16;          // 16-byte chunks of k per k-step
   // LDS reads per k-step: 16-byte reads of Q fragments, and of P fragments
   // either 16-byte reads (K-contiguous P) or twice as many 8-byte
   // transposing reads (p-contiguous P).
   static constexpr int PRD = PKM ? 2 * FC : FC;   // reads per P fragment
   static constexpr int NREAD = TQ * FC + TP * PRD;
-  // p-contiguous P: LDS rows of k, BP*E bytes, in units of one 32-row MFMA
-  // tile (UB bytes) XOR-swizzled by k mod KEYM.
+  // p-contiguous P: LDS rows of k, BP*E bytes, in units of 32 p (UB bytes)
+  // XOR-swizzled by a key of k below KEYM: k mod 8 (FP8), or for 16-bit
+  // (k mod 4) ^ 2 ((k / 8) mod 2), so that the 16 x 16 fragment's lane groups
+  // 0 and 1, which read k rows eight apart, meet different banks.
   static constexpr int PROWB = BP * E;            // bytes of one LDS row of P (one k)
   static constexpr int UB = 32 * E;
   static constexpr int KEYM = 256 / UB;
   static constexpr int RPSG = 1024 / PROWB;       // rows of P per 1 KiB copy segment
   static constexpr int NMFMA = TP * TQ;           // MFMAs per k-step
   // Copy split: FP16/BF16 issue half of a stage's copies after the barrier
-  // two stages ahead and the rest over the first two k-steps of the stage
-  // before; FP8 (two k-steps per stage) issues them all after the barrier.
+  // two stages ahead and the rest over the first NBSPAN MFMA slots of the
+  // stage before; FP8 issues them all after the barrier.
   static constexpr int NA = (Op::ELEM == 2 && NS == 2) ? NDMA / 2 : NDMA;
   static constexpr int NB = NDMA - NA;
-  static constexpr int KB = KSTEPS > 2 ? 2 : KSTEPS - 1;
-  static_assert(NB == 0 || KB >= 1, "part-B copies need k-steps before the barrier");
+  static constexpr int NBSPAN = NMFMA / 2;
+  static_assert(NB == 0 || NBSPAN <= (KSTEPS - 1) * NMFMA, "part-B copies go out before the barrier");
   static_assert(LDS <= kLdsLimit, "LDS budget");
   // The scale ring relies on every mid-stage wait draining all copies.
   static_assert(!Op::MX || NS == 2, "MX scale groups need two stages");
@@ -79,12 +90,13 @@ struct TnCfg {
   // NS - 2 later stream positions.
   static constexpr int VM_MID = (NS - 2) * NDMA;
   static_assert(!PKM || (PROWB / UB) % KEYM == 0, "swizzle keys stay within a row of P");
+  __device__ static int pkey(int k) { return E == 2 ? ((k & 3) ^ (((k >> 3) & 1) << 1)) : (k & (KEYM - 1)); }
   // The LDS-staged epilogue needs 256-byte staged rows; smaller wave tiles
   // store straight from the accumulators.
-  static constexpr bool STAGED_EPI = (TP / (Op::OE == 4 ? 2 : 1)) * 32 * Op::OE == 256;
+  static constexpr bool STAGED_EPI = (TP / (Op::OE == 4 ? 2 : 1)) * MT * Op::OE == 256;
   // Waves per SIMD the kernel is compiled for: a 64x64 wave tile is small
   // enough for two (two workgroups per CU).
-  static constexpr int WPE = TP * TQ <= 4 && NS == 2 ? 2 : 1;
+  static constexpr int WPE = TP * TQ * ACC <= 64 && NS == 2 ? 2 : 1;
 };
 
 template <class Op, bool PERSIST, bool PKM, int BP, int BQ, int NS, bool KT>
@@ -92,7 +104,9 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   using Cfg = TnCfg<Op, PKM, BP, BQ, NS>;
   constexpr int NW = Cfg::NW, E = Cfg::E, FC = Cfg::FC, ROWB = Cfg::ROWB, BK = Cfg::BK, CPE = Cfg::CPE;
   constexpr int TP = Cfg::TP, TQ = Cfg::TQ, QSEG = Cfg::QSEG, NDMA = Cfg::NDMA;
-  constexpr int NREAD = Cfg::NREAD, NMFMA = Cfg::NMFMA, NA = Cfg::NA, NB = Cfg::NB, KB = Cfg::KB;
+  constexpr int NREAD = Cfg::NREAD, NMFMA = Cfg::NMFMA, NA = Cfg::NA, NB = Cfg::NB, NBSPAN = Cfg::NBSPAN;
+  constexpr int MT = Cfg::MT, KI = Cfg::KI, CPK = Cfg::CPK;
+  using Acc = typename Cfg::Acc;
 
   __shared__ __attribute__((aligned(1024))) char smem[Cfg::LDS];
 
@@ -123,14 +137,14 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   } else {
     // p-contiguous P (NN's B): a segment holds RPSG rows of k; lane l lands
     // at row l*16 / PROWB, byte (l*16) % PROWB, i.e. physical unit pu with
-    // offset w, which holds logical unit pu ^ (k mod KEYM).  Rows past K are
-    // past num_records and read zero; columns past the tile edge read
-    // whatever follows in B (those p are never stored).
+    // offset w, which holds logical unit pu ^ pkey(k).  Rows past K are past
+    // num_records and read zero; columns past the tile edge read whatever
+    // follows in B (those p are never stored).
 #pragma unroll
     for (int i = 0; i < Cfg::PSEG; ++i) {
       const int kr = Cfg::RPSG * (i * NW + wave_u) + (lane * 16) / Cfg::PROWB;
       const int br = (lane * 16) % Cfg::PROWB;
-      const int lu = (br / Cfg::UB) ^ (kr % Cfg::KEYM);
+      const int lu = (br / Cfg::UB) ^ Cfg::pkey(kr);
       pvo[i] = (uint32_t)(kr * a.ldp + lu * Cfg::UB + br % Cfg::UB);
     }
   }
@@ -238,10 +252,13 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   };
 
   // ---- fragments and MFMAs ----
+  // A lane holds row lr = lane % MT of its P and Q fragments; its lane group
+  // lg = lane / MT selects the k it holds.
   const int l32 = lane & 31, h = lane >> 5;
-  const int sw_r = (l32 >> 1) & 7;               // swizzle key of every fragment row of this lane
-  const uint32_t pf_base = (uint32_t)((wp * Cfg::WTP + l32) * ROWB);
-  const uint32_t qf_base = (uint32_t)(Cfg::P_LDS + (wq * Cfg::WTQ + l32) * ROWB);
+  const int lr = lane % MT, lg = lane / MT;
+  const int sw_r = (lr >> 1) & 7;                // swizzle key of every fragment row of this lane
+  const uint32_t pf_base = (uint32_t)((wp * Cfg::WTP + lr) * ROWB);
+  const uint32_t qf_base = (uint32_t)(Cfg::P_LDS + (wq * Cfg::WTQ + lr) * ROWB);
   u32x4 fa[2][TP][FC], fb[2][TQ][FC];
   // Transposing reads of p-contiguous P (ds_read_b64_tr_b16 / _tr_b8): in
   // each 16-lane group, output lane i receives element i % 4 (bytes: i % 8)
@@ -257,24 +274,28 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     if (isb || !PKM) {
       const int rr = isb ? r : r - TQ * FC;
       const int tile = rr / FC, f = rr % FC;
-      // 16-byte chunk (kk*FC + f)*2 + h of the stage row: for FP8, lane half
-      // h takes chunks h and h + 2 of each 64-k step (the k order of the
-      // MFMA's two scale blocks, see OpMX8).
-      const uint32_t off = (uint32_t)(((((kk * FC + f) * 2 + h)) ^ sw_r) << 4);
-      const char* base = sb + (isb ? qf_base : pf_base) + tile * 32 * ROWB;
+      // 16-byte chunk kk*CPK + f*(CPK/FC) + lg of the stage row: 16-bit lane
+      // group lg takes the lg-th 8 k of the step; for FP8, lane half h takes
+      // chunks h and h + 2 of each 64-k step (the k order of the MFMA's two
+      // scale blocks, see OpMX8).
+      const uint32_t off = (uint32_t)(((kk * CPK + f * (CPK / FC) + lg) ^ sw_r) << 4);
+      const char* base = sb + (isb ? qf_base : pf_base) + tile * MT * ROWB;
       const u32x4 v = *(const u32x4*)(base + off);
       if (isb) fb[set][tile][f] = v; else fa[set][tile][f] = v;
     } else {
       const int rr = r - TQ * FC;
       const int tile = rr / Cfg::PRD, q8 = rr % Cfg::PRD;   // which 8-byte piece of the fragment
-      // k of this lane's row: the k-step, the lane half h = tg / 2, the
-      // piece q8 (TRK k each), and tkey.  16-bit: half h holds k 8h .. 8h+7;
-      // FP8: pieces 0-1 hold k 16h .. 16h+15 and pieces 2-3 k 32+16h ..
-      // (the k order of the MFMA's scale blocks, see OpMX8).
-      const int krow = E == 2 ? kk * Op::KI + (tg >> 1) * (Op::KI / 2) + q8 * TRK + tkey
-                              : kk * Op::KI + (q8 >> 1) * 32 + (tg >> 1) * 16 + (q8 & 1) * 8 + tkey;
-      const int unit = (wp * (Cfg::WTP / 32) + tile) ^ tkey;
-      const char* src = sb + krow * Cfg::PROWB + unit * Cfg::UB + (tg & 1) * (16 * E) + (ts % (2 * E)) * 8;
+      // k of this lane's row: the k-step, the lane group, the piece q8 (TRK
+      // k each) and tkey.  16-bit (16 x 16 tiles): group tg holds k 8tg ..
+      // 8tg+7 of the step for the tile's 16 p; FP8 (32 x 32): the lane half
+      // h = tg / 2 holds k 16h .. 16h+15 in pieces 0-1 and k 32+16h .. in
+      // pieces 2-3 (the k order of the MFMA's scale blocks, see OpMX8), and
+      // tg % 2 picks the 16 p of the tile.
+      const int krow = E == 2 ? kk * KI + tg * 8 + q8 * TRK + tkey
+                              : kk * KI + (q8 >> 1) * 32 + (tg >> 1) * 16 + (q8 & 1) * 8 + tkey;
+      const int pbyte = (wp * Cfg::WTP + tile * MT) * E + (E == 2 ? 0 : (tg & 1) * (16 * E));
+      const int unit = (pbyte / Cfg::UB) ^ Cfg::pkey(krow);
+      const char* src = sb + krow * Cfg::PROWB + unit * Cfg::UB + pbyte % Cfg::UB + (ts % (2 * E)) * 8;
       typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
       u32x2 v;
       if constexpr (E == 2) {
@@ -290,14 +311,14 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       fa[set][tile][q8 >> 1][2 * (q8 & 1) + 1] = v[1];
     }
   };
-  f32x16 acc[TP][TQ];
+  Acc acc[TP][TQ];
   auto zero_acc = [&]() {
 #pragma unroll
     for (int i = 0; i < TP; ++i)
 #pragma unroll
       for (int j = 0; j < TQ; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        for (int r = 0; r < Cfg::ACC; ++r) acc[i][j][r] = 0.0f;
   };
   // MX block scales: for the stage in use, lane l holds in scp[i] / scq[j]
   // the scales of its row of P tile i / Q tile j for k blocks h and h + 2
@@ -364,12 +385,19 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     if constexpr (Op::MX) {
       if (kk == 0) acc[i][j] = Op::template mma_mx<0>(fa[set][i], fb[set][j], acc[i][j], scp[i], scq[j]);
       else acc[i][j] = Op::template mma_mx<1>(fa[set][i], fb[set][j], acc[i][j], scp[i], scq[j]);
+    } else if constexpr (MT == 16) {
+      (void)kk;
+      acc[i][j] = Op::mma16(fa[set][i], fb[set][j], acc[i][j]);
     } else {
       (void)kk;
       acc[i][j] = Op::mma_parts(fa[set][i], fb[set][j], acc[i][j]);
     }
   };
-  auto read_slot = [](int r, int span) { return r * span / NREAD; };
+  // n operations spread over `span` MFMA slots: operation i goes out after
+  // MFMA i * span / n, so slot t issues i in [first(n, span, t),
+  // first(n, span, t + 1)).  (Ranges, not a test of every i in every slot:
+  // the unroller would give up on the larger 16 x 16 schedules.)
+  auto first = [](int n, int span, int t) { return (t * n + span - 1) / span; };
   constexpr int LAST = (Cfg::KSTEPS - 1) & 1;
 
   // ---- one stage ----
@@ -396,12 +424,11 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       for (int t = 0; t < NMFMA; ++t) {
         mfma_one(kk & 1, t, kk);
 #pragma unroll
-        for (int r = 0; r < NREAD; ++r)
-          if (read_slot(r, span) == t) read_one(sb, kk + 1, (kk + 1) & 1, r);
+        for (int r = first(NREAD, span, t); r < first(NREAD, span, t + 1); ++r) read_one(sb, kk + 1, (kk + 1) & 1, r);
         if constexpr (NB > 0) {
+          const int x = kk * NMFMA + t;
 #pragma unroll
-          for (int j = 0; j < NB; ++j)
-            if (j * (KB * NMFMA) / NB == kk * NMFMA + t) copy_d(p1, ob, NA + j);
+          for (int j = first(NB, NBSPAN, x); j < first(NB, NBSPAN, x + 1) && j < NB; ++j) copy_d(p1, ob, NA + j);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -431,11 +458,9 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     for (int t = 0; t < NMFMA; ++t) {
       mfma_one(LAST, t, Cfg::KSTEPS - 1);
 #pragma unroll
-      for (int r = 0; r < NREAD; ++r)
-        if (read_slot(r, NMFMA) == t) read_one(ob, 0, 0, r);
+      for (int r = first(NREAD, NMFMA, t); r < first(NREAD, NMFMA, t + 1); ++r) read_one(ob, 0, 0, r);
 #pragma unroll
-      for (int d = 0; d < NA; ++d)
-        if (d * NMFMA / NA == t) copy_d(p2, db, d);
+      for (int d = first(NA, NMFMA, t); d < first(NA, NMFMA, t + 1); ++d) copy_d(p2, db, d);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (Op::MX) {
@@ -494,7 +519,11 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     for (int r = 0; r < NREAD; ++r) read_one(smem, 0, 0, r);
   }
   // Epilogue straight from the accumulators: four consecutive p of one q per
-  // lane and group, one 8- or 16-byte store each.
+  // lane and group, one 8- or 16-byte store each (32 x 32 tiles: lane l
+  // holds q = 32 j + l % 32, p = 32 i + 8 g + 4 (l / 32) for group g; 16 x 16
+  // tiles: q = 16 j + l % 16, p = 16 i + 4 (l / 16)).
+  static_assert(MT == 32 || !Op::SCALED, "scale factors follow the 32 x 32 layout");
+  constexpr int NG = MT * MT / 256;   // register groups of four per tile
   auto direct_epilogue = [&](int64_t t) {
     int64_t tp, tq;
     tile_map(a.tiles_p, a.tiles_q, a.group, t, &tp, &tq);
@@ -512,11 +541,11 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       }
 #pragma unroll
       for (int j = 0; j < TQ; ++j) {
-        const int64_t q = qb + 32 * j + l32;
+        const int64_t q = qb + MT * j + lr;
         if (q >= a.Qn) continue;
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          const int64_t p = pb + 32 * i + 8 * gg + 4 * h;
+        for (int gg = 0; gg < NG; ++gg) {
+          const int64_t p = pb + MT * i + 8 * gg + 4 * lg;
           float v0 = acc[i][j][4 * gg + 0], v1 = acc[i][j][4 * gg + 1], v2 = acc[i][j][4 * gg + 2],
                 v3 = acc[i][j][4 * gg + 3];
           if constexpr (Op::SCALED) sc.apply(fp[gg], j, v0, v1, v2, v3);
@@ -556,7 +585,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       int64_t tp, tq;
       tile_map(a.tiles_p, a.tiles_q, a.group, tile, &tp, &tq);
       static_assert(!Cfg::STAGED_EPI || Cfg::WTQ * 256 * NW <= 2 * Cfg::STAGE, "staging fits in the stage buffers");
-      staged_epilogue<Op, Cfg::WTP, Cfg::WTQ, TP, TQ>(a, smem + wave_u * (Cfg::WTQ * 256), acc, lane,
+      staged_epilogue<Op, Cfg::WTP, Cfg::WTQ, TP, TQ, MT, Acc>(a, smem + wave_u * (Cfg::WTQ * 256), acc, lane,
                                                        tp * Cfg::BP + wp * Cfg::WTP, tq * Cfg::BQ + wq * Cfg::WTQ);
     } else {
       direct_epilogue(tile);
