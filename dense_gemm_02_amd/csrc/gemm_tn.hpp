@@ -76,12 +76,16 @@ struct TnCfg {
   static constexpr int KEYM = 256 / UB;
   static constexpr int RPSG = 1024 / PROWB;       // rows of P per 1 KiB copy segment
   static constexpr int NMFMA = TP * TQ;           // MFMAs per k-step
-  // Copy split: FP16/BF16 issue half of a stage's copies after the barrier
-  // two stages ahead and the rest over the first NBSPAN MFMA slots of the
-  // stage before; FP8 issues them all after the barrier.
-  static constexpr int NA = (Op::ELEM == 2 && NS == 2) ? NDMA / 2 : NDMA;
+  // Copy split: FP16/BF16 issue three quarters of a stage's copies after the
+  // barrier two stages ahead, over the first NASPAN MFMA slots, and the rest
+  // over the first NBSPAN slots of the stage before; FP8 issues them all
+  // after the barrier, over every slot.  (16 x 16 tiles, measured against an
+  // even split: +3-4%; the after-barrier copies within three quarters of the
+  // slots: +1%.)
+  static constexpr int NA = (Op::ELEM == 2 && NS == 2) ? 3 * NDMA / 4 : NDMA;
   static constexpr int NB = NDMA - NA;
-  static constexpr int NBSPAN = NMFMA / 2;
+  static constexpr int NASPAN = Op::ELEM == 2 ? 3 * NMFMA / 4 : NMFMA;
+  static constexpr int NBSPAN = NMFMA / 4;
   static_assert(NB == 0 || NBSPAN <= (KSTEPS - 1) * NMFMA, "part-B copies go out before the barrier");
   static_assert(LDS <= kLdsLimit, "LDS budget");
   // The scale ring relies on every mid-stage wait draining all copies.
@@ -105,6 +109,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   constexpr int NW = Cfg::NW, E = Cfg::E, FC = Cfg::FC, ROWB = Cfg::ROWB, BK = Cfg::BK, CPE = Cfg::CPE;
   constexpr int TP = Cfg::TP, TQ = Cfg::TQ, QSEG = Cfg::QSEG, NDMA = Cfg::NDMA;
   constexpr int NREAD = Cfg::NREAD, NMFMA = Cfg::NMFMA, NA = Cfg::NA, NB = Cfg::NB, NBSPAN = Cfg::NBSPAN;
+  constexpr int NASPAN = Cfg::NASPAN;
   constexpr int MT = Cfg::MT, KI = Cfg::KI, CPK = Cfg::CPK;
   using Acc = typename Cfg::Acc;
 
@@ -460,7 +465,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
 #pragma unroll
       for (int r = first(NREAD, NMFMA, t); r < first(NREAD, NMFMA, t + 1); ++r) read_one(ob, 0, 0, r);
 #pragma unroll
-      for (int d = first(NA, NMFMA, t); d < first(NA, NMFMA, t + 1); ++d) copy_d(p2, db, d);
+      for (int d = first(NA, NASPAN, t); d < first(NA, NASPAN, t + 1) && d < NA; ++d) copy_d(p2, db, d);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (Op::MX) {
