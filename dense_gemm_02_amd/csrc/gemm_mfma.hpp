@@ -109,6 +109,16 @@ struct OpFP8 {
                                              2, 3, 4, 5, 6, 7);
     return mma(av, bv, c);
   }
+  // The 16 x 16 x 128 MFMA (the four-wave kernel): lane l holds row l % 16
+  // of A and column l % 16 of B, each with 32 bytes of k (lanes 16g .. 16g +
+  // 15 the same k); D holds rows 4 (l / 16) .. 4 (l / 16) + 3 of column l % 16.
+  __device__ static f32x4 mma16(const u32x4 (&a)[2], const u32x4 (&b)[2], f32x4 c) {
+    const i32x8 av = __builtin_shufflevector(__builtin_bit_cast(i32x4, a[0]), __builtin_bit_cast(i32x4, a[1]), 0, 1,
+                                             2, 3, 4, 5, 6, 7);
+    const i32x8 bv = __builtin_shufflevector(__builtin_bit_cast(i32x4, b[0]), __builtin_bit_cast(i32x4, b[1]), 0, 1,
+                                             2, 3, 4, 5, 6, 7);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
+  }
 };
 
 // FP8 with per-tensor or per-row scale factors: the same MFMAs, with the
@@ -184,11 +194,12 @@ __device__ __forceinline__ void store4(const GemmArgs& a, int64_t q, int64_t p, 
 // Scale factors of one wave's tile (FP8 scaled entry point), applied as the
 // accumulators are converted: D[p][q] = acc * (sp(p) * sq(q)), each product
 // rounded to FP32, where sp(p) = a.sp[p] (a.sp_row) or a.sp[0], and likewise
-// sq.  Lane l stores q = qbase + 32 j + l % 32, whose factors it holds for the
-// whole epilogue, and groups of four consecutive p, whose factors it fetches
-// per group.  Per-row factors are read through buffer descriptors sized to
-// the vectors, so a p or q past the edge reads 0 (never stored).
-template <int TQ>
+// sq.  Lane l stores q = qbase + MT j + l % MT (MT the MFMA tile), whose
+// factors it holds for the whole epilogue, and groups of four consecutive p,
+// whose factors it fetches per group.  Per-row factors are read through
+// buffer descriptors sized to the vectors, so a p or q past the edge reads 0
+// (never stored).
+template <int TQ, int MT = 32>
 struct EpiScale {
   float fq[TQ];
   __device__ void init(const GemmArgs& a, int lane, int64_t qbase) {
@@ -197,7 +208,7 @@ struct EpiScale {
 #pragma unroll
       for (int j = 0; j < TQ; ++j)
         fq[j] = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rq, (int)((qbase + 32 * j + (lane & 31)) * 4), 0, 0));
+            float, __builtin_amdgcn_raw_buffer_load_b32(rq, (int)((qbase + MT * j + lane % MT) * 4), 0, 0));
     } else {
       const float f = a.sq[0];
 #pragma unroll
@@ -255,10 +266,9 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& a, char* reg, co
   constexpr int NG = MT * MT / 256;           // register groups of four per accumulator tile
   static_assert(RB == 256, "staged rows are 256 bytes");
   static_assert(WTQ % 4 == 0, "four rows per read-back instruction");
-  static_assert(MT == 32 || !Op::SCALED, "scale factors follow the 32 x 32 layout");
   auto key = [](int row) { return MT == 32 ? row % NSL : (OE == 2 ? 2 * (row % 16) : row % 16); };
   const int lr = lane % MT, lg = lane / MT;
-  [[maybe_unused]] EpiScale<TQ> sc;
+  [[maybe_unused]] EpiScale<TQ, MT> sc;
   if constexpr (Op::SCALED) sc.init(a, lane, qbase);
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
@@ -267,11 +277,14 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& a, char* reg, co
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         [[maybe_unused]] f32x4 fp;
-        if constexpr (Op::SCALED) fp = EpiScale<TQ>::p4(a, pbase + 32 * (pass * TPP + i) + 8 * g + 4 * lg);
+        if constexpr (Op::SCALED) fp = EpiScale<TQ, MT>::p4(a, pbase + MT * (pass * TPP + i) + 8 * g + 4 * lg);
 #pragma unroll
         for (int j = 0; j < TQ; ++j) {
           const AccT& v = acc[pass * TPP + i][j];
           float v0 = v[4 * g], v1 = v[4 * g + 1], v2 = v[4 * g + 2], v3 = v[4 * g + 3];
+          // 16 x 16: through vector registers (see the direct epilogue of
+          // the four-wave kernel).
+          if constexpr (MT == 16) asm("" : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3));
           if constexpr (Op::SCALED) sc.apply(fp, j, v0, v1, v2, v3);
           const int row = MT * j + lr;
           // slot of p = MT i + 8 g + 4 lg (32 x 32) or MT i + 4 lg (16 x 16)

@@ -51,17 +51,24 @@ struct TnCfg {
   static constexpr int QSEG = BQ / 8 / NW, PSEG = BP / 8 / NW;
   static constexpr int NDMA = QSEG + PSEG;        // copy instructions per wave per stage
   static constexpr int WTP = BP / WP, WTQ = BQ / WQ;
-  // MFMA tile: 16 x 16 x 32 for FP16/BF16, which sustains about 12% more
-  // throughput than 32 x 32 x 16 on the same wave tile once the chip runs
-  // at its power limit (random operands; equal at zero data), and
-  // 32 x 32 x 64 for FP8.
-  static constexpr int MT = E == 2 ? 16 : 32;
-  static constexpr int KI = E == 2 ? 32 : Op::KI;  // k per MFMA
+  // MFMA tile: 16 x 16 (x 32 for FP16/BF16, x 128 for FP8), which sustains
+  // 10-13% more throughput than the 32 x 32 shapes on the same wave tile
+  // once the chip runs at its power limit (random operands; equal at zero
+  // data); MXFP8 keeps 32 x 32 x 64, whose block-scale lanes are mapped.
+  static constexpr int MT = Op::MX ? 32 : 16;
+  static constexpr int KI = E == 2 ? 32 : (MT == 16 ? 128 : Op::KI);  // k per MFMA
   static constexpr int ACC = MT * MT / 64;         // accumulator registers per tile
   using Acc = std::conditional_t<MT == 16, f32x4, f32x16>;
   static constexpr int TP = WTP / MT, TQ = WTQ / MT;
   static constexpr int KSTEPS = BK / KI;
   static constexpr int CPK = KI * E / 16;          // 16-byte chunks of k per k-step
+  // One k-step per stage (FP8 16 x 16 x 128): fragments cannot be double
+  // buffered next to the accumulators, so the stage runs "rolling": P tiles
+  // 0 .. TP/2-1 against every Q tile before the barrier while P tiles TP/2 ..
+  // come in, the rest after it, Q tile by Q tile, each fragment register
+  // refilled with the next stage's data right after its last use.
+  static constexpr bool ROLL = KSTEPS == 1;
+  static_assert(!ROLL || TP % 2 == 0, "two halves of P tiles");
   // LDS reads per k-step: 16-byte reads of Q fragments, and of P fragments
   // either 16-byte reads (K-contiguous P) or twice as many 8-byte
   // transposing reads (p-contiguous P).
@@ -76,6 +83,9 @@ struct TnCfg {
   static constexpr int KEYM = 256 / UB;
   static constexpr int RPSG = 1024 / PROWB;       // rows of P per 1 KiB copy segment
   static constexpr int NMFMA = TP * TQ;           // MFMAs per k-step
+  // MFMA slots before and after the barrier
+  static constexpr int SLOTS1 = ROLL ? NMFMA / 2 : (KSTEPS - 1) * NMFMA;
+  static constexpr int SLOTS2 = ROLL ? NMFMA / 2 : NMFMA;
   // Copy split: FP16/BF16 issue three quarters of a stage's copies after the
   // barrier two stages ahead, over the first NASPAN MFMA slots, and the rest
   // over the first NBSPAN slots of the stage before; FP8 issues them all
@@ -84,9 +94,9 @@ struct TnCfg {
   // slots: +1%.)
   static constexpr int NA = (Op::ELEM == 2 && NS == 2) ? 3 * NDMA / 4 : NDMA;
   static constexpr int NB = NDMA - NA;
-  static constexpr int NASPAN = Op::ELEM == 2 ? 3 * NMFMA / 4 : NMFMA;
+  static constexpr int NASPAN = Op::ELEM == 2 ? 3 * SLOTS2 / 4 : SLOTS2;
   static constexpr int NBSPAN = NMFMA / 4;
-  static_assert(NB == 0 || NBSPAN <= (KSTEPS - 1) * NMFMA, "part-B copies go out before the barrier");
+  static_assert(NB == 0 || NBSPAN <= SLOTS1, "part-B copies go out before the barrier");
   static_assert(LDS <= kLdsLimit, "LDS budget");
   // The scale ring relies on every mid-stage wait draining all copies.
   static_assert(!Op::MX || NS == 2, "MX scale groups need two stages");
@@ -94,7 +104,12 @@ struct TnCfg {
   // NS - 2 later stream positions.
   static constexpr int VM_MID = (NS - 2) * NDMA;
   static_assert(!PKM || (PROWB / UB) % KEYM == 0, "swizzle keys stay within a row of P");
-  __device__ static int pkey(int k) { return E == 2 ? ((k & 3) ^ (((k >> 3) & 1) << 1)) : (k & (KEYM - 1)); }
+  // FP8 16 x 16: lane groups 0 and 1 read k rows sixteen apart.
+  __device__ static int pkey(int k) {
+    if constexpr (E == 2) return (k & 3) ^ (((k >> 3) & 1) << 1);
+    else if constexpr (MT == 16) return (k & 7) ^ (((k >> 4) & 1) << 2);
+    else return k & (KEYM - 1);
+  }
   // The LDS-staged epilogue needs 256-byte staged rows; smaller wave tiles
   // store straight from the accumulators.
   static constexpr bool STAGED_EPI = (TP / (Op::OE == 4 ? 2 : 1)) * MT * Op::OE == 256;
@@ -291,14 +306,18 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       const int rr = r - TQ * FC;
       const int tile = rr / Cfg::PRD, q8 = rr % Cfg::PRD;   // which 8-byte piece of the fragment
       // k of this lane's row: the k-step, the lane group, the piece q8 (TRK
-      // k each) and tkey.  16-bit (16 x 16 tiles): group tg holds k 8tg ..
-      // 8tg+7 of the step for the tile's 16 p; FP8 (32 x 32): the lane half
-      // h = tg / 2 holds k 16h .. 16h+15 in pieces 0-1 and k 32+16h .. in
-      // pieces 2-3 (the k order of the MFMA's scale blocks, see OpMX8), and
-      // tg % 2 picks the 16 p of the tile.
-      const int krow = E == 2 ? kk * KI + tg * 8 + q8 * TRK + tkey
-                              : kk * KI + (q8 >> 1) * 32 + (tg >> 1) * 16 + (q8 & 1) * 8 + tkey;
-      const int pbyte = (wp * Cfg::WTP + tile * MT) * E + (E == 2 ? 0 : (tg & 1) * (16 * E));
+      // k each) and tkey, in the order of the K-contiguous reads of Q.
+      // 16-bit (16 x 16): group tg holds k 8tg .. 8tg+7 of the step.  FP8
+      // 16 x 16: group tg holds k 16tg .. 16tg+15 in pieces 0-1 and k 64+16tg
+      // .. in pieces 2-3.  FP8 32 x 32: the lane half h = tg / 2 holds k
+      // 16h .. 16h+15 in pieces 0-1 and k 32+16h .. in pieces 2-3 (the k
+      // order of the MFMA's scale blocks, see OpMX8), and tg % 2 picks the 16
+      // p of the tile.
+      int krow;
+      if constexpr (E == 2) krow = kk * KI + tg * 8 + q8 * TRK + tkey;
+      else if constexpr (MT == 16) krow = kk * KI + (q8 >> 1) * 64 + tg * 16 + (q8 & 1) * 8 + tkey;
+      else krow = kk * KI + (q8 >> 1) * 32 + (tg >> 1) * 16 + (q8 & 1) * 8 + tkey;
+      const int pbyte = (wp * Cfg::WTP + tile * MT) * E + (MT == 16 ? 0 : (tg & 1) * (16 * E));
       const int unit = (pbyte / Cfg::UB) ^ Cfg::pkey(krow);
       const char* src = sb + krow * Cfg::PROWB + unit * Cfg::UB + pbyte % Cfg::UB + (ts % (2 * E)) * 8;
       typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -405,6 +424,74 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   auto first = [](int n, int span, int t) { return (t * n + span - 1) / span; };
   constexpr int LAST = (Cfg::KSTEPS - 1) & 1;
 
+  // Stream position g + NS (the copies after the barrier of stage g).
+  auto pos_far = [&](int s, const Src& cu, const Src& nx) -> Pos {
+    if constexpr (PERSIST) {
+      const bool n2 = s + NS >= nst;
+      const Src& src = n2 ? nx : cu;
+      return pos_at(src, n2 ? s + NS - nst : s + NS, src.qn != 0);
+    } else {
+      (void)nx;
+      return pos_at(cu, s + NS, s + NS < nst);
+    }
+  };
+
+  // ---- one stage, rolling (one k-step per stage) ----
+  // Phase 1, before the barrier: P tiles 0 .. HP-1 against every Q tile,
+  // Q-major, while P tiles HP .. TP-1 of this stage are read (their
+  // registers were freed by the previous stage's phase 2).  Phase 2: P tiles
+  // HP .. TP-1, Q-major, so Q tile j is done after slot HP (j + 1) - 1 and
+  // its next-stage fragment is read right then; P tiles 0 .. HP-1 of the
+  // next stage are read over the first three quarters of the phase.  Every
+  // read of buffer g % NS is issued before the barrier, so the copies after
+  // it may overwrite that buffer; the next stage's reads come after it, once
+  // its data is known to have landed.  Copies as in `stage`.
+  auto stage_roll = [&](int g, int s, const Src& cu, const Src& nx, Pos& p1) {
+    constexpr int HP = TP / 2, NM1 = Cfg::SLOTS1;
+    constexpr int RQ = TQ * FC;                 // reads of the Q fragments
+    constexpr int RP = HP * Cfg::PRD;           // reads of half the P fragments
+    const int b = g & (NS - 1);
+    const char* sb = smem + b * Cfg::STAGE;
+    char* ob = smem + ((g + 1) & (NS - 1)) * Cfg::STAGE;
+    auto mma_ij = [&](int i, int j) {
+      if constexpr (MT == 16) acc[i][j] = Op::mma16(fa[0][i], fb[0][j], acc[i][j]);
+    };
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < NM1; ++t) {
+      mma_ij(t % HP, t / HP);
+#pragma unroll
+      for (int x = first(RP, NM1 / 2, t); x < first(RP, NM1 / 2, t + 1) && x < RP; ++x)
+        read_one(sb, 0, 0, RQ + RP + x);
+      if constexpr (NB > 0) {
+#pragma unroll
+        for (int j = first(NB, NBSPAN, t); j < first(NB, NBSPAN, t + 1) && j < NB; ++j) copy_d(p1, ob, NA + j);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (NS == 2) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    else __builtin_amdgcn_s_waitcnt(kWaitVmcntBase | vmcnt_bits(Cfg::VM_MID));
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    const Pos p2 = pos_far(s, cu, nx);
+    char* db = smem + b * Cfg::STAGE;
+#pragma unroll
+    for (int u = 0; u < NM1; ++u) {
+      mma_ij(HP + u % HP, u / HP);
+      if (u % HP == HP - 1) {
+#pragma unroll
+        for (int f = 0; f < FC; ++f) read_one(ob, 0, 0, (u / HP) * FC + f);
+      }
+#pragma unroll
+      for (int x = first(RP, 3 * NM1 / 4, u); x < first(RP, 3 * NM1 / 4, u + 1) && x < RP; ++x)
+        read_one(ob, 0, 0, RQ + x);
+#pragma unroll
+      for (int d = first(NA, NASPAN, u); d < first(NA, NASPAN, u + 1) && d < NA; ++d) copy_d(p2, db, d);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    p1 = p2;
+  };
+
   // ---- one stage ----
   // Global stage g (buffer g % NS) is stage s of the current tile.  Copies
   // issued here belong to the stream position g + NS (after the barrier; NA
@@ -449,15 +536,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     if constexpr (Op::MX) read_scales((gam + (opens ? 1 : 0)) & 1, snext % Cfg::SG_STAGES);
     __builtin_amdgcn_sched_barrier(0);
     // stream position g + NS
-    Pos p2;
-    if constexpr (PERSIST) {
-      const bool n2 = s + NS >= nst;
-      const Src& src = n2 ? nx : cu;
-      p2 = pos_at(src, n2 ? s + NS - nst : s + NS, src.qn != 0);
-    } else {
-      (void)nx;
-      p2 = pos_at(cu, s + NS, s + NS < nst);
-    }
+    const Pos p2 = pos_far(s, cu, nx);
     char* db = smem + b * Cfg::STAGE;
 #pragma unroll
     for (int t = 0; t < NMFMA; ++t) {
@@ -520,29 +599,31 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcntBase | vmcnt_bits(Cfg::VM_MID + NA));
     __syncthreads();
     if constexpr (Op::MX) read_scales(0, 0);
+    // Stage 0's first fragments: all of them, or (rolling) the Q tiles and
+    // the first half of the P tiles.
+    constexpr int NR0 = Cfg::ROLL ? TQ * FC + (TP / 2) * Cfg::PRD : NREAD;
 #pragma unroll
-    for (int r = 0; r < NREAD; ++r) read_one(smem, 0, 0, r);
+    for (int r = 0; r < NR0; ++r) read_one(smem, 0, 0, r);
   }
   // Epilogue straight from the accumulators: four consecutive p of one q per
   // lane and group, one 8- or 16-byte store each (32 x 32 tiles: lane l
   // holds q = 32 j + l % 32, p = 32 i + 8 g + 4 (l / 32) for group g; 16 x 16
   // tiles: q = 16 j + l % 16, p = 16 i + 4 (l / 16)).
-  static_assert(MT == 32 || !Op::SCALED, "scale factors follow the 32 x 32 layout");
   constexpr int NG = MT * MT / 256;   // register groups of four per tile
   auto direct_epilogue = [&](int64_t t) {
     int64_t tp, tq;
     tile_map(a.tiles_p, a.tiles_q, a.group, t, &tp, &tq);
     const int64_t pb = tp * Cfg::BP + wp * Cfg::WTP, qb = tq * Cfg::BQ + wq * Cfg::WTQ;
-    [[maybe_unused]] EpiScale<TQ> sc;
+    [[maybe_unused]] EpiScale<TQ, MT> sc;
     if constexpr (Op::SCALED) sc.init(a, lane, qb);
     // Column by column: a lane's four stores into one column of C follow
     // each other, so each 128-byte line is written whole while it is open.
 #pragma unroll
     for (int i = 0; i < TP; ++i) {
-      [[maybe_unused]] f32x4 fp[4];
+      [[maybe_unused]] f32x4 fp[NG];
       if constexpr (Op::SCALED) {
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) fp[gg] = EpiScale<TQ>::p4(a, pb + 32 * i + 8 * gg + 4 * h);
+        for (int gg = 0; gg < NG; ++gg) fp[gg] = EpiScale<TQ, MT>::p4(a, pb + MT * i + 8 * gg + 4 * lg);
       }
 #pragma unroll
       for (int j = 0; j < TQ; ++j) {
@@ -553,6 +634,11 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
           const int64_t p = pb + MT * i + 8 * gg + 4 * lg;
           float v0 = acc[i][j][4 * gg + 0], v1 = acc[i][j][4 * gg + 1], v2 = acc[i][j][4 * gg + 2],
                 v3 = acc[i][j][4 * gg + 3];
+          // 16 x 16: take the values through vector registers.  (Stored
+          // straight from the accumulator registers, they led the register
+          // allocator to give most MFMAs of the loop a separate destination
+          // and copy every accumulator each stage.)
+          if constexpr (MT == 16) asm("" : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3));
           if constexpr (Op::SCALED) sc.apply(fp[gg], j, v0, v1, v2, v3);
           store4<Op>(a, q, p, v0, v1, v2, v3);
         }
@@ -565,7 +651,10 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   int g = 0;
   for (;;) {
     zero_acc();
-    for (int s = 0; s < nst; ++s, ++g) stage(g, s, cur, nxt, nx2, p1);
+    for (int s = 0; s < nst; ++s, ++g) {
+      if constexpr (Cfg::ROLL) stage_roll(g, s, cur, nxt, p1);
+      else stage(g, s, cur, nxt, nx2, p1);
+    }
     if constexpr (!PERSIST) break;
     // Persistent: the stores drain while the next tile's stages (already
     // copied) run.

@@ -247,8 +247,11 @@ def test_split_choice(lib, dt, layout, M, N, K, axis, at, tail):
 def test_no_split_when_rounds_are_whole_or_it_does_not_pay(lib, M, N, K):
     for dt in (1, 2, 3):
         assert " + " not in _kernel(lib, dt, 1, M, N, K)
-    # FP8 TN at 256 x 256 runs persistent workgroups, a multiple of the 8 XCDs.
-    assert "persistent" in _kernel(lib, 3, 1, 5120, 5120, 1024)
+    # MXFP8 TN at 256 x 256 runs persistent workgroups, a multiple of the 8
+    # XCDs; FP8 (16 x 16 x 128 tiles) one tile per workgroup.
+    assert "persistent" in _kernel(lib, 5, 1, 5120, 5120, 1024)
+    fp8 = _kernel(lib, 3, 1, 5120, 5120, 1024)
+    assert fp8.split()[0] == "fp8_tn_256x256_w4" and "grid=400 " in fp8, fp8
     # K not a whole number of 16-byte chunks: the eight-wave kernel.
     assert "_w4" not in _kernel(lib, 2, 1, 4096, 4096, 4100)
 
