@@ -250,9 +250,9 @@ struct EpiScale {
 // MT is the MFMA tile: 32 x 32 accumulators (lane l: q = 32 j + l % 32,
 // p = 32 i + 8 g + 4 (l / 32) + 0..3 for register group g) or 16 x 16
 // (lane l: q = 16 j + l % 16, p = 16 i + 4 (l / 16) + 0..3).  With 16 x 16
-// one write instruction covers 16 rows and four slots of each; the key
-// 2 (row mod 16) (8-byte slots) or row mod 16 (16-byte slots) spreads them
-// over all banks and keeps 8-byte slot pairs aligned.
+// one write instruction covers 16 rows and four slots of each, keyed by
+// row mod 16 (measured: SQ_LDS_BANK_CONFLICT 0; the even key 2 (row mod 16),
+// which keeps 8-byte slot pairs in place, left 4 conflict cycles per write).
 template <class Op, int WTP, int WTQ, int TP, int TQ, int MT = 32, class AccT = f32x16>
 __device__ __forceinline__ void staged_epilogue(const GemmArgs& a, char* reg, const AccT (&acc)[TP][TQ], int lane,
                                                 int64_t pbase, int64_t qbase) {
@@ -266,7 +266,7 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& a, char* reg, co
   constexpr int NG = MT * MT / 256;           // register groups of four per accumulator tile
   static_assert(RB == 256, "staged rows are 256 bytes");
   static_assert(WTQ % 4 == 0, "four rows per read-back instruction");
-  auto key = [](int row) { return MT == 32 ? row % NSL : (OE == 2 ? 2 * (row % 16) : row % 16); };
+  auto key = [](int row) { return MT == 32 ? row % NSL : row % 16; };
   const int lr = lane % MT, lg = lane / MT;
   [[maybe_unused]] EpiScale<TQ, MT> sc;
   if constexpr (Op::SCALED) sc.init(a, lane, qbase);
