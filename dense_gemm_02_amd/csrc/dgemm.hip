@@ -61,17 +61,17 @@ Launch mfma_launch(const char* name) {
                 2 * Cfg::STAGE, PT, false};
 }
 
-// Four-wave kernel (gemm_tn.hpp).  256 x 256 MXFP8, whose FP32 output is
-// twice as large, runs persistently so that each tile's stores drain under
-// the next tile's stages; every other shape runs one tile per workgroup
-// (FP8 on 16 x 16 x 128 tiles needs the registers the persistent loop would
-// keep for the next tile: there it spilled inside the stage loop).  `kt`: K is
+// Four-wave kernel (gemm_tn.hpp), one tile per workgroup.  (With 32 x 32
+// MFMA tiles, 256 x 256 FP8 ran persistently so that each tile's FP32 stores
+// drained under the next tile's stages; on 16 x 16 x 128 tiles the persistent
+// loop spilled inside its stage loop, holding the next tile's state on top of
+// the fragments.)  `kt`: K is
 // not a whole number of stages, so the copies need tail masks (a separate
 // instantiation: without a tail they cost nothing).
 template <class Op, bool PKM, int BP, int BQ, int NS = 2>
 Launch tn_launch(const char* name, bool kt) {
   using Cfg = TnCfg<Op, PKM, BP, BQ, NS>;
-  constexpr bool P = Op::MX && BP == 256 && BQ == 256;
+  constexpr bool P = Cfg::MT == 32 && Op::ELEM == 1 && BP == 256 && BQ == 256;
   const void* fn = kt ? (const void*)&gemm_tn_kernel<Op, P, PKM, BP, BQ, NS, true>
                       : (const void*)&gemm_tn_kernel<Op, P, PKM, BP, BQ, NS, false>;
   return Launch{fn, name, BP, BQ, Cfg::NT, Cfg::LDS, PKM, P};
@@ -185,7 +185,7 @@ Launch four_wave(int dt, bool nn, int idx, bool kt) {
                                               nullptr};
   static const char* const fp8sn[kNumTiles] = {"fp8s_nn_256x256_w4", "fp8s_nn_256x128_w4", nullptr,
                                                nullptr};
-  static const char* const mxn[kNumTiles] = {"mx8_nn_256x256_w4_persistent", "mx8_nn_256x128_w4", nullptr, nullptr};
+  static const char* const mxn[kNumTiles] = {"mx8_nn_256x256_w4", "mx8_nn_256x128_w4", nullptr, nullptr};
   static const char* const f16t[kNumTiles] = {"f16_tn_256x256_w4", nullptr, "f16_tn_128x128_w4",
                                              "f16_tn_128x128_w4_s4"};
   static const char* const bf16t[kNumTiles] = {"bf16_tn_256x256_w4", nullptr, "bf16_tn_128x128_w4",
@@ -194,7 +194,7 @@ Launch four_wave(int dt, bool nn, int idx, bool kt) {
                                               "fp8_tn_128x128_w4_s4"};
   static const char* const fp8st[kNumTiles] = {"fp8s_tn_256x256_w4", nullptr, "fp8s_tn_128x128_w4",
                                                "fp8s_tn_128x128_w4_s4"};
-  static const char* const mxt[kNumTiles] = {"mx8_tn_256x256_w4_persistent", nullptr, "mx8_tn_128x128_w4", nullptr};
+  static const char* const mxt[kNumTiles] = {"mx8_tn_256x256_w4", nullptr, "mx8_tn_128x128_w4", nullptr};
   if (nn) {
     switch (dt) {
       case DT_F16: return tn_make<OpF16, true>(f16n, idx, kt);

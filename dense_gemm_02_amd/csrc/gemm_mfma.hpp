@@ -148,6 +148,21 @@ struct OpMX8 : OpFP8 {
                                              2, 3, 4, 5, 6, 7);
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 2 * KK, (int)sa, 2 * KK, (int)sb);
   }
+  // 16 x 16 x 128 with block scales.  Lane group L = l / 16 holds bytes 0-15
+  // and 16-31 of its row; the instruction's four blocks of 32 k are {groups
+  // 0, 1} x bytes 0-15, {2, 3} x bytes 0-15, {0, 1} x bytes 16-31 and {2, 3} x
+  // bytes 16-31, and the scale of block L comes from lane group L (byte 0 of
+  // its scale register here).  Loading chunk L into bytes 0-15 and chunk L + 4
+  // into bytes 16-31 (16 k each) makes block L the L-th 32 k of the stage.
+  // (Determined on gfx950 with one-hot operands and one scaled lane at a
+  // time, for A and for B.)
+  __device__ static f32x4 mma16_mx(const u32x4 (&a)[2], const u32x4 (&b)[2], f32x4 c, uint32_t sa, uint32_t sb) {
+    const i32x8 av = __builtin_shufflevector(__builtin_bit_cast(i32x4, a[0]), __builtin_bit_cast(i32x4, a[1]), 0, 1,
+                                             2, 3, 4, 5, 6, 7);
+    const i32x8 bv = __builtin_shufflevector(__builtin_bit_cast(i32x4, b[0]), __builtin_bit_cast(i32x4, b[1]), 0, 1,
+                                             2, 3, 4, 5, 6, 7);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, (int)sa, 0, (int)sb);
+  }
 };
 
 // Zero the bytes of a 16-byte chunk at and beyond `valid_bytes` (0..16).

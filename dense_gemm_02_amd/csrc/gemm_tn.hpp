@@ -51,11 +51,11 @@ struct TnCfg {
   static constexpr int QSEG = BQ / 8 / NW, PSEG = BP / 8 / NW;
   static constexpr int NDMA = QSEG + PSEG;        // copy instructions per wave per stage
   static constexpr int WTP = BP / WP, WTQ = BQ / WQ;
-  // MFMA tile: 16 x 16 (x 32 for FP16/BF16, x 128 for FP8), which sustains
-  // 10-13% more throughput than the 32 x 32 shapes on the same wave tile
-  // once the chip runs at its power limit (random operands; equal at zero
-  // data); MXFP8 keeps 32 x 32 x 64, whose block-scale lanes are mapped.
-  static constexpr int MT = Op::MX ? 32 : 16;
+  // MFMA tile: 16 x 16 (x 32 for FP16/BF16, x 128 for FP8 and MXFP8), which
+  // sustains 10-13% more throughput than the 32 x 32 shapes on the same wave
+  // tile once the chip runs at its power limit (random operands; equal at
+  // zero data).  The 32 x 32 paths (MT = 32) are kept for comparison.
+  static constexpr int MT = 16;
   static constexpr int KI = E == 2 ? 32 : (MT == 16 ? 128 : Op::KI);  // k per MFMA
   static constexpr int ACC = MT * MT / 64;         // accumulator registers per tile
   using Acc = std::conditional_t<MT == 16, f32x4, f32x16>;
@@ -345,9 +345,9 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
         for (int r = 0; r < Cfg::ACC; ++r) acc[i][j][r] = 0.0f;
   };
   // MX block scales: for the stage in use, lane l holds in scp[i] / scq[j]
-  // the scales of its row of P tile i / Q tile j for k blocks h and h + 2
-  // of the stage in bytes 0 and 2 (a stage is four blocks of 32 k: byte 2kk
-  // serves k-step kk).  Scale group G of a tile (stages 4G .. 4G+3) travels
+  // the scales of its row of P tile i / Q tile j (a stage is four blocks of
+  // 32 k): 16 x 16 tiles, block lg in byte 0; 32 x 32 tiles, blocks h and h + 2
+  // in bytes 0 and 2 (byte 2kk serves k-step kk).  Scale group G of a tile (stages 4G .. 4G+3) travels
   // as one 16-byte copy per row (64 rows per instruction, spread over the
   // waves) into ring buffer gam % 2, gam counting groups along the stream of
   // stages.  The last stage of a group picks (without branching) the group
@@ -386,9 +386,9 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     if constexpr (Op::MX) {
       const char* g0 = sring + buf * Cfg::SG_BYTES + 4 * slot;
 #pragma unroll
-      for (int i = 0; i < TP; ++i) nsp[i] = *(const uint32_t*)(g0 + 16 * (wp * Cfg::WTP + 32 * i + l32));
+      for (int i = 0; i < TP; ++i) nsp[i] = *(const uint32_t*)(g0 + 16 * (wp * Cfg::WTP + MT * i + lr));
 #pragma unroll
-      for (int j = 0; j < TQ; ++j) nsq[j] = *(const uint32_t*)(g0 + 16 * (Cfg::BP + wq * Cfg::WTQ + 32 * j + l32));
+      for (int j = 0; j < TQ; ++j) nsq[j] = *(const uint32_t*)(g0 + 16 * (Cfg::BP + wq * Cfg::WTQ + MT * j + lr));
     }
   };
   // Blocks at or past K/32 read as scale byte 0 (their data are zeros; a
@@ -398,17 +398,20 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       const int64_t valid = K / 32 - 4 * (int64_t)t;
       const uint32_t m = valid >= 4 ? ~0u : (valid <= 0 ? 0u : ((1u << (8 * valid)) - 1u));
 #pragma unroll
-      for (int i = 0; i < TP; ++i) scp[i] = (sp[i] & m) >> (8 * h);
+      for (int i = 0; i < TP; ++i) scp[i] = (sp[i] & m) >> (8 * lg);
 #pragma unroll
-      for (int j = 0; j < TQ; ++j) scq[j] = (sq[j] & m) >> (8 * h);
+      for (int j = 0; j < TQ; ++j) scq[j] = (sq[j] & m) >> (8 * lg);
     }
   };
-  static_assert(!Op::MX || Cfg::KSTEPS == 2, "two k-steps of 64 per stage");
+  static_assert(!Op::MX || Cfg::KSTEPS == 2 || Cfg::ROLL, "MX: two k-steps of 64 or one of 128 per stage");
   auto mfma_one = [&](int set, int t, int kk) {
     const int i = t / TQ, j = t % TQ;
-    if constexpr (Op::MX) {
+    if constexpr (Op::MX && MT == 32) {
       if (kk == 0) acc[i][j] = Op::template mma_mx<0>(fa[set][i], fb[set][j], acc[i][j], scp[i], scq[j]);
       else acc[i][j] = Op::template mma_mx<1>(fa[set][i], fb[set][j], acc[i][j], scp[i], scq[j]);
+    } else if constexpr (Op::MX) {
+      (void)kk;
+      acc[i][j] = Op::mma16_mx(fa[set][i], fb[set][j], acc[i][j], scp[i], scq[j]);
     } else if constexpr (MT == 16) {
       (void)kk;
       acc[i][j] = Op::mma16(fa[set][i], fb[set][j], acc[i][j]);
@@ -423,6 +426,25 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   // the unroller would give up on the larger 16 x 16 schedules.)
   auto first = [](int n, int span, int t) { return (t * n + span - 1) / span; };
   constexpr int LAST = (Cfg::KSTEPS - 1) & 1;
+
+  // MX: when stage s ends group gam, its buffer takes group gam + 2, the
+  // group after the one the next stage opens: the next group of this tile, or
+  // the first or second of the next tile, or the first of the tile after it
+  // (tiles of one group).  Decided without branching; the next stage issues
+  // the copy first thing.
+  auto mx_next = [&](int s, int snext, bool opens, const Src& cu, const Src& nx, const Src& nx2) {
+    if constexpr (Op::MX) {
+      const int Gn = snext / Cfg::SG_STAGES;
+      const bool in_tile = s + 1 < nst;
+      const bool cu_more = (Gn + 1) * Cfg::SG_STAGES < nst;
+      const bool nx_more = Cfg::SG_STAGES < nst;
+      gpend = opens;
+      gpend_buf = gam & 1;
+      gpend_g = in_tile ? (cu_more ? Gn + 1 : 0) : (nx_more ? 1 : 0);
+      gpend_src = in_tile ? (cu_more ? cu : nx) : (nx_more ? nx : nx2);
+      gam += opens ? 1 : 0;
+    }
+  };
 
   // Stream position g + NS (the copies after the barrier of stage g).
   auto pos_far = [&](int s, const Src& cu, const Src& nx) -> Pos {
@@ -446,7 +468,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   // read of buffer g % NS is issued before the barrier, so the copies after
   // it may overwrite that buffer; the next stage's reads come after it, once
   // its data is known to have landed.  Copies as in `stage`.
-  auto stage_roll = [&](int g, int s, const Src& cu, const Src& nx, Pos& p1) {
+  auto stage_roll = [&](int g, int s, const Src& cu, const Src& nx, const Src& nx2, Pos& p1) {
     constexpr int HP = TP / 2, NM1 = Cfg::SLOTS1;
     constexpr int RQ = TQ * FC;                 // reads of the Q fragments
     constexpr int RP = HP * Cfg::PRD;           // reads of half the P fragments
@@ -454,8 +476,13 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     const char* sb = smem + b * Cfg::STAGE;
     char* ob = smem + ((g + 1) & (NS - 1)) * Cfg::STAGE;
     auto mma_ij = [&](int i, int j) {
-      if constexpr (MT == 16) acc[i][j] = Op::mma16(fa[0][i], fb[0][j], acc[i][j]);
+      if constexpr (MT == 16 && Op::MX) acc[i][j] = Op::mma16_mx(fa[0][i], fb[0][j], acc[i][j], scp[i], scq[j]);
+      else if constexpr (MT == 16) acc[i][j] = Op::mma16(fa[0][i], fb[0][j], acc[i][j]);
     };
+    if constexpr (Op::MX) {
+      if (gpend) copy_group(gpend_src, gpend_g, gpend_buf);
+      take_scales(s, nsp, nsq);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < NM1; ++t) {
@@ -469,9 +496,12 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    [[maybe_unused]] const int snext = s + 1 >= nst ? 0 : s + 1;
+    [[maybe_unused]] const bool opens = snext % Cfg::SG_STAGES == 0;
     if constexpr (NS == 2) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     else __builtin_amdgcn_s_waitcnt(kWaitVmcntBase | vmcnt_bits(Cfg::VM_MID));
     __syncthreads();
+    if constexpr (Op::MX) read_scales((gam + (opens ? 1 : 0)) & 1, snext % Cfg::SG_STAGES);
     __builtin_amdgcn_sched_barrier(0);
     const Pos p2 = pos_far(s, cu, nx);
     char* db = smem + b * Cfg::STAGE;
@@ -489,6 +519,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       for (int d = first(NA, NASPAN, u); d < first(NA, NASPAN, u + 1) && d < NA; ++d) copy_d(p2, db, d);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (Op::MX) mx_next(s, snext, opens, cu, nx, nx2);
     p1 = p2;
   };
 
@@ -547,21 +578,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       for (int d = first(NA, NASPAN, t); d < first(NA, NASPAN, t + 1) && d < NA; ++d) copy_d(p2, db, d);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (Op::MX) {
-      // When this stage ends group gam, its buffer takes group gam + 2, the
-      // group after the one the next stage opens: the next group of this
-      // tile, or the first or second of the next tile, or the first of the
-      // tile after it (tiles of one group).
-      const int Gn = snext / Cfg::SG_STAGES;
-      const bool in_tile = s + 1 < nst;
-      const bool cu_more = (Gn + 1) * Cfg::SG_STAGES < nst;
-      const bool nx_more = Cfg::SG_STAGES < nst;
-      gpend = opens;
-      gpend_buf = gam & 1;
-      gpend_g = in_tile ? (cu_more ? Gn + 1 : 0) : (nx_more ? 1 : 0);
-      gpend_src = in_tile ? (cu_more ? cu : nx) : (nx_more ? nx : nx2);
-      gam += opens ? 1 : 0;
-    }
+    if constexpr (Op::MX) mx_next(s, snext, opens, cu, nx, nx2);
     p1 = p2;
   };
 
@@ -652,7 +669,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   for (;;) {
     zero_acc();
     for (int s = 0; s < nst; ++s, ++g) {
-      if constexpr (Cfg::ROLL) stage_roll(g, s, cur, nxt, p1);
+      if constexpr (Cfg::ROLL) stage_roll(g, s, cur, nxt, nx2, p1);
       else stage(g, s, cur, nxt, nx2, p1);
     }
     if constexpr (!PERSIST) break;

@@ -217,7 +217,7 @@ def test_tile_choice(lib, M, N, K, tile16, tile8nn):
             want = tile8nn if dt >= 3 and layout == 0 else tile16
             if dt == 5 and want.endswith("_s4"):
                 want = want[:-3]          # MXFP8 keeps two LDS stages (its scale ring)
-            assert d.endswith(want) or d.endswith(want + "_persistent"), (dt, layout, full)
+            assert d.endswith(want), (dt, layout, full)
             assert " + " not in full, full
 
 
@@ -247,11 +247,11 @@ def test_split_choice(lib, dt, layout, M, N, K, axis, at, tail):
 def test_no_split_when_rounds_are_whole_or_it_does_not_pay(lib, M, N, K):
     for dt in (1, 2, 3):
         assert " + " not in _kernel(lib, dt, 1, M, N, K)
-    # MXFP8 TN at 256 x 256 runs persistent workgroups, a multiple of the 8
-    # XCDs; FP8 (16 x 16 x 128 tiles) one tile per workgroup.
-    assert "persistent" in _kernel(lib, 5, 1, 5120, 5120, 1024)
-    fp8 = _kernel(lib, 3, 1, 5120, 5120, 1024)
-    assert fp8.split()[0] == "fp8_tn_256x256_w4" and "grid=400 " in fp8, fp8
+    # 256 x 256 runs one tile per workgroup for every dtype (16 x 16 MFMA
+    # tiles): the grid is the tile count.
+    for dt, name in ((3, "fp8_tn_256x256_w4"), (5, "mx8_tn_256x256_w4")):
+        k = _kernel(lib, dt, 1, 5120, 5120, 1024)
+        assert k.split()[0] == name and "grid=400 " in k, k
     # K not a whole number of 16-byte chunks: the eight-wave kernel.
     assert "_w4" not in _kernel(lib, 2, 1, 4096, 4096, 4100)
 

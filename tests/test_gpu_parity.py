@@ -80,9 +80,8 @@ def kernel_name(dtype, layout, M, N, K):
 # stages, the latter also with fewer stages than buffers): exactly two stages, an odd stage count with edge
 # tiles (N not a multiple of 8 in NN, so B's rows are padded and the last p
 # tile reads past the row end), a partial last stage, and 400 tiles of
-# 256 x 256, more than the CUs, so the persistent FP8 variant walks several
-# tiles per workgroup with its copy stream crossing tiles (rows sampled),
-# also with a partial last stage (the kernels built with tail masks).
+# 256 x 256, more than the CUs (rows sampled), also with a partial last stage
+# (the kernels built with tail masks).
 @pytest.mark.parametrize("dtype,layout", [(d, l) for d in ("f16", "bf16", "fp8") for l in ("tn", "nn")])
 def test_four_wave_kernel(dtype, layout):
     bk = {"f16": 64, "bf16": 64, "fp8": 128}[dtype]
@@ -99,7 +98,7 @@ def test_four_wave_kernel(dtype, layout):
     for idx, (M, N, K, tile) in enumerate(shapes):
         name = kernel_name(dtype, layout, M, N, K)
         k = name.split()[0]
-        assert k.endswith(tile) or k.endswith(tile + "_persistent"), name
+        assert k.endswith(tile), name
         assert (" + " in name) == (idx >= 8), name
         p = make_problem(dtype, layout, M, N, K, seed=5000 + idx, pad=idx % 2)
         say(f"case w4 {name} M={M} N={N} K={K}")
@@ -273,7 +272,7 @@ def compare_scaled(p, cij, sa, sb, rows=None, exact=False):
 
 
 # Every kernel the FP8 path can pick (the eight-wave kernel for ragged K, the
-# four-wave tiles, the persistent 256 x 256 one with 400 tiles), per-tensor
+# four-wave tiles, 256 x 256 with 400 tiles), per-tensor
 # and per-row factors, K = 0 (C = 0 * factors).  Tolerance relative to
 # |sa_i sb_j| * sum_k |a b|.
 @pytest.mark.parametrize("layout", ["tn", "nn"])
@@ -369,11 +368,10 @@ def compare_mx(p, cij, SA, ldsa, SB, ldsb, rows=None, exact=False):
     return ok, err
 
 
-# Every tile the MXFP8 path picks: one or two stages (K < 256, one tile per
-# workgroup), a partial last stage whose scale dword reaches past K/32, the
-# persistent 256 x 256 kernel with 400 tiles (and with tiles of one scale
-# group, K = 384, whose next-but-one tile's group is copied at tile ends),
-# K = 0, padded scale rows full of NaN codes, launches split along q and p.
+# Every tile the MXFP8 path picks: one or two stages (K < 256), a partial
+# last stage whose scale dword reaches past K/32, 256 x 256 with 400 tiles
+# (and with tiles of one scale group, K = 384), K = 0, padded scale rows full
+# of NaN codes, launches split along q and p.
 # Scales 2^-15 .. 2^15.
 @pytest.mark.parametrize("layout", ["tn", "nn"])
 def test_mxfp8_against_oracle(layout):
