@@ -37,14 +37,13 @@ constexpr int64_t kMaxDescBytes = (int64_t(1) << 31) - 64;
 int in_elem(int dt) { return dt == DT_F32 ? 4 : (is_fp8(dt) ? 1 : 2); }
 int out_elem(int dt) { return (dt == DT_F32 || is_fp8(dt)) ? 4 : 2; }
 
-// A launchable configuration: a kernel symbol plus its tile geometry.
-// Persistent kernels run at most one workgroup per CU and walk the tiles.
+// A launchable configuration: a kernel symbol plus its tile geometry.  Every
+// kernel runs one workgroup per tile.
 struct Launch {
   const void* fn;
   const char* name;
   int bp, bq, threads, lds;
   bool p_trans;
-  bool persistent;
 };
 
 // ---- kernel table ------------------------------------------------------------
@@ -58,23 +57,18 @@ template <class Op, bool PT>
 Launch mfma_launch(const char* name) {
   using Cfg = MfmaCfg<Op, 256, 256, 2, 4, PT>;
   return Launch{(const void*)&gemm_mfma_kernel<Op, 256, 256, 2, 4, PT>, name, 256, 256, Cfg::NT,
-                2 * Cfg::STAGE, PT, false};
+                2 * Cfg::STAGE, PT};
 }
 
-// Four-wave kernel (gemm_tn.hpp), one tile per workgroup.  (With 32 x 32
-// MFMA tiles, 256 x 256 FP8 ran persistently so that each tile's FP32 stores
-// drained under the next tile's stages; on 16 x 16 x 128 tiles the persistent
-// loop spilled inside its stage loop, holding the next tile's state on top of
-// the fragments.)  `kt`: K is
-// not a whole number of stages, so the copies need tail masks (a separate
+// Four-wave kernel (gemm_tn.hpp), one tile per workgroup.  `kt`: K is not a
+// whole number of stages, so the copies need tail masks (a separate
 // instantiation: without a tail they cost nothing).
 template <class Op, bool PKM, int BP, int BQ, int NS = 2>
 Launch tn_launch(const char* name, bool kt) {
   using Cfg = TnCfg<Op, PKM, BP, BQ, NS>;
-  constexpr bool P = Cfg::MT == 32 && Op::ELEM == 1 && BP == 256 && BQ == 256;
-  const void* fn = kt ? (const void*)&gemm_tn_kernel<Op, P, PKM, BP, BQ, NS, true>
-                      : (const void*)&gemm_tn_kernel<Op, P, PKM, BP, BQ, NS, false>;
-  return Launch{fn, name, BP, BQ, Cfg::NT, Cfg::LDS, PKM, P};
+  const void* fn = kt ? (const void*)&gemm_tn_kernel<Op, PKM, BP, BQ, NS, true>
+                      : (const void*)&gemm_tn_kernel<Op, PKM, BP, BQ, NS, false>;
+  return Launch{fn, name, BP, BQ, Cfg::NT, Cfg::LDS, PKM};
 }
 
 // Whether K ends inside a stage of the four-wave kernel (stages of 128 bytes
@@ -155,14 +149,13 @@ Launch tn_make(const char* const names[kNumTiles], int idx, bool kt) {
 template <bool PT>
 Launch f32_launch(const char* name) {
   using Cfg = F32Cfg<128, 128, 2, 2, PT>;
-  return Launch{(const void*)&gemm_f32_kernel<128, 128, 2, 2, PT>, name, 128, 128, Cfg::NT, 2 * Cfg::STAGE, PT,
-                false};
+  return Launch{(const void*)&gemm_f32_kernel<128, 128, 2, 2, PT>, name, 128, 128, Cfg::NT, 2 * Cfg::STAGE, PT};
 }
 
 template <class Op, int PF>
 Launch skinny_launch(const char* name) {
   return Launch{(const void*)&gemm_skinny_kernel<Op, PF>, name, 16 * PF, SkinnyCfg<Op, PF>::BQ, SkinnyCfg<Op, PF>::NT,
-                (int)(sizeof(float) * SkinnyCfg<Op, PF>::NW * 32 * SkinnyCfg<Op, PF>::BQ), false, false};
+                (int)(sizeof(float) * SkinnyCfg<Op, PF>::NW * 32 * SkinnyCfg<Op, PF>::BQ), false};
 }
 
 // Skinny TN problems (at most 32 rows of A) stream B once with a split-K
@@ -429,19 +422,8 @@ int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
   return DGEMM_OK;
 }
 
-// One launch on the caller's stream.  Persistent kernels run one workgroup
-// per CU, rounded down to a multiple of the XCD count so that every tile of
-// a workgroup maps to the workgroup's own XCD.
+// One launch on the caller's stream.
 int launch(const Launch& L, const GemmArgs& g, int64_t grid, void* stream) {
-  if (L.persistent) {
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return hip_failed(e);
-    if (cus <= 0) return hip_failed(hipErrorInvalidValue);
-    if (cus >= kXcds) cus -= cus % kXcds;
-    if (grid > cus) grid = cus;
-  }
   GemmArgs arg = g;
   void* args[] = {(void*)&arg};
   const hipError_t err = hipLaunchKernel(L.fn, dim3((unsigned)grid), dim3(L.threads), args, 0, (hipStream_t)stream);

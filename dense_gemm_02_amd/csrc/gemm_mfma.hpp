@@ -131,23 +131,9 @@ struct OpFP8S : OpFP8 {
 
 // MXFP8: E4M3 operands with one E8M0 scale (2^(e - 127)) per 32 consecutive
 // k of each row of A and each column of B, as the block scales of the
-// scaled MFMA take them.  That instruction splits its 64 k into two blocks
-// of 32: lane l (h = l / 32) holds row l % 32 with k 16h .. 16h + 15 in
-// bytes 0-15 and k 32 + 16h .. 32 + 16h + 15 in bytes 16-31, and the scale
-// in lane l applies to k block h of row l % 32 (determined on gfx950 with
-// one-hot operands: every byte position, its output row, its partner in the
-// other operand and the lane whose scale it takes).  opsel picks the byte of
-// the 32-bit scale register.
+// scaled MFMA take them.
 struct OpMX8 : OpFP8 {
   static constexpr bool MX = true;
-  template <int KK>
-  __device__ static f32x16 mma_mx(const u32x4 (&a)[2], const u32x4 (&b)[2], f32x16 c, uint32_t sa, uint32_t sb) {
-    const i32x8 av = __builtin_shufflevector(__builtin_bit_cast(i32x4, a[0]), __builtin_bit_cast(i32x4, a[1]), 0, 1,
-                                             2, 3, 4, 5, 6, 7);
-    const i32x8 bv = __builtin_shufflevector(__builtin_bit_cast(i32x4, b[0]), __builtin_bit_cast(i32x4, b[1]), 0, 1,
-                                             2, 3, 4, 5, 6, 7);
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 2 * KK, (int)sa, 2 * KK, (int)sb);
-  }
   // 16 x 16 x 128 with block scales.  Lane group L = l / 16 holds bytes 0-15
   // and 16-31 of its row; the instruction's four blocks of 32 k are {groups
   // 0, 1} x bytes 0-15, {2, 3} x bytes 0-15, {0, 1} x bytes 16-31 and {2, 3} x

@@ -1,21 +1,17 @@
-// Persistent TN GEMM for 16-bit and 8-bit operands on gfx950: four waves,
-// one per SIMD, each owning a 128 x 128 quarter of a 256 x 256 tile.
+// TN (and NN) GEMM for 16-bit and 8-bit operands on gfx950: four waves, one
+// per SIMD, each owning a quarter of the block tile (128 x 128 of 256 x 256)
+// as 16 x 16 MFMA tiles.
 //
 // Same operation and P/Q/D mapping as gemm_mfma.hpp (D[p][q] = sum_k
-// P(p,k) Q(q,k), stored at C[q*ldc + p]), for K-contiguous P and Q, K a whole
+// P(p,k) Q(q,k), stored at C[q*ldc + p]), for K-contiguous Q, K a whole
 // number of 16-byte chunks and at least two stages.  Differences:
 //
-//  * 128 x 128 wave tiles read 0.5 KiB of LDS per 32x32 MFMA instead of 0.75
-//    for the eight-wave 128 x 64 split, and one wave per SIMD leaves all 512
-//    registers to it (accumulators in AGPRs).
-//  * The grid is one workgroup per CU; each walks tiles blockIdx.x,
-//    blockIdx.x + gridDim.x, ...  The copy stream runs on across tiles: the
-//    last stages of a tile already copy and read the first stages of the next
-//    one, so a tile's epilogue stores drain while the next tile computes, and
-//    no tile starts with an exposed copy latency.  (With the grid a multiple
-//    of 8, every tile of a workgroup lies on the workgroup's XCD.)
-//  * Copies of a stage are split: NA go out right after the barrier two
-//    stages ahead, the other NDMA - NA over the first KB k-steps of the stage
+//  * 128 x 128 wave tiles read half as much LDS per flop as the eight-wave
+//    128 x 64 split, and one wave per SIMD leaves all 512 registers to it
+//    (accumulators in AGPRs).
+//  * One tile per workgroup; tiles follow the XCD-aware order of tile_map.
+//  * Copies of a stage are split: NA go out after the barrier two stages
+//    ahead, the other NDMA - NA over the first NBSPAN MFMA slots of the stage
 //    before, so the texture unit sees them spread out.
 //  * NS LDS stages: with NS > 2 (small tiles, one workgroup per CU) every
 //    copy goes out NS stages ahead, so a stage's copy latency hides behind
@@ -54,11 +50,11 @@ struct TnCfg {
   // MFMA tile: 16 x 16 (x 32 for FP16/BF16, x 128 for FP8 and MXFP8), which
   // sustains 10-13% more throughput than the 32 x 32 shapes on the same wave
   // tile once the chip runs at its power limit (random operands; equal at
-  // zero data).  The 32 x 32 paths (MT = 32) are kept for comparison.
+  // zero data).
   static constexpr int MT = 16;
-  static constexpr int KI = E == 2 ? 32 : (MT == 16 ? 128 : Op::KI);  // k per MFMA
+  static constexpr int KI = E == 2 ? 32 : 128;    // k per MFMA
   static constexpr int ACC = MT * MT / 64;         // accumulator registers per tile
-  using Acc = std::conditional_t<MT == 16, f32x4, f32x16>;
+  using Acc = f32x4;
   static constexpr int TP = WTP / MT, TQ = WTQ / MT;
   static constexpr int KSTEPS = BK / KI;
   static constexpr int CPK = KI * E / 16;          // 16-byte chunks of k per k-step
@@ -69,15 +65,17 @@ struct TnCfg {
   // refilled with the next stage's data right after its last use.
   static constexpr bool ROLL = KSTEPS == 1;
   static_assert(!ROLL || TP % 2 == 0, "two halves of P tiles");
+  static_assert(!Op::MX || ROLL, "MX block scales follow the 16 x 16 x 128 stage");
   // LDS reads per k-step: 16-byte reads of Q fragments, and of P fragments
   // either 16-byte reads (K-contiguous P) or twice as many 8-byte
   // transposing reads (p-contiguous P).
   static constexpr int PRD = PKM ? 2 * FC : FC;   // reads per P fragment
   static constexpr int NREAD = TQ * FC + TP * PRD;
   // p-contiguous P: LDS rows of k, BP*E bytes, in units of 32 p (UB bytes)
-  // XOR-swizzled by a key of k below KEYM: k mod 8 (FP8), or for 16-bit
-  // (k mod 4) ^ 2 ((k / 8) mod 2), so that the 16 x 16 fragment's lane groups
-  // 0 and 1, which read k rows eight apart, meet different banks.
+  // XOR-swizzled by a key of k below KEYM: (k mod 8) ^ 4 ((k / 16) mod 2)
+  // (FP8) or (k mod 4) ^ 2 ((k / 8) mod 2) (16-bit), so that the fragment's
+  // lane groups 0 and 1, which read k rows sixteen (eight) apart, meet
+  // different banks.
   static constexpr int PROWB = BP * E;            // bytes of one LDS row of P (one k)
   static constexpr int UB = 32 * E;
   static constexpr int KEYM = 256 / UB;
@@ -104,11 +102,10 @@ struct TnCfg {
   // NS - 2 later stream positions.
   static constexpr int VM_MID = (NS - 2) * NDMA;
   static_assert(!PKM || (PROWB / UB) % KEYM == 0, "swizzle keys stay within a row of P");
-  // FP8 16 x 16: lane groups 0 and 1 read k rows sixteen apart.
+  // FP8: lane groups 0 and 1 read k rows sixteen apart.
   __device__ static int pkey(int k) {
     if constexpr (E == 2) return (k & 3) ^ (((k >> 3) & 1) << 1);
-    else if constexpr (MT == 16) return (k & 7) ^ (((k >> 4) & 1) << 2);
-    else return k & (KEYM - 1);
+    else return (k & 7) ^ (((k >> 4) & 1) << 2);
   }
   // The LDS-staged epilogue needs 256-byte staged rows; smaller wave tiles
   // store straight from the accumulators.
@@ -118,7 +115,7 @@ struct TnCfg {
   static constexpr int WPE = TP * TQ * ACC <= 64 && NS == 2 ? 2 : 1;
 };
 
-template <class Op, bool PERSIST, bool PKM, int BP, int BQ, int NS, bool KT>
+template <class Op, bool PKM, int BP, int BQ, int NS, bool KT>
 __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   using Cfg = TnCfg<Op, PKM, BP, BQ, NS>;
   constexpr int NW = Cfg::NW, E = Cfg::E, FC = Cfg::FC, ROWB = Cfg::ROWB, BK = Cfg::BK, CPE = Cfg::CPE;
@@ -274,7 +271,6 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   // ---- fragments and MFMAs ----
   // A lane holds row lr = lane % MT of its P and Q fragments; its lane group
   // lg = lane / MT selects the k it holds.
-  const int l32 = lane & 31, h = lane >> 5;
   const int lr = lane % MT, lg = lane / MT;
   const int sw_r = (lr >> 1) & 7;                // swizzle key of every fragment row of this lane
   const uint32_t pf_base = (uint32_t)((wp * Cfg::WTP + lr) * ROWB);
@@ -295,9 +291,9 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       const int rr = isb ? r : r - TQ * FC;
       const int tile = rr / FC, f = rr % FC;
       // 16-byte chunk kk*CPK + f*(CPK/FC) + lg of the stage row: 16-bit lane
-      // group lg takes the lg-th 8 k of the step; for FP8, lane half h takes
-      // chunks h and h + 2 of each 64-k step (the k order of the MFMA's two
-      // scale blocks, see OpMX8).
+      // group lg takes the lg-th 8 k of the step; FP8 lane group lg takes
+      // chunks lg and lg + 4 (16 k each) of its 128-k step, which puts the
+      // MFMA's scale block L on the L-th 32 k (see OpMX8).
       const uint32_t off = (uint32_t)(((kk * CPK + f * (CPK / FC) + lg) ^ sw_r) << 4);
       const char* base = sb + (isb ? qf_base : pf_base) + tile * MT * ROWB;
       const u32x4 v = *(const u32x4*)(base + off);
@@ -307,17 +303,11 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       const int tile = rr / Cfg::PRD, q8 = rr % Cfg::PRD;   // which 8-byte piece of the fragment
       // k of this lane's row: the k-step, the lane group, the piece q8 (TRK
       // k each) and tkey, in the order of the K-contiguous reads of Q.
-      // 16-bit (16 x 16): group tg holds k 8tg .. 8tg+7 of the step.  FP8
-      // 16 x 16: group tg holds k 16tg .. 16tg+15 in pieces 0-1 and k 64+16tg
-      // .. in pieces 2-3.  FP8 32 x 32: the lane half h = tg / 2 holds k
-      // 16h .. 16h+15 in pieces 0-1 and k 32+16h .. in pieces 2-3 (the k
-      // order of the MFMA's scale blocks, see OpMX8), and tg % 2 picks the 16
-      // p of the tile.
-      int krow;
-      if constexpr (E == 2) krow = kk * KI + tg * 8 + q8 * TRK + tkey;
-      else if constexpr (MT == 16) krow = kk * KI + (q8 >> 1) * 64 + tg * 16 + (q8 & 1) * 8 + tkey;
-      else krow = kk * KI + (q8 >> 1) * 32 + (tg >> 1) * 16 + (q8 & 1) * 8 + tkey;
-      const int pbyte = (wp * Cfg::WTP + tile * MT) * E + (MT == 16 ? 0 : (tg & 1) * (16 * E));
+      // 16-bit: group tg holds k 8tg .. 8tg+7 of the step.  FP8: group tg
+      // holds k 16tg .. 16tg+15 in pieces 0-1 and k 64+16tg .. in pieces 2-3.
+      const int krow = E == 2 ? kk * KI + tg * 8 + q8 * TRK + tkey
+                              : kk * KI + (q8 >> 1) * 64 + tg * 16 + (q8 & 1) * 8 + tkey;
+      const int pbyte = (wp * Cfg::WTP + tile * MT) * E;
       const int unit = (pbyte / Cfg::UB) ^ Cfg::pkey(krow);
       const char* src = sb + krow * Cfg::PROWB + unit * Cfg::UB + pbyte % Cfg::UB + (ts % (2 * E)) * 8;
       typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -345,9 +335,8 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
         for (int r = 0; r < Cfg::ACC; ++r) acc[i][j][r] = 0.0f;
   };
   // MX block scales: for the stage in use, lane l holds in scp[i] / scq[j]
-  // the scales of its row of P tile i / Q tile j (a stage is four blocks of
-  // 32 k): 16 x 16 tiles, block lg in byte 0; 32 x 32 tiles, blocks h and h + 2
-  // in bytes 0 and 2 (byte 2kk serves k-step kk).  Scale group G of a tile (stages 4G .. 4G+3) travels
+  // the scale of its row of P tile i / Q tile j for block lg of the stage (a
+  // stage is four blocks of 32 k), in byte 0.  Scale group G of a tile (stages 4G .. 4G+3) travels
   // as one 16-byte copy per row (64 rows per instruction, spread over the
   // waves) into ring buffer gam % 2, gam counting groups along the stream of
   // stages.  The last stage of a group picks (without branching) the group
@@ -403,22 +392,9 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       for (int j = 0; j < TQ; ++j) scq[j] = (sq[j] & m) >> (8 * lg);
     }
   };
-  static_assert(!Op::MX || Cfg::KSTEPS == 2 || Cfg::ROLL, "MX: two k-steps of 64 or one of 128 per stage");
-  auto mfma_one = [&](int set, int t, int kk) {
+  auto mfma_one = [&](int set, int t) {
     const int i = t / TQ, j = t % TQ;
-    if constexpr (Op::MX && MT == 32) {
-      if (kk == 0) acc[i][j] = Op::template mma_mx<0>(fa[set][i], fb[set][j], acc[i][j], scp[i], scq[j]);
-      else acc[i][j] = Op::template mma_mx<1>(fa[set][i], fb[set][j], acc[i][j], scp[i], scq[j]);
-    } else if constexpr (Op::MX) {
-      (void)kk;
-      acc[i][j] = Op::mma16_mx(fa[set][i], fb[set][j], acc[i][j], scp[i], scq[j]);
-    } else if constexpr (MT == 16) {
-      (void)kk;
-      acc[i][j] = Op::mma16(fa[set][i], fb[set][j], acc[i][j]);
-    } else {
-      (void)kk;
-      acc[i][j] = Op::mma_parts(fa[set][i], fb[set][j], acc[i][j]);
-    }
+    if constexpr (!Op::MX) acc[i][j] = Op::mma16(fa[set][i], fb[set][j], acc[i][j]);
   };
   // n operations spread over `span` MFMA slots: operation i goes out after
   // MFMA i * span / n, so slot t issues i in [first(n, span, t),
@@ -428,35 +404,23 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   constexpr int LAST = (Cfg::KSTEPS - 1) & 1;
 
   // MX: when stage s ends group gam, its buffer takes group gam + 2, the
-  // group after the one the next stage opens: the next group of this tile, or
-  // the first or second of the next tile, or the first of the tile after it
-  // (tiles of one group).  Decided without branching; the next stage issues
-  // the copy first thing.
-  auto mx_next = [&](int s, int snext, bool opens, const Src& cu, const Src& nx, const Src& nx2) {
+  // group after the one the next stage opens, if the tile has it (else the
+  // copy reads zeros from `none`).  Decided without branching; the next stage
+  // issues the copy first thing.
+  auto mx_next = [&](int s, int snext, bool opens, const Src& cu, const Src& none) {
     if constexpr (Op::MX) {
       const int Gn = snext / Cfg::SG_STAGES;
-      const bool in_tile = s + 1 < nst;
-      const bool cu_more = (Gn + 1) * Cfg::SG_STAGES < nst;
-      const bool nx_more = Cfg::SG_STAGES < nst;
+      const bool more = s + 1 < nst && (Gn + 1) * Cfg::SG_STAGES < nst;
       gpend = opens;
       gpend_buf = gam & 1;
-      gpend_g = in_tile ? (cu_more ? Gn + 1 : 0) : (nx_more ? 1 : 0);
-      gpend_src = in_tile ? (cu_more ? cu : nx) : (nx_more ? nx : nx2);
+      gpend_g = Gn + 1;
+      gpend_src = more ? cu : none;
       gam += opens ? 1 : 0;
     }
   };
 
   // Stream position g + NS (the copies after the barrier of stage g).
-  auto pos_far = [&](int s, const Src& cu, const Src& nx) -> Pos {
-    if constexpr (PERSIST) {
-      const bool n2 = s + NS >= nst;
-      const Src& src = n2 ? nx : cu;
-      return pos_at(src, n2 ? s + NS - nst : s + NS, src.qn != 0);
-    } else {
-      (void)nx;
-      return pos_at(cu, s + NS, s + NS < nst);
-    }
-  };
+  auto pos_far = [&](int s, const Src& cu) -> Pos { return pos_at(cu, s + NS, s + NS < nst); };
 
   // ---- one stage, rolling (one k-step per stage) ----
   // Phase 1, before the barrier: P tiles 0 .. HP-1 against every Q tile,
@@ -468,7 +432,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   // read of buffer g % NS is issued before the barrier, so the copies after
   // it may overwrite that buffer; the next stage's reads come after it, once
   // its data is known to have landed.  Copies as in `stage`.
-  auto stage_roll = [&](int g, int s, const Src& cu, const Src& nx, const Src& nx2, Pos& p1) {
+  auto stage_roll = [&](int g, int s, const Src& cu, const Src& none, Pos& p1) {
     constexpr int HP = TP / 2, NM1 = Cfg::SLOTS1;
     constexpr int RQ = TQ * FC;                 // reads of the Q fragments
     constexpr int RP = HP * Cfg::PRD;           // reads of half the P fragments
@@ -476,8 +440,8 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     const char* sb = smem + b * Cfg::STAGE;
     char* ob = smem + ((g + 1) & (NS - 1)) * Cfg::STAGE;
     auto mma_ij = [&](int i, int j) {
-      if constexpr (MT == 16 && Op::MX) acc[i][j] = Op::mma16_mx(fa[0][i], fb[0][j], acc[i][j], scp[i], scq[j]);
-      else if constexpr (MT == 16) acc[i][j] = Op::mma16(fa[0][i], fb[0][j], acc[i][j]);
+      if constexpr (Op::MX) acc[i][j] = Op::mma16_mx(fa[0][i], fb[0][j], acc[i][j], scp[i], scq[j]);
+      else acc[i][j] = Op::mma16(fa[0][i], fb[0][j], acc[i][j]);
     };
     if constexpr (Op::MX) {
       if (gpend) copy_group(gpend_src, gpend_g, gpend_buf);
@@ -501,9 +465,11 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     if constexpr (NS == 2) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     else __builtin_amdgcn_s_waitcnt(kWaitVmcntBase | vmcnt_bits(Cfg::VM_MID));
     __syncthreads();
+    // MX: the next stage's scales, first of the reads: it opens a group (its
+    // tile's stage 0 or a multiple of four) or continues this one.
     if constexpr (Op::MX) read_scales((gam + (opens ? 1 : 0)) & 1, snext % Cfg::SG_STAGES);
     __builtin_amdgcn_sched_barrier(0);
-    const Pos p2 = pos_far(s, cu, nx);
+    const Pos p2 = pos_far(s, cu);
     char* db = smem + b * Cfg::STAGE;
 #pragma unroll
     for (int u = 0; u < NM1; ++u) {
@@ -519,33 +485,27 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       for (int d = first(NA, NASPAN, u); d < first(NA, NASPAN, u + 1) && d < NA; ++d) copy_d(p2, db, d);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (Op::MX) mx_next(s, snext, opens, cu, nx, nx2);
+    if constexpr (Op::MX) mx_next(s, snext, opens, cu, none);
     p1 = p2;
   };
 
-  // ---- one stage ----
+  // ---- one stage (FP16/BF16: two or more k-steps) ----
   // Global stage g (buffer g % NS) is stage s of the current tile.  Copies
   // issued here belong to the stream position g + NS (after the barrier; NA
-  // of them) and g + 1 (before it; NB of them, two stages only), which may
-  // already be stages of the next tile `nx` (persistent launches have
-  // nst >= NS; with one tile per workgroup, positions past the tile read
-  // zeros).  `p1` holds position g + 1 on entry and g + NS on return: with
-  // two stages that is the next stage's g + 1.
-  auto stage = [&](int g, int s, const Src& cu, const Src& nx, const Src& nx2, Pos& p1) {
+  // of them) and g + 1 (before it; NB of them, two stages only); positions
+  // past the tile read zeros.  `p1` holds position g + 1 on entry and g + NS
+  // on return: with two stages that is the next stage's g + 1.
+  auto stage = [&](int g, int s, const Src& cu, Pos& p1) {
     const int b = g & (NS - 1);
     const char* sb = smem + b * Cfg::STAGE;
     char* ob = smem + ((g + 1) & (NS - 1)) * Cfg::STAGE;
-    if constexpr (Op::MX) {
-      if (gpend) copy_group(gpend_src, gpend_g, gpend_buf);
-      take_scales(s, nsp, nsq);
-    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk + 1 < Cfg::KSTEPS; ++kk) {
       const int span = kk + 2 == Cfg::KSTEPS ? NMFMA / 2 : NMFMA;
 #pragma unroll
       for (int t = 0; t < NMFMA; ++t) {
-        mfma_one(kk & 1, t, kk);
+        mfma_one(kk & 1, t);
 #pragma unroll
         for (int r = first(NREAD, span, t); r < first(NREAD, span, t + 1); ++r) read_one(sb, kk + 1, (kk + 1) & 1, r);
         if constexpr (NB > 0) {
@@ -557,46 +517,37 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       }
     }
     // Stream position g + 1 has landed (later positions may still be in flight).
-    [[maybe_unused]] const int snext = s + 1 >= nst ? 0 : s + 1;
-    [[maybe_unused]] const bool opens = snext % Cfg::SG_STAGES == 0;
     if constexpr (NS == 2) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     else __builtin_amdgcn_s_waitcnt(kWaitVmcntBase | vmcnt_bits(Cfg::VM_MID));
     __syncthreads();
-    // MX: the next stage's scales, first of the reads: it opens a group (its
-    // tile's stage 0 or a multiple of four) or continues this one.
-    if constexpr (Op::MX) read_scales((gam + (opens ? 1 : 0)) & 1, snext % Cfg::SG_STAGES);
     __builtin_amdgcn_sched_barrier(0);
     // stream position g + NS
-    const Pos p2 = pos_far(s, cu, nx);
+    const Pos p2 = pos_far(s, cu);
     char* db = smem + b * Cfg::STAGE;
 #pragma unroll
     for (int t = 0; t < NMFMA; ++t) {
-      mfma_one(LAST, t, Cfg::KSTEPS - 1);
+      mfma_one(LAST, t);
 #pragma unroll
       for (int r = first(NREAD, NMFMA, t); r < first(NREAD, NMFMA, t + 1); ++r) read_one(ob, 0, 0, r);
 #pragma unroll
       for (int d = first(NA, NASPAN, t); d < first(NA, NASPAN, t + 1) && d < NA; ++d) copy_d(p2, db, d);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (Op::MX) mx_next(s, snext, opens, cu, nx, nx2);
     p1 = p2;
   };
 
   // ---- tiles ----
-  int64_t tile = blockIdx.x;
+  const int64_t tile = blockIdx.x;
   if (tile >= ntiles) return;
-  const int64_t step = PERSIST ? (int64_t)gridDim.x : ntiles;
-  Src cur = tile_src(tile);
-  Src nxt = tile_src(tile + step);
-  // MX with one scale group per tile copies groups two tiles ahead.
-  [[maybe_unused]] Src nx2{};
-  if constexpr (Op::MX) nx2 = tile_src(tile + 2 * step);
+  const Src cur = tile_src(tile);
+  // A source with empty descriptors (its copies read zeros): MX scale
+  // groups past the tile's last.
+  [[maybe_unused]] const Src none = tile_src(ntiles);
   Pos p1;   // the stream position after the current stage's
   {
-    // Prologue: stream positions 0 .. NS-1, all of this tile (persistent
-    // launches have nst >= NS; with one workgroup per tile and nst < NS the
-    // later positions read zeros that nothing uses), without the part-B
-    // copies of position 1, which stage 0 issues.
+    // Prologue: stream positions 0 .. NS-1 (with nst < NS the later ones
+    // read zeros that nothing uses), without the part-B copies of position 1,
+    // which stage 0 issues.
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
       const Pos ps = pos_at(cur, t, t < nst);
@@ -608,7 +559,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
         // the wait below leaves open.
         copy_group(cur, 0, 0);
         if (Cfg::SG_STAGES < nst) copy_group(cur, 1, 1);
-        else copy_group(nxt, 0, 1);
+        else copy_group(none, 0, 1);
       }
     }
     // Position 0 has landed once at most the copies of positions 1 .. NS-1
@@ -655,7 +606,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
           // straight from the accumulator registers, they led the register
           // allocator to give most MFMAs of the loop a separate destination
           // and copy every accumulator each stage.)
-          if constexpr (MT == 16) asm("" : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3));
+          asm("" : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3));
           if constexpr (Op::SCALED) sc.apply(fp[gg], j, v0, v1, v2, v3);
           store4<Op>(a, q, p, v0, v1, v2, v3);
         }
@@ -665,52 +616,35 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
       if constexpr (Op::SCALED) __builtin_amdgcn_sched_barrier(0);
     }
   };
-  int g = 0;
-  for (;;) {
-    zero_acc();
-    for (int s = 0; s < nst; ++s, ++g) {
-      if constexpr (Cfg::ROLL) stage_roll(g, s, cur, nxt, nx2, p1);
-      else stage(g, s, cur, nxt, nx2, p1);
-    }
-    if constexpr (!PERSIST) break;
-    // Persistent: the stores drain while the next tile's stages (already
-    // copied) run.
-    direct_epilogue(tile);
-    tile += step;
-    if (tile >= ntiles) break;
-    cur = nxt;
-    if constexpr (Op::MX) {
-      nxt = nx2;
-      nx2 = tile_src(tile + 2 * step);
-    } else {
-      nxt = tile_src(tile + step);
-    }
+  zero_acc();
+  for (int s = 0; s < nst; ++s) {
+    if constexpr (Cfg::ROLL) stage_roll(s, s, cur, none, p1);
+    else stage(s, s, cur, p1);
   }
-  // Copies issued past the last tile read zeros; let them land before exit.
+  // Copies issued past the tile read zeros; let them land before the LDS is
+  // reused and before exit.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  if constexpr (!PERSIST) {
-    if constexpr (Cfg::STAGED_EPI) {
-      // One tile per workgroup: the stage buffers are free for an LDS-staged
-      // epilogue once every wave is past its last read.
-      __syncthreads();
-      int64_t tp, tq;
-      tile_map(a.tiles_p, a.tiles_q, a.group, tile, &tp, &tq);
-      static_assert(!Cfg::STAGED_EPI || Cfg::WTQ * 256 * NW <= 2 * Cfg::STAGE, "staging fits in the stage buffers");
-      staged_epilogue<Op, Cfg::WTP, Cfg::WTQ, TP, TQ, MT, Acc>(a, smem + wave_u * (Cfg::WTQ * 256), acc, lane,
-                                                       tp * Cfg::BP + wp * Cfg::WTP, tq * Cfg::BQ + wq * Cfg::WTQ);
-    } else {
-      direct_epilogue(tile);
-    }
+  if constexpr (Cfg::STAGED_EPI) {
+    // The stage buffers are free for an LDS-staged epilogue once every wave
+    // is past its last read.
+    __syncthreads();
+    int64_t tp, tq;
+    tile_map(a.tiles_p, a.tiles_q, a.group, tile, &tp, &tq);
+    static_assert(!Cfg::STAGED_EPI || Cfg::WTQ * 256 * NW <= 2 * Cfg::STAGE, "staging fits in the stage buffers");
+    staged_epilogue<Op, Cfg::WTP, Cfg::WTQ, TP, TQ, MT, Acc>(a, smem + wave_u * (Cfg::WTQ * 256), acc, lane,
+                                                             tp * Cfg::BP + wp * Cfg::WTP, tq * Cfg::BQ + wq * Cfg::WTQ);
+  } else {
+    direct_epilogue(tile);
   }
 }
 
 // KT: some stage ends inside K (K not a multiple of the stage depth), so
 // the copies carry per-lane tail masks.
-template <class Op, bool PERSIST, bool PKM, int BP, int BQ, int NS, bool KT>
+template <class Op, bool PKM, int BP, int BQ, int NS, bool KT>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(TnCfg<Op, PKM, BP, BQ, NS>::WPE, TnCfg<Op, PKM, BP, BQ, NS>::WPE)))
 gemm_tn_kernel(const GemmArgs a) {
-  gemm_tn_body<Op, PERSIST, PKM, BP, BQ, NS, KT>(a);
+  gemm_tn_body<Op, PKM, BP, BQ, NS, KT>(a);
 }
 
 }  // namespace dg
