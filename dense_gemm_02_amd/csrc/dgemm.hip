@@ -155,7 +155,7 @@ Launch f32_launch(const char* name) {
 template <class Op, int PF>
 Launch skinny_launch(const char* name) {
   return Launch{(const void*)&gemm_skinny_kernel<Op, PF>, name, 16 * PF, SkinnyCfg<Op, PF>::BQ, SkinnyCfg<Op, PF>::NT,
-                (int)(sizeof(float) * SkinnyCfg<Op, PF>::NW * 32 * SkinnyCfg<Op, PF>::BQ), false};
+                (int)(16 * SkinnyCfg<Op, PF>::NW * PF * SkinnyCfg<Op, PF>::QF * 64), false};
 }
 
 // Skinny TN problems (at most 32 rows of A) stream B once with a split-K

@@ -13,8 +13,9 @@
 //    enough bytes are outstanding to cover HBM latency;
 //  * multiplies with v_mfma_f32_16x16x32_{f16,bf16}: 16 rows of A per MFMA,
 //    which is exactly the skinny extent (the matrix pipe is far from busy);
-//  * reduces the 8 waves' partial sums through LDS and stores C with the
-//    round-to-nearest-even convert.
+//  * reduces the 8 waves' partial sums through LDS, parked in register
+//    layout, and stores four consecutive elements of a column of C at once
+//    with the round-to-nearest-even convert.
 // Rows of A past M and rows of B past N read zero through the buffer
 // descriptors' num_records; k past K is pushed out of range, and a 16-byte
 // chunk straddling K is masked in registers.
@@ -66,8 +67,11 @@ gemm_skinny_kernel(const GemmArgs a) {
   constexpr int NW = Cfg::NW, BQ = Cfg::BQ, QF = Cfg::QF, KS = Cfg::KS, DEPTH = Cfg::DEPTH, E = Cfg::E;
   constexpr int LPS = Cfg::LPS, CPE = 16 / E;
 
-  __shared__ __attribute__((aligned(16))) float red[NW][32][BQ];
+  // Partial sums of every wave, tile and lane: one 16-byte slot per lane,
+  // so each wave's writes and each summing thread's reads are contiguous.
+  __shared__ f32x4v red[NW][PF * QF][64];
   static_assert(BQ % 16 == 0, "whole 16-wide q tiles");
+  static_assert(PF * QF * 64 <= NW * 64, "one summing thread per tile lane");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -145,25 +149,21 @@ gemm_skinny_kernel(const GemmArgs a) {
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // Cross-wave reduction.  16x16 accumulator layout: lane l holds column
-  // (l % 16) and rows 4*(l/16) .. 4*(l/16)+3.
+  // (l % 16) and rows 4*(l/16) .. 4*(l/16)+3, four consecutive elements of
+  // a column of C.  Thread (t, l) sums lane l of tile t over the waves, in
+  // wave order, and stores those four elements.
 #pragma unroll
   for (int i = 0; i < PF; ++i)
 #pragma unroll
-    for (int j = 0; j < QF; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) red[wave_u][16 * i + 4 * kg + r][16 * j + r16] = acc[i][j][r];
+    for (int j = 0; j < QF; ++j) red[wave_u][i * QF + j][lane] = acc[i][j];
   __syncthreads();
-  // The threads sweep the 32 x BQ (p, q) block; p is the fast index so a
-  // column of C is written contiguously.
+  if (tid < PF * QF * 64) {
+    const int t = tid >> 6;
+    const int64_t p = 16 * (t / QF) + 4 * kg, q = q0 + 16 * (t % QF) + r16;
+    f32x4v s = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int e = tid; e < 32 * BQ; e += Cfg::NT) {
-    const int p = e & 31, q = e >> 5;
-    if (p >= a.Pn || q0 + q >= a.Qn) continue;
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) s += red[w][p][q];
-    uint16_t* c = (uint16_t*)a.C + (q0 + q) * a.ldc + p;
-    *c = Op::one(s);
+    for (int w = 0; w < NW; ++w) s += red[w][t][lane];
+    if (q < a.Qn) store4<Op>(a, q, p, s[0], s[1], s[2], s[3]);
   }
 }
 
