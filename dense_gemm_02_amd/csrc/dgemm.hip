@@ -89,6 +89,15 @@ bool k_tail(int dt, int64_t K) { return K % (128 / in_elem(dt)) != 0; }
 // 1536 x 1536 x 8192: 586 against 453), with more rounds it loses (bf16
 // 4352 x 4352 x 1024: 550 against 649; 8192^3 forced: 926 against 1012).
 // Its rate is the one measured at one round.
+// 192 x 256 (16-bit TN: wave tile 96 x 128, direct epilogue) fills a round
+// where 256 x 256 leaves CUs idle: bf16 3072 x 4096 x 8192 has 192 tiles of
+// 256 x 256 and 256 of 192 x 256 (1152 -> 1256 TF/s; 1536 x 8192 x 8192
+// 1274 -> 1383); over whole rounds it runs at 0.87 of 256 x 256 (bf16
+// 6144 x 8192 x 8192: 1302 against 1495).  It is offered from K = 4096 on:
+// at short K its direct epilogue weighs more, and as the second launch of a
+// split it lost (bf16 5120 x 5120 x 1024: 915 against 959; 4352 x 6144 x
+// 1024: 933 against 989), while at K = 4096 and up it won (3072 x 4096:
+// +10%, 6144 x 6144: +2%, 3584 x 8192 x 8192 as a split: +1-2%).
 // The choice minimises ceil(tiles / slots) * tile work / rate, i.e. the
 // number of rounds of workgroups times the time of one round ("FP16 GEMM
 // Optimization on AMD RDNA 3 and RDNA 4", Where That Leaves Us: no single
@@ -98,9 +107,12 @@ struct TileChoice {
   double rate;          // CU throughput relative to 256 x 256
   int max_rounds;       // 0: any number of rounds
 };
-constexpr int kNumTiles = 4;
-constexpr TileChoice kTiles[kNumTiles] = {
-    {256, 256, 1, 1.00, 0}, {256, 128, 1, 0.76, 0}, {128, 128, 2, 0.78, 0}, {128, 128, 1, 0.47, 1}};
+constexpr int kNumTiles = 5;
+constexpr TileChoice kTiles[kNumTiles] = {{256, 256, 1, 1.00, 0},
+                                          {256, 128, 1, 0.76, 0},
+                                          {128, 128, 2, 0.78, 0},
+                                          {128, 128, 1, 0.47, 1},
+                                          {192, 256, 1, 0.87, 0}};
 constexpr int kPlanCus = 256;  // MI355X CUs, for the tile choice only
 
 int pick_tile(int64_t Pn, int64_t Qn, unsigned allowed, double* cost = nullptr) {
@@ -123,9 +135,10 @@ int pick_tile(int64_t Pn, int64_t Qn, unsigned allowed, double* cost = nullptr) 
 // Tiles a four-wave variant allows: p-contiguous FP8 P keeps 256-wide rows
 // (the transposing-read swizzle needs eight 32-byte units per row).
 // MXFP8's scale ring needs two LDS stages, so it leaves out the four-stage
-// tile.
-unsigned tile_mask(int dt, bool nn) {
+// tile.  192 x 256 is built for 16-bit TN only (where it was measured).
+unsigned tile_mask(int dt, bool nn, int64_t K) {
   if (nn && is_fp8(dt)) return 0b0011u;
+  if (!nn && (dt == DT_F16 || dt == DT_BF16) && K >= 4096) return 0b11101u;
   return dt == DT_MX8 ? 0b0101u : 0b1101u;
 }
 
@@ -137,6 +150,9 @@ Launch tn_make(const char* const names[kNumTiles], int idx, bool kt) {
     return tn_launch<Op, PKM, 256, 256>(names[0], kt);
   } else {
     switch (idx) {
+      case 4:
+        if constexpr (Op::ELEM == 2 && !PKM) return tn_launch<Op, PKM, 192, 256>(names[4], kt);
+        [[fallthrough]];
       case 2: return tn_launch<Op, PKM, 128, 128>(names[2], kt);
       case 3:
         if constexpr (!Op::MX) return tn_launch<Op, PKM, 128, 128, 4>(names[3], kt);
@@ -171,23 +187,25 @@ Launch select_skinny(int dt, int64_t M) {
 
 Launch four_wave(int dt, bool nn, int idx, bool kt) {
   static const char* const f16n[kNumTiles] = {"f16_nn_256x256_w4", nullptr, "f16_nn_128x128_w4",
-                                             "f16_nn_128x128_w4_s4"};
+                                             "f16_nn_128x128_w4_s4", nullptr};
   static const char* const bf16n[kNumTiles] = {"bf16_nn_256x256_w4", nullptr, "bf16_nn_128x128_w4",
-                                              "bf16_nn_128x128_w4_s4"};
-  static const char* const fp8n[kNumTiles] = {"fp8_nn_256x256_w4", "fp8_nn_256x128_w4", nullptr,
+                                              "bf16_nn_128x128_w4_s4", nullptr};
+  static const char* const fp8n[kNumTiles] = {"fp8_nn_256x256_w4", "fp8_nn_256x128_w4", nullptr, nullptr,
                                               nullptr};
-  static const char* const fp8sn[kNumTiles] = {"fp8s_nn_256x256_w4", "fp8s_nn_256x128_w4", nullptr,
+  static const char* const fp8sn[kNumTiles] = {"fp8s_nn_256x256_w4", "fp8s_nn_256x128_w4", nullptr, nullptr,
                                                nullptr};
-  static const char* const mxn[kNumTiles] = {"mx8_nn_256x256_w4", "mx8_nn_256x128_w4", nullptr, nullptr};
+  static const char* const mxn[kNumTiles] = {"mx8_nn_256x256_w4", "mx8_nn_256x128_w4", nullptr, nullptr,
+                                             nullptr};
   static const char* const f16t[kNumTiles] = {"f16_tn_256x256_w4", nullptr, "f16_tn_128x128_w4",
-                                             "f16_tn_128x128_w4_s4"};
+                                             "f16_tn_128x128_w4_s4", "f16_tn_192x256_w4"};
   static const char* const bf16t[kNumTiles] = {"bf16_tn_256x256_w4", nullptr, "bf16_tn_128x128_w4",
-                                              "bf16_tn_128x128_w4_s4"};
+                                              "bf16_tn_128x128_w4_s4", "bf16_tn_192x256_w4"};
   static const char* const fp8t[kNumTiles] = {"fp8_tn_256x256_w4", nullptr, "fp8_tn_128x128_w4",
-                                              "fp8_tn_128x128_w4_s4"};
+                                              "fp8_tn_128x128_w4_s4", nullptr};
   static const char* const fp8st[kNumTiles] = {"fp8s_tn_256x256_w4", nullptr, "fp8s_tn_128x128_w4",
-                                               "fp8s_tn_128x128_w4_s4"};
-  static const char* const mxt[kNumTiles] = {"mx8_tn_256x256_w4", nullptr, "mx8_tn_128x128_w4", nullptr};
+                                               "fp8s_tn_128x128_w4_s4", nullptr};
+  static const char* const mxt[kNumTiles] = {"mx8_tn_256x256_w4", nullptr, "mx8_tn_128x128_w4", nullptr,
+                                             nullptr};
   if (nn) {
     switch (dt) {
       case DT_F16: return tn_make<OpF16, true>(f16n, idx, kt);
@@ -245,7 +263,7 @@ Choice choose(int dt, int layout, int64_t M, int64_t N, int64_t K) {
   // transposing LDS reads.
   const int e = in_elem(dt);
   if (dt == DT_MX8 || (dt != DT_F32 && K % (16 / e) == 0 && K >= 2 * (128 / e))) {
-    const unsigned mask = tile_mask(dt, nn);
+    const unsigned mask = tile_mask(dt, nn, K);
     double whole = 0.0;
     const int idx = pick_tile(Pn, Qn, mask, &whole);
     c.L = four_wave(dt, nn, idx, k_tail(dt, K));

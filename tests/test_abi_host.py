@@ -199,22 +199,29 @@ def _kernel(lib, dt, layout, M, N, K):
 # Tile choice of the four-wave kernel: rounds of workgroups over 256 CUs
 # times the time of one round. 256 x 256 tiles cost 1 per round, 128 x 128
 # ones (two per CU, two stages) 1/0.78 * 1/2, 256 x 128 ones 1/0.76 * 1/2;
-# 128 x 128 with four stages (one per CU) 1/0.47 * 1/4, for one round only.
-@pytest.mark.parametrize("M,N,K,tile16,tile8nn", [
-    (8192, 8192, 8192, "256x256_w4", "256x256_w4"),    # 1024 tiles: 4 rounds vs 8 of 128 x 128
-    (4096, 4096, 4096, "256x256_w4", "256x256_w4"),    # one full round vs two
-    (3072, 4096, 8192, "256x256_w4", "256x256_w4"),    # 192 tiles: one round vs two
-    (5120, 5120, 1024, "256x256_w4", "256x256_w4"),    # 400 tiles: 2 rounds (2) vs 4 (2.56)
-    (2560, 2304, 4096, "128x128_w4", "256x128_w4"),    # 360 tiles of 128 x 128: one round at two per CU
-    (2048, 2048, 2048, "128x128_w4_s4", "256x128_w4"),  # 256 tiles of 128 x 128, one per CU
-    (300, 521, 512, "128x128_w4_s4", "256x128_w4"),
+# 128 x 128 with four stages (one per CU) 1/0.47 * 1/4, for one round only;
+# 192 x 256 (16-bit TN, K >= 4096) 1/0.87 * 3/4.
+@pytest.mark.parametrize("M,N,K,tile16,tile8nn,tile16tn", [
+    (8192, 8192, 8192, "256x256_w4", "256x256_w4", None),  # 1024 tiles: 4 rounds vs 8 of 128 x 128, 6 of 192 x 256
+    (4096, 4096, 4096, "256x256_w4", "256x256_w4", None),  # one full round vs two
+    (3072, 4096, 8192, "256x256_w4", "256x256_w4", "192x256_w4"),  # 192 tiles: one round (1) vs 256 of 192 x 256 (0.86)
+    (1536, 8192, 8192, "256x256_w4", "256x256_w4", "192x256_w4"),  # the same along q
+    (5120, 5120, 1024, "256x256_w4", "256x256_w4", None),  # 400 tiles: 2 rounds (2) vs 4 (2.56)
+    (3072, 4096, 2048, "256x256_w4", "256x256_w4", None),  # below K = 4096 no 192 x 256
+    (2560, 2304, 4096, "128x128_w4", "256x128_w4", None),  # 360 tiles of 128 x 128: one round at two per CU
+    (2048, 2048, 2048, "128x128_w4_s4", "256x128_w4", None),  # 256 tiles of 128 x 128, one per CU
+    (300, 521, 512, "128x128_w4_s4", "256x128_w4", None),
 ])
-def test_tile_choice(lib, M, N, K, tile16, tile8nn):
+def test_tile_choice(lib, M, N, K, tile16, tile8nn, tile16tn):
     for dt in (1, 2, 3, 4, 5):
         for layout in (0, 1):
             full = _kernel(lib, dt, layout, M, N, K)
             d = full.split()[0]
             want = tile8nn if dt >= 3 and layout == 0 else tile16
+            if tile16tn and dt <= 2 and layout == 1:
+                if tile16tn == "split":
+                    continue              # a whole round plus a second launch (the split test)
+                want = tile16tn
             if dt == 5 and want.endswith("_s4"):
                 want = want[:-3]          # MXFP8 keeps two LDS stages (its scale ring)
             assert d.endswith(want), (dt, layout, full)
@@ -231,9 +238,11 @@ def test_tile_choice(lib, M, N, K, tile16, tile8nn):
     (2, 0, 4096, 14336, 4096, "p", 12288, "bf16_nn_128x128_w4"),    # NN: p runs along N
     (3, 0, 4096, 14336, 4096, "p", 12288, "fp8_nn_256x128_w4"),
     (2, 1, 14336, 4096, 4096, "p", 12288, "bf16_tn_128x128_w4"),
-    (1, 1, 6144, 6144, 4096, "q", 5376, "f16_tn_128x128_w4"),        # 576 tiles: 504 + 48 x 6 of 128
+    (1, 0, 6144, 6144, 4096, "q", 5376, "f16_nn_128x128_w4"),        # 576 tiles: 504 + 48 x 6 of 128 (TN: 768 of 192 x 256)
     (2, 1, 4352, 4352, 1024, "q", 3840, "bf16_tn_128x128_w4_s4"),    # 289 tiles: 255 + 136 of 128, one per CU
     (4, 1, 2560, 14336, 8192, "q", 13056, "fp8s_tn_128x128_w4_s4"),
+    (2, 1, 5120, 5120, 4096, "q", 3072, "bf16_tn_192x256_w4"),       # 400 tiles: 240 + 216 of 192 x 256
+    (1, 1, 3584, 8192, 8192, "p", 2048, "f16_tn_192x256_w4"),        # 448 tiles: 256 + 256 of 192 x 256
 ])
 def test_split_choice(lib, dt, layout, M, N, K, axis, at, tail):
     full = _kernel(lib, dt, layout, M, N, K)
@@ -243,7 +252,7 @@ def test_split_choice(lib, dt, layout, M, N, K, axis, at, tail):
     assert rest.endswith(f"from {axis}={at}"), full
 
 
-@pytest.mark.parametrize("M,N,K", [(8192, 8192, 8192), (3584, 8192, 8192), (8191, 8190, 8200), (3072, 4096, 8192)])
+@pytest.mark.parametrize("M,N,K", [(8192, 8192, 8192), (3584, 8192, 2048), (8191, 8190, 8200), (3072, 4096, 8192)])
 def test_no_split_when_rounds_are_whole_or_it_does_not_pay(lib, M, N, K):
     for dt in (1, 2, 3):
         assert " + " not in _kernel(lib, dt, 1, M, N, K)
