@@ -89,7 +89,7 @@ bool k_tail(int dt, int64_t K) { return K % (128 / in_elem(dt)) != 0; }
 // 1536 x 1536 x 8192: 586 against 453), with more rounds it loses (bf16
 // 4352 x 4352 x 1024: 550 against 649; 8192^3 forced: 926 against 1012).
 // Its rate is the one measured at one round.
-// 192 x 256 (16-bit TN: wave tile 96 x 128, direct epilogue) fills a round
+// 192 x 256 (TN: wave tile 96 x 128, direct epilogue) fills a round
 // where 256 x 256 leaves CUs idle: bf16 3072 x 4096 x 8192 has 192 tiles of
 // 256 x 256 and 256 of 192 x 256 (1152 -> 1256 TF/s; 1536 x 8192 x 8192
 // 1274 -> 1383); over whole rounds it runs at 0.87 of 256 x 256 (bf16
@@ -135,10 +135,12 @@ int pick_tile(int64_t Pn, int64_t Qn, unsigned allowed, double* cost = nullptr) 
 // Tiles a four-wave variant allows: p-contiguous FP8 P keeps 256-wide rows
 // (the transposing-read swizzle needs eight 32-byte units per row).
 // MXFP8's scale ring needs two LDS stages, so it leaves out the four-stage
-// tile.  192 x 256 is built for 16-bit TN only (where it was measured).
+// tile.  192 x 256 is built for TN without block scales (where it was
+// measured: fp8 3072 x 4096 x 8192 2155 -> 2423 TF/s, 1536 x 8192 x 8192
+// 2307 -> 2573).
 unsigned tile_mask(int dt, bool nn, int64_t K) {
   if (nn && is_fp8(dt)) return 0b0011u;
-  if (!nn && (dt == DT_F16 || dt == DT_BF16) && K >= 4096) return 0b11101u;
+  if (!nn && dt != DT_MX8 && K >= 4096) return 0b11101u;
   return dt == DT_MX8 ? 0b0101u : 0b1101u;
 }
 
@@ -151,7 +153,7 @@ Launch tn_make(const char* const names[kNumTiles], int idx, bool kt) {
   } else {
     switch (idx) {
       case 4:
-        if constexpr (Op::ELEM == 2 && !PKM) return tn_launch<Op, PKM, 192, 256>(names[4], kt);
+        if constexpr (!PKM && !Op::MX) return tn_launch<Op, PKM, 192, 256>(names[4], kt);
         [[fallthrough]];
       case 2: return tn_launch<Op, PKM, 128, 128>(names[2], kt);
       case 3:
@@ -201,9 +203,9 @@ Launch four_wave(int dt, bool nn, int idx, bool kt) {
   static const char* const bf16t[kNumTiles] = {"bf16_tn_256x256_w4", nullptr, "bf16_tn_128x128_w4",
                                               "bf16_tn_128x128_w4_s4", "bf16_tn_192x256_w4"};
   static const char* const fp8t[kNumTiles] = {"fp8_tn_256x256_w4", nullptr, "fp8_tn_128x128_w4",
-                                              "fp8_tn_128x128_w4_s4", nullptr};
+                                              "fp8_tn_128x128_w4_s4", "fp8_tn_192x256_w4"};
   static const char* const fp8st[kNumTiles] = {"fp8s_tn_256x256_w4", nullptr, "fp8s_tn_128x128_w4",
-                                               "fp8s_tn_128x128_w4_s4", nullptr};
+                                               "fp8s_tn_128x128_w4_s4", "fp8s_tn_192x256_w4"};
   static const char* const mxt[kNumTiles] = {"mx8_tn_256x256_w4", nullptr, "mx8_tn_128x128_w4", nullptr,
                                              nullptr};
   if (nn) {

@@ -81,7 +81,7 @@ def kernel_name(dtype, layout, M, N, K):
 # tiles (N not a multiple of 8 in NN, so B's rows are padded and the last p
 # tile reads past the row end), a partial last stage, and 400 tiles of
 # 256 x 256, more than the CUs (rows sampled), also with a partial last stage
-# (the kernels built with tail masks); then (16-bit TN) the 192 x 256 tile,
+# (the kernels built with tail masks); then (TN) the 192 x 256 tile,
 # a whole round and a ragged one with a partial last stage.
 @pytest.mark.parametrize("dtype,layout", [(d, l) for d in ("f16", "bf16", "fp8") for l in ("tn", "nn")])
 def test_four_wave_kernel(dtype, layout):
@@ -96,7 +96,7 @@ def test_four_wave_kernel(dtype, layout):
               (1000, 1100, 9 * bk + 16, small), (2048, 1800, 2 * bk + 16, small), (2560, 2304, 3 * bk, mid),
               (129, 77, 5 * bk + 16, small), (5120, 5120, 3 * bk + 16, "256x256_w4"),
               (4352, 4352, 3 * bk, "256x256_w4"), (psplit[0], psplit[1], 3 * bk + 16, "256x256_w4")]
-    t192 = "192x256_w4" if dtype != "fp8" and layout == "tn" else "256x256_w4"
+    t192 = "192x256_w4" if layout == "tn" else "256x256_w4"
     shapes += [(1536, 8192, 4096, t192), (1500, 8000, 4096 + 16, t192)]
     for idx, (M, N, K, tile) in enumerate(shapes):
         name = kernel_name(dtype, layout, M, N, K)
@@ -275,7 +275,7 @@ def compare_scaled(p, cij, sa, sb, rows=None, exact=False):
 
 
 # Every kernel the FP8 path can pick (the eight-wave kernel for ragged K, the
-# four-wave tiles, 256 x 256 with 400 tiles), per-tensor
+# four-wave tiles, 256 x 256 with 400 tiles, 192 x 256 in TN), per-tensor
 # and per-row factors, K = 0 (C = 0 * factors).  Tolerance relative to
 # |sa_i sb_j| * sum_k |a b|.
 @pytest.mark.parametrize("layout", ["tn", "nn"])
@@ -284,7 +284,7 @@ def test_fp8_scaled_against_oracle(layout, mode):
     rng = np.random.default_rng(6000 + (layout == "nn") + 2 * (mode == "row"))
     shapes = [(1, 1, 1), (257, 129, 77), (33, 65, 300), (300, 521, 384), (512, 512, 256), (1000, 1100, 1168),
               (5120, 5120, 384), (5120, 5120, 400), (70, 90, 0), (4352, 4352, 384), (14336, 4096, 384)
-              if layout == "tn" else (4096, 14336, 384)]
+              if layout == "tn" else (4096, 14336, 384), (1500, 8000, 4096 + 16)]
     for idx, (M, N, K) in enumerate(shapes):
         p = make_problem("fp8", layout, M, N, K, seed=6100 + idx, pad=idx % 2)
         sa = _factors(rng, M if mode == "row" else 1)
