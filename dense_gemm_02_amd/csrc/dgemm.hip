@@ -93,11 +93,16 @@ bool k_tail(int dt, int64_t K) { return K % (128 / in_elem(dt)) != 0; }
 // where 256 x 256 leaves CUs idle: bf16 3072 x 4096 x 8192 has 192 tiles of
 // 256 x 256 and 256 of 192 x 256 (1152 -> 1256 TF/s; 1536 x 8192 x 8192
 // 1274 -> 1383); over whole rounds it runs at 0.87 of 256 x 256 (bf16
-// 6144 x 8192 x 8192: 1302 against 1495).  It is offered from K = 4096 on:
+// 6144 x 8192 x 8192: 1302 against 1495); 256 x 192 does the same along q
+// (bf16 4096 x 3072 x 8192 1209 -> 1374, 8192 x 1536 x 8192 1278 -> 1436;
+// fp8 2162 -> 2458, 2302 -> 2596).  Both are offered for one round only
+// (over two or three rounds they gained or lost a few percent against the
+// 256 x 256 grid or its split: bf16 3072 x 8192 x 8192 +4%, 1536 x 14336 x
+// 8192 -4%, 2560 x 14336 x 8192 -7%) and from K = 4096 on:
 // at short K its direct epilogue weighs more, and as the second launch of a
 // split it lost (bf16 5120 x 5120 x 1024: 915 against 959; 4352 x 6144 x
 // 1024: 933 against 989), while at K = 4096 and up it won (3072 x 4096:
-// +10%, 6144 x 6144: +2%, 3584 x 8192 x 8192 as a split: +1-2%).
+// +10%, 1024 x 10240 x 4096: +10%, 3584 x 8192 x 8192 as a split: +1-2%).
 // The choice minimises ceil(tiles / slots) * tile work / rate, i.e. the
 // number of rounds of workgroups times the time of one round ("FP16 GEMM
 // Optimization on AMD RDNA 3 and RDNA 4", Where That Leaves Us: no single
@@ -107,12 +112,13 @@ struct TileChoice {
   double rate;          // CU throughput relative to 256 x 256
   int max_rounds;       // 0: any number of rounds
 };
-constexpr int kNumTiles = 5;
+constexpr int kNumTiles = 6;
 constexpr TileChoice kTiles[kNumTiles] = {{256, 256, 1, 1.00, 0},
                                           {256, 128, 1, 0.76, 0},
                                           {128, 128, 2, 0.78, 0},
                                           {128, 128, 1, 0.47, 1},
-                                          {192, 256, 1, 0.87, 0}};
+                                          {192, 256, 1, 0.87, 1},
+                                          {256, 192, 1, 0.87, 1}};
 constexpr int kPlanCus = 256;  // MI355X CUs, for the tile choice only
 
 int pick_tile(int64_t Pn, int64_t Qn, unsigned allowed, double* cost = nullptr) {
@@ -140,7 +146,7 @@ int pick_tile(int64_t Pn, int64_t Qn, unsigned allowed, double* cost = nullptr) 
 // 2307 -> 2573).
 unsigned tile_mask(int dt, bool nn, int64_t K) {
   if (nn && is_fp8(dt)) return 0b0011u;
-  if (!nn && dt != DT_MX8 && K >= 4096) return 0b11101u;
+  if (!nn && dt != DT_MX8 && K >= 4096) return 0b111101u;
   return dt == DT_MX8 ? 0b0101u : 0b1101u;
 }
 
@@ -154,6 +160,9 @@ Launch tn_make(const char* const names[kNumTiles], int idx, bool kt) {
     switch (idx) {
       case 4:
         if constexpr (!PKM && !Op::MX) return tn_launch<Op, PKM, 192, 256>(names[4], kt);
+        [[fallthrough]];
+      case 5:
+        if constexpr (!PKM && !Op::MX) return tn_launch<Op, PKM, 256, 192>(names[5], kt);
         [[fallthrough]];
       case 2: return tn_launch<Op, PKM, 128, 128>(names[2], kt);
       case 3:
@@ -189,25 +198,25 @@ Launch select_skinny(int dt, int64_t M) {
 
 Launch four_wave(int dt, bool nn, int idx, bool kt) {
   static const char* const f16n[kNumTiles] = {"f16_nn_256x256_w4", nullptr, "f16_nn_128x128_w4",
-                                             "f16_nn_128x128_w4_s4", nullptr};
+                                             "f16_nn_128x128_w4_s4", nullptr, nullptr};
   static const char* const bf16n[kNumTiles] = {"bf16_nn_256x256_w4", nullptr, "bf16_nn_128x128_w4",
-                                              "bf16_nn_128x128_w4_s4", nullptr};
+                                              "bf16_nn_128x128_w4_s4", nullptr, nullptr};
   static const char* const fp8n[kNumTiles] = {"fp8_nn_256x256_w4", "fp8_nn_256x128_w4", nullptr, nullptr,
-                                              nullptr};
+                                              nullptr, nullptr};
   static const char* const fp8sn[kNumTiles] = {"fp8s_nn_256x256_w4", "fp8s_nn_256x128_w4", nullptr, nullptr,
-                                               nullptr};
+                                               nullptr, nullptr};
   static const char* const mxn[kNumTiles] = {"mx8_nn_256x256_w4", "mx8_nn_256x128_w4", nullptr, nullptr,
-                                             nullptr};
+                                             nullptr, nullptr};
   static const char* const f16t[kNumTiles] = {"f16_tn_256x256_w4", nullptr, "f16_tn_128x128_w4",
-                                             "f16_tn_128x128_w4_s4", "f16_tn_192x256_w4"};
+                                             "f16_tn_128x128_w4_s4", "f16_tn_192x256_w4", "f16_tn_256x192_w4"};
   static const char* const bf16t[kNumTiles] = {"bf16_tn_256x256_w4", nullptr, "bf16_tn_128x128_w4",
-                                              "bf16_tn_128x128_w4_s4", "bf16_tn_192x256_w4"};
+                                              "bf16_tn_128x128_w4_s4", "bf16_tn_192x256_w4", "bf16_tn_256x192_w4"};
   static const char* const fp8t[kNumTiles] = {"fp8_tn_256x256_w4", nullptr, "fp8_tn_128x128_w4",
-                                              "fp8_tn_128x128_w4_s4", "fp8_tn_192x256_w4"};
+                                              "fp8_tn_128x128_w4_s4", "fp8_tn_192x256_w4", "fp8_tn_256x192_w4"};
   static const char* const fp8st[kNumTiles] = {"fp8s_tn_256x256_w4", nullptr, "fp8s_tn_128x128_w4",
-                                               "fp8s_tn_128x128_w4_s4", "fp8s_tn_192x256_w4"};
+                                               "fp8s_tn_128x128_w4_s4", "fp8s_tn_192x256_w4", "fp8s_tn_256x192_w4"};
   static const char* const mxt[kNumTiles] = {"mx8_tn_256x256_w4", nullptr, "mx8_tn_128x128_w4", nullptr,
-                                             nullptr};
+                                             nullptr, nullptr};
   if (nn) {
     switch (dt) {
       case DT_F16: return tn_make<OpF16, true>(f16n, idx, kt);

@@ -200,12 +200,13 @@ def _kernel(lib, dt, layout, M, N, K):
 # times the time of one round. 256 x 256 tiles cost 1 per round, 128 x 128
 # ones (two per CU, two stages) 1/0.78 * 1/2, 256 x 128 ones 1/0.76 * 1/2;
 # 128 x 128 with four stages (one per CU) 1/0.47 * 1/4, for one round only;
-# 192 x 256 (TN without block scales, K >= 4096) 1/0.87 * 3/4.
+# 192 x 256 and 256 x 192 (TN without block scales, K >= 4096) 1/0.87 * 3/4.
 @pytest.mark.parametrize("M,N,K,tile16,tile8nn,tile16tn", [
     (8192, 8192, 8192, "256x256_w4", "256x256_w4", None),  # 1024 tiles: 4 rounds vs 8 of 128 x 128, 6 of 192 x 256
     (4096, 4096, 4096, "256x256_w4", "256x256_w4", None),  # one full round vs two
     (3072, 4096, 8192, "256x256_w4", "256x256_w4", "192x256_w4"),  # 192 tiles: one round (1) vs 256 of 192 x 256 (0.86)
-    (1536, 8192, 8192, "256x256_w4", "256x256_w4", "192x256_w4"),  # the same along q
+    (1536, 8192, 8192, "256x256_w4", "256x256_w4", "192x256_w4"),  # the same with more q tiles
+    (4096, 3072, 8192, "256x256_w4", "256x256_w4", "256x192_w4"),  # 192 tiles: 256 of 256 x 192
     (5120, 5120, 1024, "256x256_w4", "256x256_w4", None),  # 400 tiles: 2 rounds (2) vs 4 (2.56)
     (3072, 4096, 2048, "256x256_w4", "256x256_w4", None),  # below K = 4096 no 192 x 256
     (2560, 2304, 4096, "128x128_w4", "256x128_w4", None),  # 360 tiles of 128 x 128: one round at two per CU
@@ -240,7 +241,7 @@ def test_tile_choice(lib, M, N, K, tile16, tile8nn, tile16tn):
     (2, 1, 14336, 4096, 4096, "p", 12288, "bf16_tn_128x128_w4"),
     (1, 0, 6144, 6144, 4096, "q", 5376, "f16_nn_128x128_w4"),        # 576 tiles: 504 + 48 x 6 of 128 (TN: 768 of 192 x 256)
     (2, 1, 4352, 4352, 1024, "q", 3840, "bf16_tn_128x128_w4_s4"),    # 289 tiles: 255 + 136 of 128, one per CU
-    (4, 1, 2560, 14336, 8192, "q", 13056, "fp8s_tn_128x128_w4_s4"),
+    (4, 1, 2560, 14336, 2048, "q", 13056, "fp8s_tn_128x128_w4_s4"),  # (K >= 4096: 750 tiles of 256 x 192)
     (2, 1, 5120, 5120, 4096, "q", 3072, "bf16_tn_192x256_w4"),       # 400 tiles: 240 + 216 of 192 x 256
     (1, 1, 3584, 8192, 8192, "p", 2048, "f16_tn_192x256_w4"),        # 448 tiles: 256 + 256 of 192 x 256
 ])
