@@ -141,12 +141,12 @@ int pick_tile(int64_t Pn, int64_t Qn, unsigned allowed, double* cost = nullptr) 
 // Tiles a four-wave variant allows: p-contiguous FP8 P keeps 256-wide rows
 // (the transposing-read swizzle needs eight 32-byte units per row).
 // MXFP8's scale ring needs two LDS stages, so it leaves out the four-stage
-// tile.  192 x 256 is built for TN without block scales (where it was
+// tile.  192 x 256 and 256 x 192 are built for TN (where they were
 // measured: fp8 3072 x 4096 x 8192 2155 -> 2423 TF/s, 1536 x 8192 x 8192
 // 2307 -> 2573).
 unsigned tile_mask(int dt, bool nn, int64_t K) {
   if (nn && is_fp8(dt)) return 0b0011u;
-  if (!nn && dt != DT_MX8 && K >= 4096) return 0b111101u;
+  if (!nn && K >= 4096) return dt == DT_MX8 ? 0b110101u : 0b111101u;
   return dt == DT_MX8 ? 0b0101u : 0b1101u;
 }
 
@@ -159,10 +159,10 @@ Launch tn_make(const char* const names[kNumTiles], int idx, bool kt) {
   } else {
     switch (idx) {
       case 4:
-        if constexpr (!PKM && !Op::MX) return tn_launch<Op, PKM, 192, 256>(names[4], kt);
+        if constexpr (!PKM) return tn_launch<Op, PKM, 192, 256>(names[4], kt);
         [[fallthrough]];
       case 5:
-        if constexpr (!PKM && !Op::MX) return tn_launch<Op, PKM, 256, 192>(names[5], kt);
+        if constexpr (!PKM) return tn_launch<Op, PKM, 256, 192>(names[5], kt);
         [[fallthrough]];
       case 2: return tn_launch<Op, PKM, 128, 128>(names[2], kt);
       case 3:
@@ -216,7 +216,7 @@ Launch four_wave(int dt, bool nn, int idx, bool kt) {
   static const char* const fp8st[kNumTiles] = {"fp8s_tn_256x256_w4", nullptr, "fp8s_tn_128x128_w4",
                                                "fp8s_tn_128x128_w4_s4", "fp8s_tn_192x256_w4", "fp8s_tn_256x192_w4"};
   static const char* const mxt[kNumTiles] = {"mx8_tn_256x256_w4", nullptr, "mx8_tn_128x128_w4", nullptr,
-                                             nullptr, nullptr};
+                                             "mx8_tn_192x256_w4", "mx8_tn_256x192_w4"};
   if (nn) {
     switch (dt) {
       case DT_F16: return tn_make<OpF16, true>(f16n, idx, kt);

@@ -200,7 +200,7 @@ def _kernel(lib, dt, layout, M, N, K):
 # times the time of one round. 256 x 256 tiles cost 1 per round, 128 x 128
 # ones (two per CU, two stages) 1/0.78 * 1/2, 256 x 128 ones 1/0.76 * 1/2;
 # 128 x 128 with four stages (one per CU) 1/0.47 * 1/4, for one round only;
-# 192 x 256 and 256 x 192 (TN without block scales, K >= 4096) 1/0.87 * 3/4.
+# 192 x 256 and 256 x 192 (TN, K >= 4096) 1/0.87 * 3/4, for one round only.
 @pytest.mark.parametrize("M,N,K,tile16,tile8nn,tile16tn", [
     (8192, 8192, 8192, "256x256_w4", "256x256_w4", None),  # 1024 tiles: 4 rounds vs 8 of 128 x 128, 6 of 192 x 256
     (4096, 4096, 4096, "256x256_w4", "256x256_w4", None),  # one full round vs two
@@ -219,7 +219,7 @@ def test_tile_choice(lib, M, N, K, tile16, tile8nn, tile16tn):
             full = _kernel(lib, dt, layout, M, N, K)
             d = full.split()[0]
             want = tile8nn if dt >= 3 and layout == 0 else tile16
-            if tile16tn and dt <= 4 and layout == 1:
+            if tile16tn and layout == 1:
                 if tile16tn == "split":
                     continue              # a whole round plus a second launch (the split test)
                 want = tile16tn

@@ -382,7 +382,7 @@ def test_mxfp8_against_oracle(layout):
     rng = np.random.default_rng(7000 + (layout == "nn"))
     shapes = [(1, 1, 32), (33, 65, 96), (257, 129, 224), (300, 521, 384), (512, 512, 256), (1000, 1100, 1184),
               (5120, 5120, 384), (70, 90, 0), (4352, 4352, 384), (14336, 4096, 384) if layout == "tn" else
-              (4096, 14336, 384), (5120, 5120, 1184)]
+              (4096, 14336, 384), (5120, 5120, 1184), (1500, 8000, 4096 + 32), (8192, 1500, 4096)]
     for idx, (M, N, K) in enumerate(shapes):
         p = make_problem("fp8", layout, M, N, K, seed=7100 + idx, pad=idx % 2)
         nb = K // 32
