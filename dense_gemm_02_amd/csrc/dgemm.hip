@@ -143,11 +143,12 @@ int pick_tile(int64_t Pn, int64_t Qn, unsigned allowed, double* cost = nullptr) 
 // MXFP8's scale ring needs two LDS stages, so it leaves out the four-stage
 // tile.  192 x 256 and 256 x 192 are built for TN (where they were
 // measured: fp8 3072 x 4096 x 8192 2155 -> 2423 TF/s, 1536 x 8192 x 8192
-// 2307 -> 2573).
+// 2307 -> 2573); NN, whose p-contiguous P keeps 256-wide rows, takes
+// 256 x 192 only.
 unsigned tile_mask(int dt, bool nn, int64_t K) {
-  if (nn && is_fp8(dt)) return 0b0011u;
-  if (!nn && K >= 4096) return dt == DT_MX8 ? 0b110101u : 0b111101u;
-  return dt == DT_MX8 ? 0b0101u : 0b1101u;
+  const unsigned t192 = K < 4096 ? 0u : (nn ? 0b100000u : 0b110000u);
+  if (nn && is_fp8(dt)) return 0b0011u | t192;
+  return (dt == DT_MX8 ? 0b0101u : 0b1101u) | t192;
 }
 
 // The four-wave launch of kTiles entry `idx` (one tile_mask allows).
@@ -155,15 +156,14 @@ template <class Op, bool PKM>
 Launch tn_make(const char* const names[kNumTiles], int idx, bool kt) {
   if constexpr (PKM && Op::ELEM == 1) {
     if (idx == 1) return tn_launch<Op, PKM, 256, 128>(names[1], kt);
+    if (idx == 5) return tn_launch<Op, PKM, 256, 192>(names[5], kt);
     return tn_launch<Op, PKM, 256, 256>(names[0], kt);
   } else {
     switch (idx) {
       case 4:
         if constexpr (!PKM) return tn_launch<Op, PKM, 192, 256>(names[4], kt);
         [[fallthrough]];
-      case 5:
-        if constexpr (!PKM) return tn_launch<Op, PKM, 256, 192>(names[5], kt);
-        [[fallthrough]];
+      case 5: return tn_launch<Op, PKM, 256, 192>(names[5], kt);
       case 2: return tn_launch<Op, PKM, 128, 128>(names[2], kt);
       case 3:
         if constexpr (!Op::MX) return tn_launch<Op, PKM, 128, 128, 4>(names[3], kt);
@@ -198,15 +198,15 @@ Launch select_skinny(int dt, int64_t M) {
 
 Launch four_wave(int dt, bool nn, int idx, bool kt) {
   static const char* const f16n[kNumTiles] = {"f16_nn_256x256_w4", nullptr, "f16_nn_128x128_w4",
-                                             "f16_nn_128x128_w4_s4", nullptr, nullptr};
+                                             "f16_nn_128x128_w4_s4", nullptr, "f16_nn_256x192_w4"};
   static const char* const bf16n[kNumTiles] = {"bf16_nn_256x256_w4", nullptr, "bf16_nn_128x128_w4",
-                                              "bf16_nn_128x128_w4_s4", nullptr, nullptr};
-  static const char* const fp8n[kNumTiles] = {"fp8_nn_256x256_w4", "fp8_nn_256x128_w4", nullptr, nullptr,
-                                              nullptr, nullptr};
-  static const char* const fp8sn[kNumTiles] = {"fp8s_nn_256x256_w4", "fp8s_nn_256x128_w4", nullptr, nullptr,
-                                               nullptr, nullptr};
-  static const char* const mxn[kNumTiles] = {"mx8_nn_256x256_w4", "mx8_nn_256x128_w4", nullptr, nullptr,
-                                             nullptr, nullptr};
+                                             "bf16_nn_128x128_w4_s4", nullptr, "bf16_nn_256x192_w4"};
+  static const char* const fp8n[kNumTiles] = {"fp8_nn_256x256_w4", "fp8_nn_256x128_w4", nullptr,
+                                             nullptr, nullptr, "fp8_nn_256x192_w4"};
+  static const char* const fp8sn[kNumTiles] = {"fp8s_nn_256x256_w4", "fp8s_nn_256x128_w4", nullptr,
+                                             nullptr, nullptr, "fp8s_nn_256x192_w4"};
+  static const char* const mxn[kNumTiles] = {"mx8_nn_256x256_w4", "mx8_nn_256x128_w4", nullptr,
+                                             nullptr, nullptr, "mx8_nn_256x192_w4"};
   static const char* const f16t[kNumTiles] = {"f16_tn_256x256_w4", nullptr, "f16_tn_128x128_w4",
                                              "f16_tn_128x128_w4_s4", "f16_tn_192x256_w4", "f16_tn_256x192_w4"};
   static const char* const bf16t[kNumTiles] = {"bf16_tn_256x256_w4", nullptr, "bf16_tn_128x128_w4",

@@ -200,13 +200,14 @@ def _kernel(lib, dt, layout, M, N, K):
 # times the time of one round. 256 x 256 tiles cost 1 per round, 128 x 128
 # ones (two per CU, two stages) 1/0.78 * 1/2, 256 x 128 ones 1/0.76 * 1/2;
 # 128 x 128 with four stages (one per CU) 1/0.47 * 1/4, for one round only;
-# 192 x 256 and 256 x 192 (TN, K >= 4096) 1/0.87 * 3/4, for one round only.
+# 192 x 256 (TN) and 256 x 192 (K >= 4096) 1/0.87 * 3/4, for one round only.
 @pytest.mark.parametrize("M,N,K,tile16,tile8nn,tile16tn", [
     (8192, 8192, 8192, "256x256_w4", "256x256_w4", None),  # 1024 tiles: 4 rounds vs 8 of 128 x 128, 6 of 192 x 256
     (4096, 4096, 4096, "256x256_w4", "256x256_w4", None),  # one full round vs two
-    (3072, 4096, 8192, "256x256_w4", "256x256_w4", "192x256_w4"),  # 192 tiles: one round (1) vs 256 of 192 x 256 (0.86)
-    (1536, 8192, 8192, "256x256_w4", "256x256_w4", "192x256_w4"),  # the same with more q tiles
-    (4096, 3072, 8192, "256x256_w4", "256x256_w4", "256x192_w4"),  # 192 tiles: 256 of 256 x 192
+    # 192 tiles of 256 x 256: one round (1) vs 256 of 192 x 256 or 256 x 192 (0.86); NN (p along N) has 256 x 192 only
+    (3072, 4096, 8192, "256x256_w4", "256x256_w4", ("192x256_w4", "256x192_w4")),
+    (1536, 8192, 8192, "256x256_w4", "256x256_w4", ("192x256_w4", "256x192_w4")),
+    (4096, 3072, 8192, "256x256_w4", "256x256_w4", ("256x192_w4", "256x256_w4")),
     (5120, 5120, 1024, "256x256_w4", "256x256_w4", None),  # 400 tiles: 2 rounds (2) vs 4 (2.56)
     (3072, 4096, 2048, "256x256_w4", "256x256_w4", None),  # below K = 4096 no 192 x 256
     (2560, 2304, 4096, "128x128_w4", "256x128_w4", None),  # 360 tiles of 128 x 128: one round at two per CU
@@ -219,10 +220,8 @@ def test_tile_choice(lib, M, N, K, tile16, tile8nn, tile16tn):
             full = _kernel(lib, dt, layout, M, N, K)
             d = full.split()[0]
             want = tile8nn if dt >= 3 and layout == 0 else tile16
-            if tile16tn and layout == 1:
-                if tile16tn == "split":
-                    continue              # a whole round plus a second launch (the split test)
-                want = tile16tn
+            if tile16tn:
+                want = tile16tn[0] if layout == 1 else tile16tn[1]
             if dt == 5 and want.endswith("_s4"):
                 want = want[:-3]          # MXFP8 keeps two LDS stages (its scale ring)
             assert d.endswith(want), (dt, layout, full)

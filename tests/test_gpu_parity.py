@@ -81,8 +81,9 @@ def kernel_name(dtype, layout, M, N, K):
 # tiles (N not a multiple of 8 in NN, so B's rows are padded and the last p
 # tile reads past the row end), a partial last stage, and 400 tiles of
 # 256 x 256, more than the CUs (rows sampled), also with a partial last stage
-# (the kernels built with tail masks); then (TN) the 192 x 256 tile,
-# a whole round and a ragged one with a partial last stage, and 256 x 192.
+# (the kernels built with tail masks); then the one-round 192 tiles (TN
+# 192 x 256 and 256 x 192, NN 256 x 192), a whole round and ragged ones with
+# a partial last stage.
 @pytest.mark.parametrize("dtype,layout", [(d, l) for d in ("f16", "bf16", "fp8") for l in ("tn", "nn")])
 def test_four_wave_kernel(dtype, layout):
     bk = {"f16": 64, "bf16": 64, "fp8": 128}[dtype]
@@ -96,7 +97,9 @@ def test_four_wave_kernel(dtype, layout):
               (1000, 1100, 9 * bk + 16, small), (2048, 1800, 2 * bk + 16, small), (2560, 2304, 3 * bk, mid),
               (129, 77, 5 * bk + 16, small), (5120, 5120, 3 * bk + 16, "256x256_w4"),
               (4352, 4352, 3 * bk, "256x256_w4"), (psplit[0], psplit[1], 3 * bk + 16, "256x256_w4")]
-    t192 = "192x256_w4" if layout == "tn" else "256x256_w4"
+    # NN runs p along N: the same shapes take 256 x 192 there (and the third
+    # one 256 x 256).
+    t192 = "192x256_w4" if layout == "tn" else "256x192_w4"
     q192 = "256x192_w4" if layout == "tn" else "256x256_w4"
     shapes += [(1536, 8192, 4096, t192), (1500, 8000, 4096 + 16, t192), (8192, 1500, 4096 + 16, q192)]
     for idx, (M, N, K, tile) in enumerate(shapes):
