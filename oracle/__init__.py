@@ -235,14 +235,17 @@ def check(c_bits, c_ref_bits, sab, out_fmt, tol):
 
     err_ij = |c_ij - c_ref_ij| / sab_ij with both values decoded exactly, in
     FP64.  Passes when max err <= tol, every element with sab == 0 matches
-    exactly, and no NaN/Inf appears where the reference is finite.
+    exactly, no NaN/Inf appears where the reference is finite, and where the
+    reference is not finite the result is of the same kind: the same signed
+    infinity (an overflow of the output format), or NaN for NaN.
     Returns (ok, max_err, n_bad).
     """
     c = decode(out_fmt, c_bits)
     r = decode(out_fmt, c_ref_bits)
     sab = np.asarray(sab, dtype=np.float64)
     finite_ref = np.isfinite(r)
-    bad_nonfinite = finite_ref & ~np.isfinite(c)
+    same_kind = (np.isnan(r) & np.isnan(c)) | (np.isinf(r) & (c == r))
+    bad_nonfinite = (finite_ref & ~np.isfinite(c)) | (~finite_ref & ~same_kind)
     diff = np.abs(c - r)
     zero = sab == 0
     with np.errstate(divide="ignore", invalid="ignore"):

@@ -410,6 +410,22 @@ def test_checker_accepts_and_rejects_as_predicted(oracle_lib):
     # NaN where the reference is finite fails
     nanc = c.copy(); nanc[0, 0] = 0x7fc0
     assert not oracle.check(nanc, c, sab, oracle.BF16, 1.0)[0]
+    # where the reference overflows to +-Inf (or is NaN) only the same kind
+    # passes: a finite value, the other infinity or NaN against Inf fail, and
+    # so does a finite value or an infinity against NaN, at any tolerance
+    pinf, ninf, qnan = 0x7f80, 0xff80, 0x7fc0
+    ref = c.copy(); ref[1, 2] = pinf; ref[2, 3] = ninf; ref[4, 4] = qnan
+    assert oracle.check(ref, ref, sab, oracle.BF16, oracle.TOL["bf16"])[0]
+    for at, planted in (((1, 2), c[1, 2]), ((1, 2), ninf), ((1, 2), qnan), ((2, 3), pinf), ((2, 3), 0x7f7f),
+                        ((4, 4), pinf), ((4, 4), 0)):
+        got = ref.copy(); got[at] = planted
+        ok, _, nbad = oracle.check(got, ref, sab, oracle.BF16, 1e300)
+        assert not ok and nbad == 1, (at, hex(int(planted)))
+    # the same for an FP32 output (FP8 products) overflowing
+    r32 = np.array([[0x7f800000, 0x3f800000]], np.uint32)
+    s32 = np.ones((1, 2))
+    assert oracle.check(r32, r32, s32, oracle.F32, 2.0 ** -7)[0]
+    assert not oracle.check(np.array([[0x7f7fffff, 0x3f800000]], np.uint32), r32, s32, oracle.F32, 1e300)[0]
     # sab == 0 requires exact equality
     z = np.zeros((1, 1), np.uint16)
     assert oracle.check(z, z, np.zeros((1, 1)), oracle.BF16, 1.0)[0]
