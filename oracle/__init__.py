@@ -9,7 +9,9 @@ accumulation, one round-to-nearest-even rounding to the output format).  This
 module only builds and loads that library, marshals numpy arrays, applies
 the FP8 scale factors to the exact sums (``gemm_fp8_scaled``), computes the
 block-scaled MXFP8 product from per-block library matrix products in FP64
-(``gemm_mxfp8``), and holds the acceptance check.
+(``gemm_mxfp8``), gives the same definition with the FP64 sum taken by a
+library matrix product for whole outputs at full size (``gemm_lib``), and
+holds the acceptance check.
 
 Definition followed: "Optimizing GEMM in HIP", section "GEMM fundamentals"
 (C_ij = inner product of row i of A and column j of B); storage layouts from
@@ -114,6 +116,73 @@ def gemm(in_fmt, layout, M, N, K, A, lda, B, ldb, rows=None, threads=0, plain=Fa
     if rc != 0:
         raise ValueError("oracle_gemm rejected its arguments")
     return c, s, sab
+
+
+def _decode_a_rows(in_fmt, K, A, lda, rows):
+    """a[i][k] = A[i*lda + k] for the requested rows, decoded exactly with the
+    oracle's own decoder ("Optimizing GEMM in HIP", GEMM fundamentals)."""
+    A2 = np.asarray(A).reshape(-1, lda)
+    return decode(in_fmt, np.ascontiguousarray(A2[rows, :K]))
+
+
+def _decode_b(in_fmt, layout, N, K, B, ldb):
+    """b as a K x N array: B[k*ldb + j] (NN) or B[j*ldb + k] (TN: B stored
+    column-major, "FP16 GEMM Optimization on AMD RDNA 3 and RDNA 4", What We
+    Are Computing), decoded exactly.  For TN the result is a transposed view
+    of the decoded N x K storage (the library product takes it as it is)."""
+    B2 = np.asarray(B).reshape(-1, ldb)
+    if layout == NN:
+        return decode(in_fmt, np.ascontiguousarray(B2[:K, :N]))
+    return decode(in_fmt, np.ascontiguousarray(B2[:N, :K])).T
+
+
+def gemm_lib(in_fmt, layout, M, N, K, A, lda, B, ldb, rows=None, with_sab=True, block=1024):
+    """The definition ``gemm`` computes, with the FP64 sum formed by a library
+    matrix product (numpy's BLAS) instead of the triple loop; for checking
+    whole outputs at sizes where the loop would take minutes.
+
+    Steps, per element (i, j): a(i,k) and b(k,j) decoded exactly (the same
+    decoder as ``gemm``), s_ij = sum_k a(i,k) b(k,j) in FP64,
+    sab_ij = sum_k |a(i,k) b(k,j)| in FP64 (skipped when ``with_sab`` is
+    false, e.g. for bit-exact comparisons), and s_ij rounded once to the
+    output format (the same encoder).  The library sums in its own order:
+    where every partial sum is exact in FP64 (E4M3 operands: multiples of
+    2^-18 below 2^49; +-1 and identity operands) the result equals ``gemm``'s
+    bit for bit; otherwise s differs from the loop's by FP64 rounding
+    (<= K 2^-52 sab), which changes the rounded output only where s lies that
+    close to a rounding midpoint of the output format.
+
+    Returns (c_bits, sab) shaped [len(rows) or M][N] (sab is None without
+    ``with_sab``).  Rows are processed in blocks of ``block``.
+    """
+    rows = np.arange(M, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    of = out_fmt_of(in_fmt)
+    c = np.empty((len(rows), N), dtype=np.uint32 if of == F32 else np.uint16)
+    sab = np.empty((len(rows), N), dtype=np.float64) if with_sab else None
+    if K == 0 or len(rows) == 0 or N == 0:
+        c[...] = 0
+        if with_sab:
+            sab[...] = 0.0
+        return c, sab
+    b = _decode_b(in_fmt, layout, N, K, B, ldb)
+    babs = None
+    if with_sab:
+        babs = np.abs(b.T).T if layout == TN else np.abs(b)   # elementwise, in storage order
+    # one set of block buffers, reused (fresh memory is slow to touch)
+    nb = min(block, len(rows))
+    acc = np.empty((nb, N), dtype=np.float64)
+    aabs = np.empty((nb, K), dtype=np.float64) if with_sab else None
+    with np.errstate(invalid="ignore", over="ignore"):
+        for r0 in range(0, len(rows), block):
+            blk = rows[r0:r0 + block]
+            n = len(blk)
+            a = _decode_a_rows(in_fmt, K, A, lda, blk)
+            np.matmul(a, b, out=acc[:n])
+            c[r0:r0 + n] = encode(of, acc[:n])
+            if with_sab:
+                np.abs(a, out=aabs[:n])
+                np.matmul(aabs[:n], babs, out=sab[r0:r0 + n])
+    return c, sab
 
 
 def scale_vector(scale, n):

@@ -234,13 +234,16 @@ int oracle_gemm_plain(int in_fmt, int out_fmt, int layout, int64_t M, int64_t N,
   return 0;
 }
 
-// Codec access for the self-tests.
+// Codec access for the self-tests and the library-product check.  Each
+// element is converted on its own; threads only split the range.
 void oracle_decode(int fmt, const void* src, int64_t n, double* dst) {
+#pragma omp parallel for schedule(static) if (n > 65536)
   for (int64_t i = 0; i < n; ++i) dst[i] = decode(fmt, src, i);
 }
 
 // fmt: 0 f32 (uint32 out), 1 f16, 2 bf16 (uint16 out)
 void oracle_encode(int fmt, const double* src, int64_t n, void* dst) {
+#pragma omp parallel for schedule(static) if (n > 65536)
   for (int64_t i = 0; i < n; ++i) {
     if (fmt == FMT_F32)      ((uint32_t*)dst)[i] = enc_f32(src[i]);
     else if (fmt == FMT_F16) ((uint16_t*)dst)[i] = enc_f16(src[i]);

@@ -390,6 +390,65 @@ def test_threads_rows_and_plain_loop_agree(oracle_lib):
         assert np.array_equal(cr, c1[rows]) and np.array_equal(sr.view(np.uint64), s1[rows].view(np.uint64))
 
 
+# ---- the library-product leg (whole outputs at full size) ----------------------
+
+def run_lib(p, rows=None, with_sab=True, block=1024):
+    return oracle.gemm_lib(FMT[p.dtype], LAY[p.layout], p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, rows=rows,
+                           with_sab=with_sab, block=block)
+
+
+@pytest.mark.parametrize("dtype,layout", [(d, l) for d in ("f32", "f16", "bf16", "fp8") for l in ("nn", "tn")])
+def test_library_product_equals_the_loop(oracle_lib, dtype, layout):
+    # Same decode, same single rounding; only the FP64 summation order
+    # differs, so on these inputs (no sum within K 2^-52 sab of an output
+    # midpoint) the bits are equal, with padded leading dimensions holding
+    # garbage, blocks that do not divide the rows, and row subsets.
+    dist = {"f32": "uniform", "f16": "normal", "bf16": "normal", "fp8": "uniform4"}[dtype]
+    M, N, K = 70, 45, 777
+    la, lb, _ = inputs.min_ld(layout, M, N, K)
+    p = inputs.make(dtype, layout, M, N, K, 21, dist, lda=la + 16, ldb=lb + 16)
+    c, s, sab = run(p)
+    c2, sab2 = run_lib(p, block=32)
+    assert np.array_equal(c, c2)
+    assert np.all(np.abs(sab - sab2) <= 2 * K * 2.0 ** -53 * sab)
+    rows = np.array([69, 3, 3, 40])
+    c3, sab3 = run_lib(p, rows=rows, block=3)
+    assert np.array_equal(c3, c[rows]) and np.all(np.abs(sab3 - sab[rows]) <= 2 * K * 2.0 ** -53 * sab[rows])
+    c4, none = run_lib(p, with_sab=False)
+    assert none is None and np.array_equal(c4, c)
+
+
+@pytest.mark.parametrize("dtype,layout", [("f16", "tn"), ("bf16", "nn"), ("fp8", "tn"), ("f32", "tn")])
+def test_library_product_exact_sets(oracle_lib, dtype, layout):
+    # +-1 operands at K = 8192 (partial sums exact in any order): the output
+    # is the integer matrix product rounded once; the identity gives A back.
+    p = inputs.make(dtype, layout, 24, 20, 8192, 2, "pm1")
+    c, sab = run_lib(p)
+    a = lib_decode(dtype, p.A).astype(np.int64)
+    b = lib_decode(dtype, p.B).astype(np.int64)
+    ref = a @ (b if layout == "nn" else b.T)
+    assert np.all(sab == p.K)
+    assert np.array_equal(oracle.decode(out_fmt(dtype), c), lib_round(out_of(dtype), ref.astype(np.float64)))
+    q = inputs.make(dtype, layout, 30, 64, 64, 4, "uniform4" if dtype == "fp8" else "normal")
+    ident = inputs.identity(dtype, layout, 64, q.A, q.lda)
+    ci, _ = run_lib(ident)
+    assert np.array_equal(oracle.decode(out_fmt(dtype), ci), lib_decode(dtype, q.A[:, :64]))
+    # empty sums and empty row sets
+    z, zs = run_lib(inputs.make(dtype, layout, 5, 6, 0, 1, "pm1"))
+    assert np.all(z == 0) and np.all(zs == 0)
+
+
+def test_library_product_catches_planted_mistakes(oracle_lib):
+    p = inputs.make("bf16", "tn", 64, 64, 64, 3, "pm1")
+    c, _ = run_lib(p, with_sab=False)
+    # B read in the other layout (a transposed operand)
+    wrong = oracle.gemm_lib(oracle.BF16, oracle.NN, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, with_sab=False)[0]
+    assert not np.array_equal(wrong, c)
+    # one k term dropped (K - 1): every +-1 sum changes parity
+    short = oracle.gemm_lib(oracle.BF16, oracle.TN, p.M, p.N, p.K - 1, p.A, p.lda, p.B, p.ldb, with_sab=False)[0]
+    assert not np.any(short == c)
+
+
 # ---- acceptance checker -------------------------------------------------------
 
 def test_checker_accepts_and_rejects_as_predicted(oracle_lib):
