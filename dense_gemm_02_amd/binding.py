@@ -146,51 +146,89 @@ _BY_DTYPE = {"f32": gemm_f32, "f16": gemm_f16, "bf16": gemm_bf16, "fp8": gemm_fp
 _ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 
 
+def _bytes_after(t) -> int:
+    """Bytes of t's storage from its first element to the end of the storage."""
+    return t.untyped_storage().nbytes() - t.storage_offset() * t.element_size()
+
+
+def _need(t, nbytes, what):
+    if nbytes > 0 and _bytes_after(t) < nbytes:
+        raise ValueError(f"{what} holds {_bytes_after(t)} bytes from its first element, the call reads or "
+                         f"writes {nbytes}")
+
+
+def _check_extents(layout, M, N, K, A, lda, B, ldb, C, ldc, ein, eout):
+    """The extents include/dgemm.h requires of the caller's memory: A over
+    M*lda elements and B over K*ldb (NN) or N*ldb (TN) when K > 0 (whole rows
+    of the pitch: the kernels copy 16-byte pieces), and C over the last
+    element written, (M-1)*ldc + N (NN) or (N-1)*ldc + M (TN)."""
+    if M <= 0 or N <= 0:
+        return
+    if K > 0:
+        _need(A, M * lda * ein, "A")
+        _need(B, (K if layout in ("nn", DGEMM_NN) else N) * ldb * ein, "B")
+    last = (M - 1) * ldc + N if layout in ("nn", DGEMM_NN) else (N - 1) * ldc + M
+    _need(C, last * eout, "C")
+
+
+def _device_tensors(names, *ts):
+    import torch
+    for t in ts:
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{names} must be device tensors")
+
+
+def _factor_vector(t, n, what):
+    import torch
+    if t.dtype != torch.float32 or not t.is_contiguous():
+        raise TypeError(f"{what} must be a contiguous float32 tensor")
+    if t.numel() not in (1, n):
+        raise ValueError(f"{what} holds {t.numel()} values, not 1 or {n}")
+
+
 def gemm(dtype, layout, M, N, K, A, lda, B, ldb, C, ldc, stream=None):
     """Tensor-level call.  A, B, C are torch device tensors holding the
     operands' storage (any integer or float dtype of the right width); the
-    leading dimensions are in elements."""
-    import torch
-    for t in (A, B, C):
-        if not isinstance(t, torch.Tensor) or not t.is_cuda:
-            raise TypeError("A, B and C must be device tensors")
+    leading dimensions are in elements.  The storage behind each tensor must
+    cover what the call reads or writes (checked here)."""
+    _device_tensors("A, B and C", A, B, C)
     ebytes = _ELEM[dtype]
     if A.element_size() != ebytes or B.element_size() != ebytes:
         raise TypeError(f"{dtype} operands need {ebytes}-byte elements")
     cbytes = 4 if dtype in ("f32", "fp8") else 2
     if C.element_size() != cbytes:
         raise TypeError(f"{dtype} output needs {cbytes}-byte elements")
+    _check_extents(layout, M, N, K, A, lda, B, ldb, C, ldc, ebytes, cbytes)
     _BY_DTYPE[dtype](M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, layout, stream)
 
 
 def gemm_scaled(layout, M, N, K, A, lda, B, ldb, C, ldc, scale_a, scale_b, stream=None):
     """Tensor-level FP8 call with scale factors: A, B hold E4M3 bytes, C FP32
-    storage, scale_a / scale_b are FP32 device tensors of 1 or M / 1 or N
-    values."""
-    import torch
-    for t in (A, B, C, scale_a, scale_b):
-        if not isinstance(t, torch.Tensor) or not t.is_cuda:
-            raise TypeError("A, B, C and the scale factors must be device tensors")
+    storage, scale_a / scale_b are contiguous FP32 device tensors of 1 or M /
+    1 or N values."""
+    _device_tensors("A, B, C and the scale factors", A, B, C, scale_a, scale_b)
     if A.element_size() != 1 or B.element_size() != 1 or C.element_size() != 4:
         raise TypeError("fp8 operands need 1-byte elements and a 4-byte output")
-    for t in (scale_a, scale_b):
-        if t.dtype != torch.float32 or not t.is_contiguous():
-            raise TypeError("scale factors must be contiguous float32 tensors")
+    _factor_vector(scale_a, M, "scale_a")
+    _factor_vector(scale_b, N, "scale_b")
+    _check_extents(layout, M, N, K, A, lda, B, ldb, C, ldc, 1, 4)
     gemm_fp8_scaled(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, scale_a.data_ptr(),
                     scale_a.numel(), scale_b.data_ptr(), scale_b.numel(), layout, stream)
 
 
 def gemm_mx(layout, M, N, K, A, lda, B, ldb, C, ldc, scale_a, ldsa, scale_b, ldsb, stream=None):
     """Tensor-level MXFP8 call: A, B hold E4M3 bytes, C FP32 storage,
-    scale_a / scale_b E8M0 bytes (device tensors) with row pitches ldsa / ldsb."""
-    import torch
-    for t in (A, B, C, scale_a, scale_b):
-        if not isinstance(t, torch.Tensor) or not t.is_cuda:
-            raise TypeError("A, B, C and the block scales must be device tensors")
+    scale_a / scale_b E8M0 bytes (device tensors covering M*ldsa / N*ldsb
+    bytes) with row pitches ldsa / ldsb."""
+    _device_tensors("A, B, C and the block scales", A, B, C, scale_a, scale_b)
     if A.element_size() != 1 or B.element_size() != 1 or C.element_size() != 4:
         raise TypeError("fp8 operands need 1-byte elements and a 4-byte output")
     if scale_a.element_size() != 1 or scale_b.element_size() != 1:
         raise TypeError("block scales are bytes")
+    _check_extents(layout, M, N, K, A, lda, B, ldb, C, ldc, 1, 4)
+    if M > 0 and N > 0 and K > 0:
+        _need(scale_a, M * ldsa, "scale_a")
+        _need(scale_b, N * ldsb, "scale_b")
     gemm_mxfp8(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, scale_a.data_ptr(), ldsa,
                scale_b.data_ptr(), ldsb, layout, stream)
 
@@ -254,9 +292,14 @@ def matmul(a, b, out=None, scale_a=None, scale_b=None, stream=None):
         if out.stride(0) != 1 and M * N > 1:
             raise ValueError("TN writes a column-major C")
         ldc = out.stride(1) if N > 1 else max(M, 1)
+    ein = _ELEM[dt]
+    _check_extents(layout, M, N, K, a, lda, b, ldb, out, ldc, ein, out.element_size())
     if scale_a is not None or scale_b is not None:
         if dt != "fp8" or scale_a is None or scale_b is None:
             raise ValueError("scale factors go with fp8 operands, both of them")
+        _device_tensors("scale factors", scale_a, scale_b)
+        _factor_vector(scale_a, M, "scale_a")
+        _factor_vector(scale_b, N, "scale_b")
         gemm_fp8_scaled(M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, scale_a.data_ptr(),
                         scale_a.numel(), scale_b.data_ptr(), scale_b.numel(), layout, stream)
     else:

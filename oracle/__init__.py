@@ -159,17 +159,33 @@ def gemm_lib(in_fmt, layout, M, N, K, A, lda, B, ldb, rows=None, with_sab=True, 
     of = out_fmt_of(in_fmt)
     c = np.empty((len(rows), N), dtype=np.uint32 if of == F32 else np.uint16)
     sab = np.empty((len(rows), N), dtype=np.float64) if with_sab else None
-    if K == 0 or len(rows) == 0 or N == 0:
-        c[...] = 0
+    for r0, cb, sb in gemm_lib_blocks(in_fmt, layout, M, N, K, A, lda, B, ldb, rows, with_sab, block):
+        c[r0:r0 + len(cb)] = cb
         if with_sab:
-            sab[...] = 0.0
-        return c, sab
+            sab[r0:r0 + len(cb)] = sb
+    return c, sab
+
+
+def gemm_lib_blocks(in_fmt, layout, M, N, K, A, lda, B, ldb, rows=None, with_sab=True, block=1024):
+    """``gemm_lib`` one block of rows at a time: yields (r0, c_bits, sab) for
+    rows[r0 : r0 + block] (sab None without ``with_sab``).  The arrays of a
+    block are reused for the next one."""
+    rows = np.arange(M, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    of = out_fmt_of(in_fmt)
+    if len(rows) == 0:
+        return
+    nb = min(block, len(rows))
+    cbuf = np.zeros((nb, N), dtype=np.uint32 if of == F32 else np.uint16)
+    sbuf = np.zeros((nb, N), dtype=np.float64) if with_sab else None
+    if K == 0 or N == 0:
+        for r0 in range(0, len(rows), block):
+            n = len(rows[r0:r0 + block])
+            yield r0, cbuf[:n], (sbuf[:n] if with_sab else None)
+        return
     b = _decode_b(in_fmt, layout, N, K, B, ldb)
     babs = None
     if with_sab:
         babs = np.abs(b.T).T if layout == TN else np.abs(b)   # elementwise, in storage order
-    # one set of block buffers, reused (fresh memory is slow to touch)
-    nb = min(block, len(rows))
     acc = np.empty((nb, N), dtype=np.float64)
     aabs = np.empty((nb, K), dtype=np.float64) if with_sab else None
     with np.errstate(invalid="ignore", over="ignore"):
@@ -178,11 +194,11 @@ def gemm_lib(in_fmt, layout, M, N, K, A, lda, B, ldb, rows=None, with_sab=True, 
             n = len(blk)
             a = _decode_a_rows(in_fmt, K, A, lda, blk)
             np.matmul(a, b, out=acc[:n])
-            c[r0:r0 + n] = encode(of, acc[:n])
+            cbuf[:n] = encode(of, acc[:n])
             if with_sab:
                 np.abs(a, out=aabs[:n])
-                np.matmul(aabs[:n], babs, out=sab[r0:r0 + n])
-    return c, sab
+                np.matmul(aabs[:n], babs, out=sbuf[:n])
+            yield r0, cbuf[:n], (sbuf[:n] if with_sab else None)
 
 
 def scale_vector(scale, n):

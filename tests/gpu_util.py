@@ -77,16 +77,36 @@ def oracle_ref(p, rows=None):
     return oracle.gemm(FMT[p.dtype], LAY[p.layout], p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, rows=rows)
 
 
+# Above this many multiply-adds a whole output is checked with the oracle's
+# library-product leg (the same definition, pinned to the loop bit for bit),
+# block by block; below it the triple loop itself is the reference.
+LOOP_MACS = 5e8
+
+
 def compare(p, cij, rows=None, exact=False, tol=None):
-    """Compare GPU output rows with the oracle.  Returns (ok, max_err, n_bad)."""
+    """Compare GPU output rows (all of them when rows is None) with the
+    oracle.  Returns (ok, max_err, n_bad)."""
+    of = OUT_FMT[p.dtype]
+    tol = oracle.TOL[p.dtype] if tol is None else tol
+    if rows is None and p.M * p.N * max(p.K, 1) > LOOP_MACS:
+        ok, max_err, nbad = True, 0.0, 0
+        for r0, c_ref, sab in oracle.gemm_lib_blocks(FMT[p.dtype], LAY[p.layout], p.M, p.N, p.K, p.A, p.lda,
+                                                     p.B, p.ldb, with_sab=not exact, block=2048):
+            got = cij[r0:r0 + len(c_ref)]
+            if exact:
+                if not oracle.bits_equal(got, c_ref, of):
+                    ok = False
+                    nbad += int(np.sum(got != c_ref))
+            else:
+                o, e, nb = oracle.check(got, c_ref, sab, of, tol)
+                ok, max_err, nbad = ok and o, max(max_err, e), nbad + nb
+        return ok, max_err, nbad
     c_ref, _, sab = oracle_ref(p, rows)
     got = cij if rows is None else cij[np.asarray(rows)]
-    of = OUT_FMT[p.dtype]
     if exact:
         ok = oracle.bits_equal(got, c_ref, of)
         nbad = 0 if ok else int(np.sum(got != c_ref))
         return ok, 0.0, nbad
-    tol = oracle.TOL[p.dtype] if tol is None else tol
     return oracle.check(got, c_ref, sab, of, tol)
 
 

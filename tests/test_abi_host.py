@@ -272,3 +272,61 @@ def test_matmul_rejects_host_and_mismatched_tensors():
         matmul(torch.ones(2, 3), torch.ones(3, 4))
     with pytest.raises(TypeError):
         matmul(np.ones((2, 3)), np.ones((3, 4)))
+
+
+# ---- tensor-level binding checks (host side, no GPU work) --------------------
+
+def test_binding_rejects_host_tensors():
+    import torch
+    from dense_gemm_02_amd import binding
+    a = torch.zeros(64, dtype=torch.int16)
+    f = torch.ones(1)
+    with pytest.raises(TypeError):
+        binding.gemm("bf16", "tn", 8, 8, 8, a, 8, a, 8, a, 8)
+    u8, c32 = torch.zeros(64, dtype=torch.uint8), torch.zeros(64, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        binding.gemm_scaled("tn", 8, 8, 8, u8, 8, u8, 8, c32, 8, f, f)
+    with pytest.raises(TypeError):
+        binding.gemm_mx("tn", 8, 8, 32, u8, 32, u8, 32, c32, 8, u8, 16, u8, 16)
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+def test_binding_extent_checks(layout):
+    import torch
+    from dense_gemm_02_amd import binding
+    M, N, K, lda, ldb, ldc = 5, 7, 16, 24, 32, 9
+
+    def t(n, dtype=torch.int16):
+        return torch.zeros(n, dtype=dtype)
+
+    nb_rows = K if layout == "nn" else N
+    c_last = (M - 1) * ldc + N if layout == "nn" else (N - 1) * ldc + M
+    ok = dict(A=t(M * lda), B=t(nb_rows * ldb), C=t(c_last))
+    binding._check_extents(layout, M, N, K, ok["A"], lda, ok["B"], ldb, ok["C"], ldc, 2, 2)
+    for which, short in (("A", t(M * lda - 1)), ("B", t(nb_rows * ldb - 1)), ("C", t(c_last - 1))):
+        args = dict(ok, **{which: short})
+        with pytest.raises(ValueError, match=which):
+            binding._check_extents(layout, M, N, K, args["A"], lda, args["B"], ldb, args["C"], ldc, 2, 2)
+    # a view that starts inside its storage counts only what follows it
+    big = t(M * lda + 8)
+    binding._check_extents(layout, M, N, K, big[8:], lda, ok["B"], ldb, ok["C"], ldc, 2, 2)
+    with pytest.raises(ValueError):
+        binding._check_extents(layout, M, N, K, big[9:], lda, ok["B"], ldb, ok["C"], ldc, 2, 2)
+    # nothing is read at K = 0, nothing at all for an empty output
+    binding._check_extents(layout, M, N, 0, t(0), lda, t(0), ldb, ok["C"], ldc, 2, 2)
+    binding._check_extents(layout, 0, N, K, t(0), lda, t(0), ldb, t(0), ldc, 2, 2)
+
+
+def test_binding_factor_checks():
+    import torch
+    from dense_gemm_02_amd import binding
+    binding._factor_vector(torch.ones(1), 9, "scale_a")
+    binding._factor_vector(torch.ones(9), 9, "scale_a")
+    with pytest.raises(TypeError):
+        binding._factor_vector(torch.ones(9, dtype=torch.float64), 9, "scale_a")
+    with pytest.raises(TypeError):
+        binding._factor_vector(torch.ones(9, dtype=torch.bfloat16), 9, "scale_a")
+    with pytest.raises(TypeError):
+        binding._factor_vector(torch.ones(18)[::2], 9, "scale_a")
+    with pytest.raises(ValueError):
+        binding._factor_vector(torch.ones(8), 9, "scale_a")

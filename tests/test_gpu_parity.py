@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from dense_gemm_02_amd import inputs
-from gpu_util import alloc_c, c_host, compare, pad_untouched, run_gpu, sample_rows, say, to_dev
+from gpu_util import alloc_c, c_host, compare, pad_untouched, run_gpu, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -80,7 +80,7 @@ def kernel_name(dtype, layout, M, N, K):
 # stages, the latter also with fewer stages than buffers): exactly two stages, an odd stage count with edge
 # tiles (N not a multiple of 8 in NN, so B's rows are padded and the last p
 # tile reads past the row end), a partial last stage, and 400 tiles of
-# 256 x 256, more than the CUs (rows sampled), also with a partial last stage
+# 256 x 256, more than the CUs, also with a partial last stage
 # (the kernels built with tail masks); then the one-round 192 tiles (TN
 # 192 x 256 and 256 x 192, NN 256 x 192), a whole round and ragged ones with
 # a partial last stage.
@@ -111,15 +111,13 @@ def test_four_wave_kernel(dtype, layout):
         say(f"case w4 {name} M={M} N={N} K={K}")
         cij, pad = c_host(p, run_gpu(p))
         assert pad_untouched(pad, dtype)
-        rows = sample_rows(M, seed=idx) if M * N * K > 5e8 else None
-        ok, err, nbad = compare(p, cij, rows=rows)
+        ok, err, nbad = compare(p, cij)
         assert ok, f"{dtype} {layout} {(M, N, K)}: max err {err:.3e}, {nbad} bad"
     for idx, (M, N) in enumerate([(260, 300), (4096, 4096)]):
         p = make_problem(dtype, layout, M, N, 16 * bk, seed=5100 + idx, dist="pm1")
         say(f"case w4 pm1 {kernel_name(dtype, layout, M, N, 16 * bk)} M={M} N={N}")
         cij, _ = c_host(p, run_gpu(p))
-        rows = sample_rows(M, seed=idx) if M > 1000 else None
-        ok, _, nbad = compare(p, cij, rows=rows, exact=True)
+        ok, _, nbad = compare(p, cij, exact=True)
         assert ok, f"pm1 {(M, N)}: {nbad} elements differ"
 
 
@@ -131,6 +129,99 @@ def test_pm1_bit_exact(dtype, layout):
         cij, _ = c_host(p, run_gpu(p))
         ok, _, nbad = compare(p, cij, exact=True)
         assert ok, f"{nbad} elements differ"
+
+
+# +-1 operands on the paths the cases above reach only with random data:
+# every partial sum is an integer below 2^24, so FP32 accumulation is exact
+# in any order and the output must equal the oracle bit for bit ("FP16 GEMM
+# Optimization on AMD RDNA 3 and RDNA 4", What We Are Computing).  A dropped,
+# doubled or misplaced stage, chunk or tile shows here even where the
+# tolerance would hide it.  The kernel each case must reach is asserted.
+PM1_PATHS = [
+    # four-wave FP8 with the K-tail instantiation (K = 3 * 128 + 16)
+    ("fp8", "tn", 5120, 5120, 400, "fp8_tn_256x256_w4", None),
+    ("fp8", "nn", 5120, 5120, 400, "fp8_nn_256x256_w4", None),
+    ("fp8", "tn", 600, 520, 400, "fp8_tn_128x128_w4_s4", None),
+    ("fp8", "nn", 600, 520, 400, "fp8_nn_256x128_w4", None),
+    # the one-round 192 tiles (K >= 4096), with and without a K tail
+    ("bf16", "tn", 1536, 8192, 4096, "bf16_tn_192x256_w4", None),
+    ("f16", "nn", 1536, 8192, 4096, "f16_nn_256x192_w4", None),
+    ("fp8", "tn", 1536, 8192, 4096, "fp8_tn_192x256_w4", None),
+    ("fp8", "tn", 8192, 1500, 4112, "fp8_tn_256x192_w4", None),
+    ("bf16", "tn", 8192, 1500, 4104, "bf16_tn_256x192_w4", None),
+    # split launches: whole 256 x 256 rounds plus a second launch along q / p
+    ("bf16", "tn", 4352, 4352, 192, "bf16_tn_256x256_w4", "q"),
+    ("bf16", "tn", 14336, 4096, 192, "bf16_tn_256x256_w4", "p"),
+    ("fp8", "tn", 4352, 4352, 384, "fp8_tn_256x256_w4", "q"),
+    ("fp8", "nn", 4096, 14336, 384, "fp8_nn_256x256_w4", "p"),
+]
+
+
+@pytest.mark.parametrize("dtype,layout,M,N,K,kern,split", PM1_PATHS,
+                         ids=lambda v: str(v) if not isinstance(v, str) or len(v) < 12 else v.split("_", 2)[-1])
+def test_pm1_bit_exact_paths(dtype, layout, M, N, K, kern, split):
+    name = kernel_name(dtype, layout, M, N, K)
+    assert name.split()[0] == kern, name
+    assert (f" from {split}=" in name) if split else (" + " not in name), name
+    p = make_problem(dtype, layout, M, N, K, seed=3100 + M % 97 + K, dist="pm1", pad=1)
+    say(f"case pm1 path {name} M={M} N={N} K={K}")
+    cij, pad = c_host(p, run_gpu(p))
+    assert pad_untouched(pad, dtype)
+    ok, _, nbad = compare(p, cij, exact=True)
+    assert ok, f"{name}: {nbad} elements differ"
+
+
+# Bit-for-bit repeatability, one case per kernel family, on random data and a
+# side stream: an LDS race (a read before a copy lands, a copy over a buffer
+# still being read) shows as two runs that differ.
+DETERMINISM = [
+    ("bf16", "tn", 5120, 5120, 512, None),       # 16-bit two-k-step stage, staged epilogue
+    ("f16", "nn", 5120, 5120, 512, None),        # transposing reads of B
+    ("fp8", "tn", 5120, 5120, 384, None),        # rolling FP8 stage
+    ("fp8", "nn", 5120, 5120, 400, None),        # rolling stage, transposing reads, K tail
+    ("fp8", "tn", 5120, 5120, 384, "scaled"),    # factors in the epilogue
+    ("fp8", "tn", 3000, 3000, 4096, "mx"),       # MX scale ring, 192 x 256
+    ("fp8", "nn", 5120, 5120, 1184, "mx"),       # MX scale ring, partial scale group
+    ("bf16", "tn", 1536, 8192, 4096, None),      # 192 x 256, direct epilogue
+    ("bf16", "tn", 1000, 1000, 2048, None),      # 128 x 128, four LDS stages
+    ("bf16", "tn", 14336, 4096, 192, None),      # split launch along p
+    ("bf16", "tn", 1000, 1000, 1001, None),      # eight-wave kernel, ragged K
+    ("bf16", "tn", 16, 3000, 4096, None),        # skinny split-K, LDS reduction
+    ("f32", "nn", 1000, 1000, 1000, None),       # FP32 MFMA kernel
+]
+
+
+@pytest.mark.parametrize("dtype,layout,M,N,K,variant", DETERMINISM)
+def test_deterministic_per_kernel_family(dtype, layout, M, N, K, variant):
+    import torch
+    from dense_gemm_02_amd import binding
+    p = make_problem(dtype, layout, M, N, K, seed=9100 + K)
+    A, B = to_dev(p.A), to_dev(p.B)
+    rng = np.random.default_rng(9)
+    if variant == "scaled":
+        sa = torch.from_numpy(_factors(rng, M)).cuda()
+        sb = torch.from_numpy(_factors(rng, N)).cuda()
+    elif variant == "mx":
+        ld = ((K // 32 + 15) // 16) * 16
+        sa = torch.from_numpy(mx_scales(rng, M, K // 32, ld).reshape(-1)).cuda()
+        sb = torch.from_numpy(mx_scales(rng, N, K // 32, ld).reshape(-1)).cuda()
+    kern = kernel_name({"scaled": "fp8s", "mx": "mx8"}.get(variant, dtype), layout, M, N, K)
+    say(f"case determinism {kern} M={M} N={N} K={K}")
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    outs = []
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            C = alloc_c(p)
+            if variant == "scaled":
+                binding.gemm_scaled(layout, M, N, K, A, p.lda, B, p.ldb, C, p.ldc, sa, sb, stream=s)
+            elif variant == "mx":
+                binding.gemm_mx(layout, M, N, K, A, p.lda, B, p.ldb, C, p.ldc, sa, ld, sb, ld, stream=s)
+            else:
+                binding.gemm(dtype, layout, M, N, K, A, p.lda, B, p.ldb, C, p.ldc, stream=s)
+            outs.append(C)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]), f"{kern}: two runs differ"
 
 
 @pytest.mark.parametrize("dtype,layout", COMBOS)
@@ -296,8 +387,7 @@ def test_fp8_scaled_against_oracle(layout, mode):
         say(f"case scaled {kernel_name('fp8s', layout, M, N, K)} mode={mode} M={M} N={N} K={K}")
         cij, pad = c_host(p, run_scaled(p, sa, sb))
         assert pad_untouched(pad, "fp8")
-        rows = sample_rows(M, seed=idx) if M * N * max(K, 1) > 5e8 else None
-        ok, err = compare_scaled(p, cij, sa, sb, rows=rows)
+        ok, err = compare_scaled(p, cij, sa, sb)
         assert ok, f"{layout} {mode} {(M, N, K)}: max err {err:.3e}"
 
 
@@ -312,8 +402,7 @@ def test_fp8_scaled_bit_exact(layout):
         sa, sb = _factors(rng, M, pow2=True), _factors(rng, N, pow2=True)
         say(f"case scaled pm1 {layout} M={M} N={N} K={K}")
         cij, _ = c_host(p, run_scaled(p, sa, sb))
-        rows = sample_rows(M, seed=idx) if M > 1000 else None
-        ok, _ = compare_scaled(p, cij, sa, sb, rows=rows, exact=True)
+        ok, _ = compare_scaled(p, cij, sa, sb, exact=True)
         assert ok, f"{(M, N, K)}: not bit-exact"
         one = np.float32([1.0])
         c1, _ = c_host(p, run_scaled(p, one, one))
@@ -394,8 +483,7 @@ def test_mxfp8_against_oracle(layout):
         say(f"case mx {kernel_name('mx8', layout, M, N, K)} M={M} N={N} K={K} ld={ld}")
         cij, pad = c_host(p, run_mx(p, SA, ld, SB, ld))
         assert pad_untouched(pad, "fp8")
-        rows = sample_rows(M, seed=idx) if M * N * max(K, 1) > 5e8 else None
-        ok, err = compare_mx(p, cij, SA, ld, SB, ld, rows=rows)
+        ok, err = compare_mx(p, cij, SA, ld, SB, ld)
         assert ok, f"{layout} {(M, N, K)}: max err {err:.3e}"
 
 
@@ -412,8 +500,7 @@ def test_mxfp8_bit_exact(layout):
         SA, SB = mx_scales(rng, M, nb, ld, 124, 131), mx_scales(rng, N, nb, ld, 124, 131)
         say(f"case mx pm1 {layout} M={M} N={N} K={K}")
         cij, _ = c_host(p, run_mx(p, SA, ld, SB, ld))
-        rows = sample_rows(M, seed=idx) if M > 1000 else None
-        ok, _ = compare_mx(p, cij, SA, ld, SB, ld, rows=rows, exact=True)
+        ok, _ = compare_mx(p, cij, SA, ld, SB, ld, exact=True)
         assert ok, f"{(M, N, K)}: not bit-exact"
         if K >= 256:
             one = np.full((max(M, N), ld), 127, np.uint8)
@@ -492,3 +579,34 @@ def test_leading_dimensions_at_the_descriptor_limit(dtype, layout):
     assert ok, f"max err {err:.3e}, {nbad} bad"
     del A, B
     torch.cuda.empty_cache()
+
+
+# The tensor-level calls refuse, before any launch, device tensors too small
+# for what the call would read or write, and host, float64 or strided scale
+# factors.
+def test_binding_rejects_bad_device_tensors():
+    import torch
+    from dense_gemm_02_amd import binding, matmul
+    M, N, K = 64, 48, 256
+    A = torch.zeros(M * K, dtype=torch.int16, device="cuda")
+    B = torch.zeros(N * K, dtype=torch.int16, device="cuda")
+    C = torch.zeros(N * M, dtype=torch.int16, device="cuda")
+    binding.gemm("bf16", "tn", M, N, K, A, K, B, K, C, M)
+    for a, b, c in ((A[: M * K - 1], B, C), (A, B[: N * K - 8], C), (A, B, C[: N * M - 1])):
+        with pytest.raises(ValueError):
+            binding.gemm("bf16", "tn", M, N, K, a, K, b, K, c, M)
+    a8 = torch.zeros((M, K), dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    b8 = torch.zeros((N, K), dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn).t()
+    good = torch.ones(M, device="cuda")
+    for bad in (torch.ones(M), torch.ones(M, dtype=torch.float64, device="cuda"),
+                torch.ones(2 * M, device="cuda")[::2]):
+        with pytest.raises(TypeError):
+            matmul(a8, b8, scale_a=bad, scale_b=torch.ones(1, device="cuda"))
+    with pytest.raises(ValueError):
+        matmul(a8, b8, scale_a=good[:5], scale_b=torch.ones(1, device="cuda"))
+    c32 = torch.zeros(M * N, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        binding.gemm_mx("tn", M, N, K, a8.view(torch.uint8).reshape(-1), K, b8.t().contiguous().view(torch.uint8),
+                        K, c32, M, torch.zeros(M * 16 - 1, dtype=torch.uint8, device="cuda"), 16,
+                        torch.zeros(N * 16, dtype=torch.uint8, device="cuda"), 16)
+    torch.cuda.synchronize()
