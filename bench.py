@@ -8,12 +8,17 @@ FP16 output.  BF16 TN and FP8 E4M3 TN at the same size are timed in the
 same run and reported under "per_dtype".
 
 Timing: W untimed warm-up steps, then exactly K steps between two
-synchronisations, with HIP events recorded on the stream the kernels run on.
-TFLOP/s = 2*M*N*K / t.  Prints one JSON line.
+synchronisations, with HIP events recorded on the stream the kernels run on
+(one before each launch, so the mean, min and median per launch are
+known).  TFLOP/s = 2*M*N*K / t.  After the timed region the engine clock is
+measured with the library's clock probe right behind launches of the same
+workload, and each throughput is also given as a fraction of the MFMA peak
+at that clock.  Prints one JSON line.
 
-cpu_baseline: the CPU oracle (test infrastructure, never tuned) timed on a
-bounded sample of whole output rows of the same workload, on this host's
-cores; its rate is scaled to TFLOP/s of useful work.
+cpu_baseline: the CPU oracle (test infrastructure, never tuned) timed on
+whole output rows of the same workload, as many as fit about 25 s (all of
+them when the host is fast enough), on every core the process may use; its
+rate is scaled to TFLOP/s of useful work.
 """
 
 from __future__ import annotations
@@ -35,6 +40,8 @@ METRIC = "GEMM TFLOP/s + % of dense MFMA peak (FP16/BF16/FP8, M=N=K=8192)"
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}
 HBM_GBS = 8000.0
+# Engine clock the published MFMA peaks assume (MHz).
+PEAK_CLOCK_MHZ = 2400.0
 WORKLOADS = {
     "f16": ("f16", "tn", 8192, 8192, 8192, 3, "normal"),
     "bf16": ("bf16", "tn", 8192, 8192, 8192, 4, "normal"),
@@ -142,43 +149,91 @@ def time_gemm(dtype, steps, warmup, spec=None, rotate=1):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    # One event before every launch and one after the last: the region from
+    # the first to the last event is the timed one (mean = its length / K);
+    # consecutive events give each launch's own time (min, median).
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(steps):
+    for i in range(steps):
+        ev[i].record(stream)
         step()
-    e1.record(stream)
+    ev[steps].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / steps
+    ms = ev[0].elapsed_time(ev[steps]) / steps
+    each = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     flops = p.flops
-    return p, {"ms_per_launch": ms, "tflops": flops / (ms * 1e-3) / 1e12, "wall_s": wall}
+    res = {"ms_per_launch": ms, "tflops": flops / (ms * 1e-3) / 1e12, "wall_s": wall,
+           "min_ms": each[0], "median_ms": each[len(each) // 2] if steps % 2 else
+           0.5 * (each[steps // 2 - 1] + each[steps // 2]), "max_ms": each[-1]}
+    res["clock_mhz"] = engine_clock(step, stream)
+    return p, res
 
 
-def cpu_baseline(dtype, target_s=12.0):
-    """The oracle on whole output rows of the same workload, timed wall-clock."""
+def engine_clock(step, stream, pairs=8):
+    """Engine clock (MHz) right after launches of the timed workload: each of
+    `pairs` launches is followed by the library's clock probe (one wave
+    comparing the core clock counter with the 100 MHz real-time counter over
+    ~20 us); the median is returned.  Runs after the timed region."""
+    import torch
+    from dense_gemm_02_amd import binding
+    L = binding.load_library()
+    out = torch.zeros(3 * pairs, dtype=torch.int64, device="cuda")
+    for i in range(pairs):
+        step()
+        st = L.dgemm_clock_probe(out.data_ptr() + 24 * i, 20000, stream.cuda_stream)
+        if st != 0:
+            raise binding.DgemmError(st, "dgemm_clock_probe")
+    torch.cuda.synchronize()
+    v = out.view(pairs, 3).cpu().numpy()
+    mhz = sorted(100.0 * float(c) / float(r) for c, r, _ in v if r > 0)
+    return mhz[len(mhz) // 2] if mhz else None
+
+
+def cpu_baseline(dtype, target_s=25.0):
+    """The oracle (never tuned) on the headline workload, timed wall-clock on
+    every core this process may run on.  A short run on 32 rows measures its
+    rate; then whole output rows, up to all of them, are computed in one
+    timed call sized to about `target_s` seconds, so the default bench stays
+    within minutes on hosts where the full product would take longer."""
     import oracle
     from dense_gemm_02_amd import inputs
     dt, layout, M, N, K, seed, dist = WORKLOADS[dtype]
     p = inputs.make(dt, layout, M, N, K, seed, dist)
     fmt = {"f32": oracle.F32, "f16": oracle.F16, "bf16": oracle.BF16, "fp8": oracle.E4M3}[dt]
     lay = oracle.TN if layout == "tn" else oracle.NN
-    threads = oracle.max_threads()
+    cores = len(os.sched_getaffinity(0))
     rng = np.random.default_rng(0)
-    nrows = 8
-    while True:
-        rows = np.sort(rng.choice(M, nrows, replace=False))
-        t0 = time.perf_counter()
-        oracle.gemm(fmt, lay, M, N, K, p.A, p.lda, p.B, p.ldb, rows=rows, threads=threads)
-        dt_s = time.perf_counter() - t0
-        if dt_s >= target_s * 0.5 or nrows >= M:
-            break
-        nrows = min(M, max(nrows * 2, int(nrows * target_s / max(dt_s, 1e-3))))
+    probe = np.sort(rng.choice(M, 32, replace=False))
+    t0 = time.perf_counter()
+    oracle.gemm(fmt, lay, M, N, K, p.A, p.lda, p.B, p.ldb, rows=probe, threads=cores)
+    per_row = (time.perf_counter() - t0) / len(probe)
+    nrows = int(min(M, max(64, target_s / max(per_row, 1e-6))))
+    rows = None if nrows >= M else np.sort(rng.choice(M, nrows, replace=False))
+    t0 = time.perf_counter()
+    oracle.gemm(fmt, lay, M, N, K, p.A, p.lda, p.B, p.ldb, rows=rows, threads=cores)
+    dt_s = time.perf_counter() - t0
+    nrows = M if rows is None else nrows
     flops = 2.0 * nrows * N * K
-    return {"value": flops / dt_s / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{nrows} of {M} output rows (all {N} columns, K={K}) of {dtype} {layout} "
-                      f"{M}x{N}x{K}, {dt_s:.1f} s wall"}
+    what = ("the full product" if rows is None else
+            f"{nrows} of {M} output rows (all {N} columns, K={K}; the full product would take "
+            f"~{per_row * M:.0f} s)")
+    return {"value": flops / dt_s / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{what} of {dtype} {layout} {M}x{N}x{K}, {dt_s:.1f} s wall on {cores} threads"}
+
+
+def timing_fields(r, peak=None):
+    """Per-launch statistics and the measured engine clock; with a peak, the
+    throughput as a fraction of the peak at that clock (the published peak
+    scaled by measured clock / 2400 MHz)."""
+    out = {"mean_ms": round(r["ms_per_launch"], 5), "min_ms": round(r["min_ms"], 5),
+           "median_ms": round(r["median_ms"], 5), "max_ms": round(r["max_ms"], 5),
+           "clock_mhz": None if r["clock_mhz"] is None else round(r["clock_mhz"], 1)}
+    if peak is not None and r["clock_mhz"]:
+        at = peak * r["clock_mhz"] / PEAK_CLOCK_MHZ
+        out["peak_at_clock"] = round(at, 1)
+        out["frac_at_clock"] = round(r["tflops"] / at, 4)
+    return out
 
 
 def main():
@@ -228,12 +283,14 @@ def main():
                  "frac": round(r["tflops"] / PEAK_TFLOPS[spec[0]], 4), "traffic": load_traffic(args.workload)})
         print(json.dumps({"workload": args.workload, "value": round(r["tflops"], 2), "unit": "TFLOP/s",
                           "ms_per_launch": round(r["ms_per_launch"], 5), "steps": args.steps,
+                          "timing": timing_fields(r, None if skinny else PEAK_TFLOPS[spec[0]]),
                           "warmup": args.warmup, "rotated_B_copies": ROTATE if skinny else 1,
                           "roofline": roof}), flush=True)
         return
 
     p, head = time_gemm(args.dtype, args.steps, args.warmup)
-    print(f"[bench] {args.dtype}: {head['ms_per_launch']:.4f} ms/launch, {head['tflops']:.1f} TFLOP/s",
+    print(f"[bench] {args.dtype}: {head['ms_per_launch']:.4f} ms/launch, {head['tflops']:.1f} TFLOP/s, "
+          f"min {head['min_ms']:.4f} median {head['median_ms']:.4f} ms, clock {head['clock_mhz']} MHz",
           file=sys.stderr, flush=True)
     per = {}
     if not args.only:
@@ -242,8 +299,9 @@ def main():
                 continue
             _, r = time_gemm(d, args.steps, args.warmup)
             per[d] = {"tflops": round(r["tflops"], 1), "ms_per_launch": round(r["ms_per_launch"], 4),
-                      "frac_of_peak": round(r["tflops"] / PEAK_TFLOPS[d], 4)}
-            print(f"[bench] {d}: {r['ms_per_launch']:.4f} ms/launch, {r['tflops']:.1f} TFLOP/s",
+                      "frac_of_peak": round(r["tflops"] / PEAK_TFLOPS[d], 4), **timing_fields(r, PEAK_TFLOPS[d])}
+            print(f"[bench] {d}: {r['ms_per_launch']:.4f} ms/launch, {r['tflops']:.1f} TFLOP/s, "
+                  f"min {r['min_ms']:.4f} median {r['median_ms']:.4f} ms, clock {r['clock_mhz']} MHz",
                   file=sys.stderr, flush=True)
 
     workload = f"{p.dtype}_{p.layout}_{p.M}x{p.N}x{p.K}"
@@ -269,6 +327,7 @@ def main():
                    "inputs": f"{p.meta['dist']} seed {p.meta['seed']}", "accumulate": "f32",
                    "kernel_sources": kernel_source_hash()},
         "roofline": roof,
+        "timing": timing_fields(head, PEAK_TFLOPS[args.dtype]),
         "cpu_baseline": cpu,
         "per_dtype": per,
     }

@@ -13,7 +13,7 @@
 #include "gemm_f32.hpp"
 #include "gemm_mfma.hpp"
 #include "gemm_skinny.hpp"
-#include "gemm_tn.hpp"
+#include "launch.hpp"
 
 namespace dg {
 namespace {
@@ -37,15 +37,6 @@ constexpr int64_t kMaxDescBytes = (int64_t(1) << 31) - 64;
 int in_elem(int dt) { return dt == DT_F32 ? 4 : (is_fp8(dt) ? 1 : 2); }
 int out_elem(int dt) { return (dt == DT_F32 || is_fp8(dt)) ? 4 : 2; }
 
-// A launchable configuration: a kernel symbol plus its tile geometry.  Every
-// kernel runs one workgroup per tile.
-struct Launch {
-  const void* fn;
-  const char* name;
-  int bp, bq, threads, lds;
-  bool p_trans;
-};
-
 // ---- kernel table ------------------------------------------------------------
 // 16-bit and FP8: 256 x 256 block tile, 8 waves as 2 (p) x 4 (q), wave tile
 // 128 x 64 (4 x 2 MFMA tiles of 32 x 32), 128 bytes of K per stage, two LDS
@@ -58,17 +49,6 @@ Launch mfma_launch(const char* name) {
   using Cfg = MfmaCfg<Op, 256, 256, 2, 4, PT>;
   return Launch{(const void*)&gemm_mfma_kernel<Op, 256, 256, 2, 4, PT>, name, 256, 256, Cfg::NT,
                 2 * Cfg::STAGE, PT};
-}
-
-// Four-wave kernel (gemm_tn.hpp), one tile per workgroup.  `kt`: K is not a
-// whole number of stages, so the copies need tail masks (a separate
-// instantiation: without a tail they cost nothing).
-template <class Op, bool PKM, int BP, int BQ, int NS = 2>
-Launch tn_launch(const char* name, bool kt) {
-  using Cfg = TnCfg<Op, PKM, BP, BQ, NS>;
-  const void* fn = kt ? (const void*)&gemm_tn_kernel<Op, PKM, BP, BQ, NS, true>
-                      : (const void*)&gemm_tn_kernel<Op, PKM, BP, BQ, NS, false>;
-  return Launch{fn, name, BP, BQ, Cfg::NT, Cfg::LDS, PKM};
 }
 
 // Whether K ends inside a stage of the four-wave kernel (stages of 128 bytes
@@ -112,7 +92,6 @@ struct TileChoice {
   double rate;          // CU throughput relative to 256 x 256
   int max_rounds;       // 0: any number of rounds
 };
-constexpr int kNumTiles = 6;
 constexpr TileChoice kTiles[kNumTiles] = {{256, 256, 1, 1.00, 0},
                                           {256, 128, 1, 0.76, 0},
                                           {128, 128, 2, 0.78, 0},
@@ -151,28 +130,6 @@ unsigned tile_mask(int dt, bool nn, int64_t K) {
   return (dt == DT_MX8 ? 0b0101u : 0b1101u) | t192;
 }
 
-// The four-wave launch of kTiles entry `idx` (one tile_mask allows).
-template <class Op, bool PKM>
-Launch tn_make(const char* const names[kNumTiles], int idx, bool kt) {
-  if constexpr (PKM && Op::ELEM == 1) {
-    if (idx == 1) return tn_launch<Op, PKM, 256, 128>(names[1], kt);
-    if (idx == 5) return tn_launch<Op, PKM, 256, 192>(names[5], kt);
-    return tn_launch<Op, PKM, 256, 256>(names[0], kt);
-  } else {
-    switch (idx) {
-      case 4:
-        if constexpr (!PKM) return tn_launch<Op, PKM, 192, 256>(names[4], kt);
-        [[fallthrough]];
-      case 5: return tn_launch<Op, PKM, 256, 192>(names[5], kt);
-      case 2: return tn_launch<Op, PKM, 128, 128>(names[2], kt);
-      case 3:
-        if constexpr (!Op::MX) return tn_launch<Op, PKM, 128, 128, 4>(names[3], kt);
-        [[fallthrough]];
-      default: return tn_launch<Op, PKM, 256, 256>(names[0], kt);
-    }
-  }
-}
-
 template <bool PT>
 Launch f32_launch(const char* name) {
   using Cfg = F32Cfg<128, 128, 2, 2, PT>;
@@ -196,42 +153,16 @@ Launch select_skinny(int dt, int64_t M) {
   return M <= 16 ? skinny_launch<OpBF16, 1>("bf16_tn_skinny16") : skinny_launch<OpBF16, 2>("bf16_tn_skinny32");
 }
 
+// The four-wave kernel (gemm_tn.hpp) for kTiles entry `idx` (one tile_mask
+// allows); its instantiations live in four_wave.hip, one translation unit
+// per format and layout.
 Launch four_wave(int dt, bool nn, int idx, bool kt) {
-  static const char* const f16n[kNumTiles] = {"f16_nn_256x256_w4", nullptr, "f16_nn_128x128_w4",
-                                             "f16_nn_128x128_w4_s4", nullptr, "f16_nn_256x192_w4"};
-  static const char* const bf16n[kNumTiles] = {"bf16_nn_256x256_w4", nullptr, "bf16_nn_128x128_w4",
-                                             "bf16_nn_128x128_w4_s4", nullptr, "bf16_nn_256x192_w4"};
-  static const char* const fp8n[kNumTiles] = {"fp8_nn_256x256_w4", "fp8_nn_256x128_w4", nullptr,
-                                             nullptr, nullptr, "fp8_nn_256x192_w4"};
-  static const char* const fp8sn[kNumTiles] = {"fp8s_nn_256x256_w4", "fp8s_nn_256x128_w4", nullptr,
-                                             nullptr, nullptr, "fp8s_nn_256x192_w4"};
-  static const char* const mxn[kNumTiles] = {"mx8_nn_256x256_w4", "mx8_nn_256x128_w4", nullptr,
-                                             nullptr, nullptr, "mx8_nn_256x192_w4"};
-  static const char* const f16t[kNumTiles] = {"f16_tn_256x256_w4", nullptr, "f16_tn_128x128_w4",
-                                             "f16_tn_128x128_w4_s4", "f16_tn_192x256_w4", "f16_tn_256x192_w4"};
-  static const char* const bf16t[kNumTiles] = {"bf16_tn_256x256_w4", nullptr, "bf16_tn_128x128_w4",
-                                              "bf16_tn_128x128_w4_s4", "bf16_tn_192x256_w4", "bf16_tn_256x192_w4"};
-  static const char* const fp8t[kNumTiles] = {"fp8_tn_256x256_w4", nullptr, "fp8_tn_128x128_w4",
-                                              "fp8_tn_128x128_w4_s4", "fp8_tn_192x256_w4", "fp8_tn_256x192_w4"};
-  static const char* const fp8st[kNumTiles] = {"fp8s_tn_256x256_w4", nullptr, "fp8s_tn_128x128_w4",
-                                               "fp8s_tn_128x128_w4_s4", "fp8s_tn_192x256_w4", "fp8s_tn_256x192_w4"};
-  static const char* const mxt[kNumTiles] = {"mx8_tn_256x256_w4", nullptr, "mx8_tn_128x128_w4", nullptr,
-                                             "mx8_tn_192x256_w4", "mx8_tn_256x192_w4"};
-  if (nn) {
-    switch (dt) {
-      case DT_F16: return tn_make<OpF16, true>(f16n, idx, kt);
-      case DT_BF16: return tn_make<OpBF16, true>(bf16n, idx, kt);
-      case DT_FP8S: return tn_make<OpFP8S, true>(fp8sn, idx, kt);
-      case DT_MX8: return tn_make<OpMX8, true>(mxn, idx, kt);
-      default: return tn_make<OpFP8, true>(fp8n, idx, kt);
-    }
-  }
   switch (dt) {
-    case DT_F16: return tn_make<OpF16, false>(f16t, idx, kt);
-    case DT_BF16: return tn_make<OpBF16, false>(bf16t, idx, kt);
-    case DT_FP8S: return tn_make<OpFP8S, false>(fp8st, idx, kt);
-    case DT_MX8: return tn_make<OpMX8, false>(mxt, idx, kt);
-    default: return tn_make<OpFP8, false>(fp8t, idx, kt);
+    case DT_F16: return nn ? four_wave_f16_nn(idx, kt) : four_wave_f16_tn(idx, kt);
+    case DT_BF16: return nn ? four_wave_bf16_nn(idx, kt) : four_wave_bf16_tn(idx, kt);
+    case DT_FP8S: return nn ? four_wave_fp8s_nn(idx, kt) : four_wave_fp8s_tn(idx, kt);
+    case DT_MX8: return nn ? four_wave_mx8_nn(idx, kt) : four_wave_mx8_tn(idx, kt);
+    default: return nn ? four_wave_fp8_nn(idx, kt) : four_wave_fp8_tn(idx, kt);
   }
 }
 
@@ -264,8 +195,7 @@ Choice choose(int dt, int layout, int64_t M, int64_t N, int64_t K) {
       return c;
     }
     if (K < 256) {
-      c.L = nn ? tn_launch<OpMX8, true, 256, 128>("mx8_nn_256x128_w4", k_tail(dt, K))
-               : tn_launch<OpMX8, false, 128, 128>("mx8_tn_128x128_w4", k_tail(dt, K));
+      c.L = four_wave(dt, nn, nn ? 1 : 2, k_tail(dt, K));
       return c;
     }
   }
@@ -470,10 +400,38 @@ int run(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
   return launch(pl.L2, pl.g2, pl.grid2, stream);
 }
 
+// Clock probe (diagnostics): one wave reads the core clock counter and the
+// constant 100 MHz real-time counter around a chain of dependent FMAs, so
+// the ratio of the two differences times 100 MHz is the engine clock while
+// the wave ran.  out[0] = core clock ticks, out[1] = real-time ticks,
+// out[2] = the chain's result (keeps the chain alive).
+__global__ void __launch_bounds__(64) clock_probe_kernel(unsigned long long* out, int iters) {
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  float x = (float)threadIdx.x;
+  for (int i = 0; i < iters; ++i) x = __builtin_fmaf(x, 1.0000001f, 1e-7f);
+  const uint64_t c1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    out[0] = c1 - c0;
+    out[1] = r1 - r0;
+    out[2] = (unsigned long long)__builtin_bit_cast(uint32_t, x);
+  }
+}
+
 }  // namespace
 }  // namespace dg
 
 extern "C" {
+
+int dgemm_clock_probe(unsigned long long* out, int iters, void* stream) {
+  if (out == nullptr) return DGEMM_ERR_NULL_POINTER;
+  if (iters < 0) return DGEMM_ERR_INVALID_DIM;
+  hipLaunchKernelGGL(dg::clock_probe_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, out, iters);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return dg::hip_failed(err);
+  return DGEMM_OK;
+}
 
 int gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B, int64_t ldb, float* C,
              int64_t ldc, int layout, void* stream) {

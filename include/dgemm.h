@@ -169,6 +169,18 @@ const char* dgemm_hip_error_string(int code);
  * 2 bf16, 3 fp8, 4 fp8 with scale factors, 5 MXFP8.  Returns 0, or a
  * dgemm_status for invalid arguments.
  */
+/*
+ * dgemm_clock_probe (diagnostics, used to report the engine clock next to
+ * measured throughput): enqueues on `stream` one 64-lane wave that reads the
+ * core clock counter and the constant 100 MHz real-time counter around
+ * `iters` dependent FMAs and writes three 64-bit values to the DEVICE
+ * pointer `out`: core clock ticks, real-time ticks, and a value that only
+ * keeps the FMA chain alive.  Engine clock in Hz = out[0] / out[1] * 1e8.
+ * Returns DGEMM_ERR_NULL_POINTER for a NULL out, DGEMM_ERR_INVALID_DIM for
+ * iters < 0, DGEMM_ERR_HIP for a launch error.
+ */
+int dgemm_clock_probe(unsigned long long* out, int iters, void* stream);
+
 int dgemm_tile_map(int64_t tiles_p, int64_t tiles_q, int64_t group, int64_t pid,
                    int64_t* tile_p, int64_t* tile_q);
 int64_t dgemm_lds_bytes(int bm, int bn, int bk, int elem, int pad_bytes, int buffers);
