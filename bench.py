@@ -121,6 +121,8 @@ def time_gemm(dtype, steps, warmup, spec=None, rotate=1):
     import torch
     from dense_gemm_02_amd import binding
     p, A, B, C = make_inputs(dtype, spec)
+    print(f"[bench] {p.dtype} {p.layout} {p.M}x{p.N}x{p.K}: operands on the device, launching", file=sys.stderr,
+          flush=True)
     Bs = [B] + [B.clone() for _ in range(rotate - 1)]
     stream = torch.cuda.current_stream()
     it = [0]
@@ -258,7 +260,10 @@ def main():
     import torch
     from dense_gemm_02_amd import binding
     binding.load_library()
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU: torch sees none", file=sys.stderr, flush=True)
+        sys.exit(3)
+    print(f"[bench] device: {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
     if args.calibrate_copy:
         n = args.calibrate_copy << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")

@@ -592,7 +592,13 @@ def test_binding_rejects_bad_device_tensors():
     B = torch.zeros(N * K, dtype=torch.int16, device="cuda")
     C = torch.zeros(N * M, dtype=torch.int16, device="cuda")
     binding.gemm("bf16", "tn", M, N, K, A, K, B, K, C, M)
-    for a, b, c in ((A[: M * K - 1], B, C), (A, B[: N * K - 8], C), (A, B, C[: N * M - 1])):
+
+    def short(n):
+        return torch.zeros(n, dtype=torch.int16, device="cuda")
+
+    # (a view counts the storage behind it: a slice of A still covers A)
+    for a, b, c in ((short(M * K - 1), B, C), (A, short(N * K - 8), C), (A, B, short(N * M - 1)),
+                    (A[1:], B, C)):
         with pytest.raises(ValueError):
             binding.gemm("bf16", "tn", M, N, K, a, K, b, K, c, M)
     a8 = torch.zeros((M, K), dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
