@@ -179,13 +179,10 @@ def engine_clock(step, stream, pairs=8):
     ~20 us); the median is returned.  Runs after the timed region."""
     import torch
     from dense_gemm_02_amd import binding
-    L = binding.load_library()
-    out = torch.zeros(3 * pairs, dtype=torch.int64, device="cuda")
+    out = torch.zeros((pairs, 3), dtype=torch.int64, device="cuda")
     for i in range(pairs):
         step()
-        st = L.dgemm_clock_probe(out.data_ptr() + 24 * i, 20000, stream.cuda_stream)
-        if st != 0:
-            raise binding.DgemmError(st, "dgemm_clock_probe")
+        binding.clock_probe(out[i], 20000, stream=stream)
     torch.cuda.synchronize()
     v = out.view(pairs, 3).cpu().numpy()
     mhz = sorted(100.0 * float(c) / float(r) for c, r, _ in v if r > 0)

@@ -71,6 +71,8 @@ def load_library():
     L.dgemm_lds_bytes.restype = i64
     L.dgemm_kernel_config.argtypes = [ci, ci, i64, i64, i64, ctypes.c_char_p, i64]
     L.dgemm_kernel_config.restype = ci
+    L.dgemm_clock_probe.argtypes = [vp, ci, vp]
+    L.dgemm_clock_probe.restype = ci
     _lib = L
     return L
 
@@ -231,6 +233,20 @@ def gemm_mx(layout, M, N, K, A, lda, B, ldb, C, ldc, scale_a, ldsa, scale_b, lds
         _need(scale_b, N * ldsb, "scale_b")
     gemm_mxfp8(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, scale_a.data_ptr(), ldsa,
                scale_b.data_ptr(), ldsb, layout, stream)
+
+
+def clock_probe(out, iters=20000, stream=None):
+    """Enqueue the library's clock probe, writing (core clock ticks,
+    real-time ticks at 100 MHz, chain value) to the first three elements of
+    ``out`` (an int64 device tensor); the engine clock in MHz is then
+    out[0] / out[1] * 100 after the stream has run it."""
+    import torch
+    _device_tensors("out", out)
+    if out.dtype != torch.int64 or out.numel() < 3 or not out.is_contiguous():
+        raise TypeError("out must be a contiguous int64 device tensor of at least 3 elements")
+    st = load_library().dgemm_clock_probe(out.data_ptr(), int(iters), _stream_handle(stream))
+    if st != 0:
+        raise DgemmError(st, "dgemm_clock_probe")
 
 
 _TORCH_DT = None

@@ -330,3 +330,23 @@ def test_binding_factor_checks():
         binding._factor_vector(torch.ones(18)[::2], 9, "scale_a")
     with pytest.raises(ValueError):
         binding._factor_vector(torch.ones(8), 9, "scale_a")
+
+
+def test_binding_declares_every_entry_point():
+    # ctypes passes an undeclared argument as a C int: a 64-bit device
+    # pointer would be cut to its low 32 bits.  Every function the header
+    # declares must have its argument and result types set by the binding,
+    # one per parameter, a pointer type wherever the header has a pointer.
+    from dense_gemm_02_amd import binding
+    L = binding.load_library()
+    hdr = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "dgemm.h")).read(), flags=re.S)
+    decls = re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(\w+)\(([^)]*)\);", hdr, re.M)
+    assert len(decls) >= 13
+    for name, params in decls:
+        fn = getattr(L, name)
+        assert fn.argtypes is not None and fn.restype is not None, name
+        ps = [p.strip() for p in params.split(",") if p.strip() and p.strip() != "void"]
+        assert len(fn.argtypes) == len(ps), name
+        for p, t in zip(ps, fn.argtypes):
+            is_ptr = t in (ctypes.c_void_p, ctypes.c_char_p) or t.__name__.startswith("LP_")
+            assert is_ptr == ("*" in p), (name, p, t)

@@ -616,3 +616,22 @@ def test_binding_rejects_bad_device_tensors():
                         K, c32, M, torch.zeros(M * 16 - 1, dtype=torch.uint8, device="cuda"), 16,
                         torch.zeros(N * 16, dtype=torch.uint8, device="cuda"), 16)
     torch.cuda.synchronize()
+
+
+# The clock probe (diagnostics): both counters advance and the ratio is an
+# engine clock in a plausible range.
+def test_clock_probe_reports_an_engine_clock():
+    import torch
+    from dense_gemm_02_amd import binding
+    out = torch.zeros((2, 3), dtype=torch.int64, device="cuda")
+    say("case clock probe")
+    binding.clock_probe(out[0], 20000)
+    binding.clock_probe(out[1], 0)
+    torch.cuda.synchronize()
+    c, r, _ = (int(v) for v in out[0].cpu())
+    assert c > 0 and r > 0
+    assert 300.0 < 100.0 * c / r < 3000.0, (c, r)
+    with pytest.raises(TypeError):
+        binding.clock_probe(torch.zeros(3, dtype=torch.int32, device="cuda"))
+    with pytest.raises(TypeError):
+        binding.clock_probe(torch.zeros(2, dtype=torch.int64, device="cuda"))
