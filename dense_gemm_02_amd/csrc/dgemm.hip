@@ -270,6 +270,13 @@ struct MxScales {
   int64_t ldsb;
 };
 
+// p + n, leaving a null pointer null (the host-only planning helpers plan
+// without operands).
+template <class T>
+T* advance(T* p, int64_t n) {
+  return p ? p + n : p;
+}
+
 // Validation in the documented order, then the (P, Q, D) mapping.
 int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
          void* C, int64_t ldc, int layout, Plan* out, bool check_pointers, const Scales* sc = nullptr,
@@ -349,15 +356,15 @@ int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
     GemmArgs g2 = g;
     const int64_t x0 = ch.at;
     if (!ch.split_p) {
-      g2.Q = g.Q + x0 * g.ldq;
-      g2.C = (char*)C + x0 * ldc * oe;
+      g2.Q = advance(g.Q, x0 * g.ldq);
+      g2.C = advance((char*)C, x0 * ldc * oe);
       g2.Qn = g.Qn - x0;
       if (g.sq && g.sq_row) g2.sq = g.sq + x0;
       if (g.msq) g2.msq = g.msq + x0 * g.ldsq;
       g.Qn = x0;
     } else {
-      g2.P = g.P + (ch.L.p_trans ? x0 * e : x0 * g.ldp);
-      g2.C = (char*)C + x0 * oe;
+      g2.P = advance(g.P, ch.L.p_trans ? x0 * e : x0 * g.ldp);
+      g2.C = advance((char*)C, x0 * oe);
       g2.Pn = g.Pn - x0;
       if (g.sp && g.sp_row) g2.sp = g.sp + x0;
       if (g.msp) g2.msp = g.msp + x0 * g.ldsp;

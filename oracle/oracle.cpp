@@ -181,7 +181,7 @@ int oracle_gemm(int in_fmt, int out_fmt, int layout, int64_t M, int64_t N, int64
     const int64_t rn = (nrows - r0) < 4 ? (nrows - r0) : 4;
     for (int64_t j = 0; j < N; ++j) {
       double acc[4] = {0, 0, 0, 0}, aab[4] = {0, 0, 0, 0};
-      const float* bj = &b[(size_t)j * K];
+      const float* bj = b.data() + (size_t)j * K;   // (no element when K == 0)
       for (int64_t k = 0; k < K; ++k) {
         const double bv = (double)bj[k];
         for (int64_t q = 0; q < rn; ++q) {
