@@ -10,10 +10,10 @@ same run and reported under "per_dtype".
 Timing: W untimed warm-up steps, then exactly K steps between two
 synchronisations, with HIP events recorded on the stream the kernels run on
 (one before each launch, so the mean, min and median per launch are
-known).  TFLOP/s = 2*M*N*K / t.  After the timed region the engine clock is
-measured with the library's clock probe right behind launches of the same
-workload, and each throughput is also given as a fraction of the MFMA peak
-at that clock.  Prints one JSON line.
+known).  TFLOP/s = 2*M*N*K / t.  After the timed region one more launch runs
+with the library's clock trace on, which gives the engine clock the kernel
+ran at (per workgroup, median); each throughput is also given as a fraction
+of the MFMA peak at that clock.  Prints one JSON line.
 
 cpu_baseline: the CPU oracle (test infrastructure, never tuned) timed on
 whole output rows of the same workload, as many as fit about 25 s (all of
@@ -168,25 +168,42 @@ def time_gemm(dtype, steps, warmup, spec=None, rotate=1):
     res = {"ms_per_launch": ms, "tflops": flops / (ms * 1e-3) / 1e12, "wall_s": wall,
            "min_ms": each[0], "median_ms": each[len(each) // 2] if steps % 2 else
            0.5 * (each[steps // 2 - 1] + each[steps // 2]), "max_ms": each[-1]}
-    res["clock_mhz"] = engine_clock(step, stream)
+    res["clock_mhz"] = engine_clock(step, stream, kernel_grid(p))
     return p, res
 
 
-def engine_clock(step, stream, pairs=8):
-    """Engine clock (MHz) right after launches of the timed workload: each of
-    `pairs` launches is followed by the library's clock probe (one wave
-    comparing the core clock counter with the 100 MHz real-time counter over
-    ~20 us); the median is returned.  Runs after the timed region."""
+def kernel_grid(p):
+    """Workgroups of the main launch of this workload (from the library's
+    own description of the launch)."""
+    import ctypes
+    import re
+    from dense_gemm_02_amd import binding
+    code = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}[p.dtype]
+    buf = ctypes.create_string_buffer(512)
+    binding.load_library().dgemm_kernel_config(code, 1 if p.layout == "tn" else 0, p.M, p.N, p.K, buf, 512)
+    m = re.search(r"grid=(\d+)", buf.value.decode())
+    return int(m.group(1)) if m else 1
+
+
+def engine_clock(step, stream, grid):
+    """Engine clock (MHz) the GEMM itself ran at: one more launch of the timed
+    workload (after the timed region) with the library's clock trace on;
+    each workgroup's core-clock ticks over its real-time ticks (100 MHz),
+    median over the workgroups."""
+    import numpy as np
     import torch
     from dense_gemm_02_amd import binding
-    out = torch.zeros((pairs, 3), dtype=torch.int64, device="cuda")
-    for i in range(pairs):
-        step()
-        binding.clock_probe(out[i], 20000, stream=stream)
+    buf = torch.zeros(4 * grid, dtype=torch.int64, device="cuda")
     torch.cuda.synchronize()
-    v = out.view(pairs, 3).cpu().numpy()
-    mhz = sorted(100.0 * float(c) / float(r) for c, r, _ in v if r > 0)
-    return mhz[len(mhz) // 2] if mhz else None
+    binding.trace_clock(buf)
+    try:
+        step()
+        torch.cuda.synchronize()
+    finally:
+        binding.trace_clock(None)
+    mhz = binding.traced_clock_mhz(buf, grid)
+    mhz = mhz[np.isfinite(mhz)]
+    return float(np.median(mhz)) if mhz.size else None
 
 
 def cpu_baseline(dtype, target_s=25.0):

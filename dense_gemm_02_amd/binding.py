@@ -71,8 +71,8 @@ def load_library():
     L.dgemm_lds_bytes.restype = i64
     L.dgemm_kernel_config.argtypes = [ci, ci, i64, i64, i64, ctypes.c_char_p, i64]
     L.dgemm_kernel_config.restype = ci
-    L.dgemm_clock_probe.argtypes = [vp, ci, vp]
-    L.dgemm_clock_probe.restype = ci
+    L.dgemm_trace_clock.argtypes = [vp, i64]
+    L.dgemm_trace_clock.restype = ci
     _lib = L
     return L
 
@@ -235,18 +235,30 @@ def gemm_mx(layout, M, N, K, A, lda, B, ldb, C, ldc, scale_a, ldsa, scale_b, lds
                scale_b.data_ptr(), ldsb, layout, stream)
 
 
-def clock_probe(out, iters=20000, stream=None):
-    """Enqueue the library's clock probe, writing (core clock ticks,
-    real-time ticks at 100 MHz, chain value) to the first three elements of
-    ``out`` (an int64 device tensor); the engine clock in MHz is then
-    out[0] / out[1] * 100 after the stream has run it."""
+def trace_clock(buf):
+    """Set (an int64 device tensor of 4 * n values, n workgroups) or clear
+    (None) the calling thread's clock trace: later four-wave launches record
+    each workgroup's start and end stamps of the core clock counter and of
+    the 100 MHz real-time counter."""
     import torch
-    _device_tensors("out", out)
-    if out.dtype != torch.int64 or out.numel() < 3 or not out.is_contiguous():
-        raise TypeError("out must be a contiguous int64 device tensor of at least 3 elements")
-    st = load_library().dgemm_clock_probe(out.data_ptr(), int(iters), _stream_handle(stream))
+    if buf is None:
+        st = load_library().dgemm_trace_clock(None, 0)
+    else:
+        _device_tensors("buf", buf)
+        if buf.dtype != torch.int64 or not buf.is_contiguous():
+            raise TypeError("buf must be a contiguous int64 device tensor")
+        st = load_library().dgemm_trace_clock(buf.data_ptr(), buf.numel() // 4)
     if st != 0:
-        raise DgemmError(st, "dgemm_clock_probe")
+        raise DgemmError(st, "dgemm_trace_clock")
+
+
+def traced_clock_mhz(buf, n):
+    """Engine clock (MHz) of each of the first n traced workgroups, from the
+    host copy of a trace buffer."""
+    import numpy as np
+    t = np.asarray(buf.cpu()).reshape(-1, 4)[:n].astype(np.float64)
+    dr = t[:, 3] - t[:, 1]
+    return np.where(dr > 0, (t[:, 2] - t[:, 0]) / np.where(dr > 0, dr, 1.0) * 100.0, np.nan)
 
 
 _TORCH_DT = None

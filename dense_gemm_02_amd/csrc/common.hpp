@@ -141,6 +141,11 @@ struct GemmArgs {
   const uint8_t* msp;
   const uint8_t* msq;
   int64_t ldsp, ldsq;
+  // Clock trace (diagnostics, four-wave kernels only): workgroup w <
+  // trace_n writes its start and end stamps of the core clock counter and
+  // of the 100 MHz real-time counter to trace[4w .. 4w + 3].
+  unsigned long long* trace;
+  int64_t trace_n;
 };
 
 }  // namespace dg

@@ -21,6 +21,11 @@ namespace {
 // hipError_t behind the calling thread's most recent DGEMM_ERR_HIP.
 thread_local int g_last_hip_error = 0;
 
+// Clock trace buffer of the calling thread (dgemm_trace_clock), passed to
+// the four-wave kernels of its later calls.
+thread_local unsigned long long* g_trace = nullptr;
+thread_local int64_t g_trace_n = 0;
+
 int hip_failed(hipError_t e) {
   g_last_hip_error = (int)e;
   return DGEMM_ERR_HIP;
@@ -321,6 +326,8 @@ int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
     g.Q = (const char*)A; g.ldq = lda * e; g.Qn = M;
   }
   g.C = C; g.ldc = ldc; g.K = K;
+  g.trace = g_trace;
+  g.trace_n = g_trace_n;
   if (sc) {
     // Factor vectors are addressed through buffer descriptors in bytes.
     if (sc->na * 4 > kMaxDescBytes || sc->nb * 4 > kMaxDescBytes) return DGEMM_ERR_UNSUPPORTED;
@@ -354,6 +361,7 @@ int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
     // arrays along q, columns of D) or p >= at (rows of P -- for
     // p-contiguous P its columns --, factors along p, rows of D).
     GemmArgs g2 = g;
+    g2.trace = nullptr;   // the trace records the main launch
     const int64_t x0 = ch.at;
     if (!ch.split_p) {
       g2.Q = advance(g.Q, x0 * g.ldq);
@@ -407,36 +415,15 @@ int run(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
   return launch(pl.L2, pl.g2, pl.grid2, stream);
 }
 
-// Clock probe (diagnostics): one wave reads the core clock counter and the
-// constant 100 MHz real-time counter around a chain of dependent FMAs, so
-// the ratio of the two differences times 100 MHz is the engine clock while
-// the wave ran.  out[0] = core clock ticks, out[1] = real-time ticks,
-// out[2] = the chain's result (keeps the chain alive).
-__global__ void __launch_bounds__(64) clock_probe_kernel(unsigned long long* out, int iters) {
-  const uint64_t c0 = __builtin_amdgcn_s_memtime();
-  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
-  float x = (float)threadIdx.x;
-  for (int i = 0; i < iters; ++i) x = __builtin_fmaf(x, 1.0000001f, 1e-7f);
-  const uint64_t c1 = __builtin_amdgcn_s_memtime();
-  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
-  if (threadIdx.x == 0) {
-    out[0] = c1 - c0;
-    out[1] = r1 - r0;
-    out[2] = (unsigned long long)__builtin_bit_cast(uint32_t, x);
-  }
-}
-
 }  // namespace
 }  // namespace dg
 
 extern "C" {
 
-int dgemm_clock_probe(unsigned long long* out, int iters, void* stream) {
-  if (out == nullptr) return DGEMM_ERR_NULL_POINTER;
-  if (iters < 0) return DGEMM_ERR_INVALID_DIM;
-  hipLaunchKernelGGL(dg::clock_probe_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, out, iters);
-  const hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return dg::hip_failed(err);
+int dgemm_trace_clock(unsigned long long* buf, int64_t n_workgroups) {
+  if (buf != nullptr && n_workgroups < 0) return DGEMM_ERR_INVALID_DIM;
+  dg::g_trace = buf;
+  dg::g_trace_n = buf ? n_workgroups : 0;
   return DGEMM_OK;
 }
 

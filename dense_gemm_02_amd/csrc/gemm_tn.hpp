@@ -539,6 +539,16 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   // ---- tiles ----
   const int64_t tile = blockIdx.x;
   if (tile >= ntiles) return;
+  // Clock trace: the start stamps go out now, so that nothing of the trace
+  // stays live across the stage loop.
+  auto stamp = [&](int at) {
+    if (a.trace != nullptr && tid == 0 && tile < a.trace_n) {
+      unsigned long long* t = a.trace + 4 * tile + at;
+      t[0] = __builtin_amdgcn_s_memtime();
+      t[1] = __builtin_amdgcn_s_memrealtime();
+    }
+  };
+  stamp(0);
   const Src cur = tile_src(tile);
   // A source with empty descriptors (its copies read zeros): MX scale
   // groups past the tile's last.
@@ -636,6 +646,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   } else {
     direct_epilogue(tile);
   }
+  stamp(2);
 }
 
 // KT: some stage ends inside K (K not a multiple of the stage depth), so

@@ -170,16 +170,21 @@ const char* dgemm_hip_error_string(int code);
  * dgemm_status for invalid arguments.
  */
 /*
- * dgemm_clock_probe (diagnostics, used to report the engine clock next to
- * measured throughput): enqueues on `stream` one 64-lane wave that reads the
- * core clock counter and the constant 100 MHz real-time counter around
- * `iters` dependent FMAs and writes three 64-bit values to the DEVICE
- * pointer `out`: core clock ticks, real-time ticks, and a value that only
- * keeps the FMA chain alive.  Engine clock in Hz = out[0] / out[1] * 1e8.
- * Returns DGEMM_ERR_NULL_POINTER for a NULL out, DGEMM_ERR_INVALID_DIM for
- * iters < 0, DGEMM_ERR_HIP for a launch error.
+ * dgemm_trace_clock (diagnostics, used to report the engine clock the GEMM
+ * itself ran at): while `buf` is set, every launch of the four-wave kernels
+ * made by later calls from the calling thread records, for each workgroup
+ * w < n_workgroups, four 64-bit values at buf[4w .. 4w + 3]: the core clock
+ * counter and the 100 MHz real-time counter when the workgroup started, and
+ * both again when it finished.  Engine clock in Hz over the workgroup =
+ * (buf[4w+2] - buf[4w]) / (buf[4w+3] - buf[4w+1]) * 1e8 (the counters of
+ * different XCDs have different origins: compare stamps of one workgroup
+ * only).  `buf` is a DEVICE pointer to 4*n_workgroups values owned by the
+ * caller, written asynchronously on the call's stream; later launches
+ * overwrite it.  NULL turns the trace off.  Only the main launch of a call
+ * is traced (not the second launch of a split call); other kernels (FP32,
+ * skinny, ragged K) ignore it.  Returns DGEMM_ERR_INVALID_DIM for n_workgroups < 0.
  */
-int dgemm_clock_probe(unsigned long long* out, int iters, void* stream);
+int dgemm_trace_clock(unsigned long long* buf, int64_t n_workgroups);
 
 int dgemm_tile_map(int64_t tiles_p, int64_t tiles_q, int64_t group, int64_t pid,
                    int64_t* tile_p, int64_t* tile_q);

@@ -61,7 +61,8 @@ int main() {
          DGEMM_ERR_INVALID_LD, "MX ld");
   expect(gemm_mxfp8(4, 4, 64, buf8, 64, buf8, 64, out32, 4, buf8 + 1, 16, buf8, 16, DGEMM_TN, nullptr),
          DGEMM_ERR_MISALIGNED, "MX base");
-  expect(dgemm_clock_probe(nullptr, 10, nullptr), DGEMM_ERR_NULL_POINTER, "probe");
+  expect(dgemm_trace_clock((unsigned long long*)buf32, -1), DGEMM_ERR_INVALID_DIM, "trace count");
+  expect(dgemm_trace_clock(nullptr, 0), DGEMM_OK, "trace off");
   for (int s = -1; s < 10; ++s) expect(gemm_strerror(s) != nullptr, 1, "strerror", s);
   // kernel choice over many shapes (host planning only)
   char desc[512];

@@ -618,20 +618,29 @@ def test_binding_rejects_bad_device_tensors():
     torch.cuda.synchronize()
 
 
-# The clock probe (diagnostics): both counters advance and the ratio is an
-# engine clock in a plausible range.
-def test_clock_probe_reports_an_engine_clock():
+# The clock trace (diagnostics): each workgroup of a traced four-wave launch
+# records stamps whose ratio is an engine clock in a plausible range; the
+# result is unchanged, and the trace is off again afterwards.
+def test_clock_trace_reports_the_engine_clock():
     import torch
     from dense_gemm_02_amd import binding
-    out = torch.zeros((2, 3), dtype=torch.int64, device="cuda")
-    say("case clock probe")
-    binding.clock_probe(out[0], 20000)
-    binding.clock_probe(out[1], 0)
-    torch.cuda.synchronize()
-    c, r, _ = (int(v) for v in out[0].cpu())
-    assert c > 0 and r > 0
-    assert 300.0 < 100.0 * c / r < 3000.0, (c, r)
+    p = make_problem("bf16", "tn", 1024, 768, 512, seed=77)
+    A, B = to_dev(p.A), to_dev(p.B)
+    grid = int(kernel_name("bf16", "tn", 1024, 768, 512).split("grid=")[1].split()[0])
+    buf = torch.zeros(4 * grid + 4, dtype=torch.int64, device="cuda")
+    say(f"case clock trace grid={grid}")
+    C0 = run_gpu(p, A=A, B=B)
+    binding.trace_clock(buf)
+    try:
+        C1 = run_gpu(p, A=A, B=B)
+    finally:
+        binding.trace_clock(None)
+    assert torch.equal(C0, C1)
+    mhz = binding.traced_clock_mhz(buf, grid)
+    assert np.all((mhz > 300.0) & (mhz < 3000.0)), mhz
+    assert int(buf[4 * grid:].abs().sum()) == 0, "wrote past the requested workgroups"
+    buf.zero_()
+    run_gpu(p, A=A, B=B)
+    assert int(buf.abs().sum()) == 0, "trace still on"
     with pytest.raises(TypeError):
-        binding.clock_probe(torch.zeros(3, dtype=torch.int32, device="cuda"))
-    with pytest.raises(TypeError):
-        binding.clock_probe(torch.zeros(2, dtype=torch.int64, device="cuda"))
+        binding.trace_clock(torch.zeros(8, dtype=torch.int32, device="cuda"))
