@@ -45,7 +45,8 @@ FOUR_WAVE = [
 
 def units():
     """(source, object, extra flags) of every translation unit."""
-    out = [(os.path.join(CSRC, "dgemm.hip"), os.path.join(OBJDIR, "dgemm.o"), [])]
+    out = [(os.path.join(CSRC, "dgemm.hip"), os.path.join(OBJDIR, "dgemm.o"), []),
+           (os.path.join(CSRC, "pp.hip"), os.path.join(OBJDIR, "pp.o"), [])]
     for tag, op, nn in FOUR_WAVE:
         out.append((os.path.join(CSRC, "four_wave.hip"), os.path.join(OBJDIR, f"four_wave_{tag}.o"),
                     [f"-DDG_OP={op}", f"-DDG_PKM={nn}", f"-DDG_TAG={tag}", f"-DDG_FN=four_wave_{tag}"]))

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "dgemm.h"
 #include "common.hpp"
@@ -171,6 +173,17 @@ Launch four_wave(int dt, bool nn, int idx, bool kt) {
   }
 }
 
+// The kernel for kTiles entry `idx`: TN 256 x 256 tiles of FP16, BF16 and
+// FP8 (with or without scale factors) run the eight-wave ping-pong kernel
+// (gemm_pp.hpp; at 8192^3 on one box: FP8 2648 -> 2859 TF/s, BF16 1513 ->
+// 1550, FP16 1437 -> 1473, against the four-wave kernel); everything else
+// the four-wave kernel.
+Launch main_tile(int dt, bool nn, int idx, bool kt) {
+  if (idx == 0 && !nn && dt != DT_MX8)
+    return ping_pong_tn(dt == DT_F16 ? 0 : dt == DT_BF16 ? 1 : dt == DT_FP8 ? 2 : 3, kt);
+  return four_wave(dt, nn, idx, kt);
+}
+
 // The kernels of one call: a main launch, and optionally a second one over
 // the rest of one axis, p >= at (split_p) or q >= at.
 struct Choice {
@@ -187,6 +200,34 @@ struct Choice {
 // it (e.g. bf16 6144^2 x 4096: 1032 -> 1157 TF/s, fp8 8192 x 5120 x 8192:
 // 2287 -> 2540 TF/s).  Taken when the cost model (rounds x round time, as
 // pick_tile) gains at least 5%.
+// Sweeps and A/B timing: DGEMM_CONFIG=<kernel name>, as dgemm_kernel_config
+// prints it, forces that kernel (one launch, no split) for every call it
+// can serve: a four-wave tile of the call's format and layout, or the
+// eight-wave ping-pong kernel for TN.  Other calls keep the table's choice.
+// Read at every call; nothing is cached.
+bool forced_choice(int dt, bool nn, int64_t K, Choice* c) {
+  const char* want = getenv("DGEMM_CONFIG");
+  if (want == nullptr || *want == 0) return false;
+  const int e = in_elem(dt);
+  if (!(dt == DT_MX8 || (dt != DT_F32 && K % (16 / e) == 0 && K >= 2 * (128 / e)))) return false;
+  const bool kt = k_tail(dt, K);
+  for (int idx = 0; idx < kNumTiles; ++idx) {
+    const Launch L = four_wave(dt, nn, idx, kt);
+    if (strcmp(L.name, want) == 0) {
+      c->L = L;
+      return true;
+    }
+  }
+  if (!nn && dt != DT_MX8) {
+    const Launch L = ping_pong_tn(dt == DT_F16 ? 0 : dt == DT_BF16 ? 1 : dt == DT_FP8 ? 2 : 3, kt);
+    if (strcmp(L.name, want) == 0) {
+      c->L = L;
+      return true;
+    }
+  }
+  return false;
+}
+
 Choice choose(int dt, int layout, int64_t M, int64_t N, int64_t K) {
   const bool nn = layout == DGEMM_NN;
   const int64_t Pn = nn ? N : M, Qn = nn ? M : N;
@@ -212,7 +253,7 @@ Choice choose(int dt, int layout, int64_t M, int64_t N, int64_t K) {
     const unsigned mask = tile_mask(dt, nn, K);
     double whole = 0.0;
     const int idx = pick_tile(Pn, Qn, mask, &whole);
-    c.L = four_wave(dt, nn, idx, k_tail(dt, K));
+    c.L = main_tile(dt, nn, idx, k_tail(dt, K));
     const int64_t slots = kPlanCus;
     const int64_t tp = (Pn + 255) / 256, tq = (Qn + 255) / 256, tiles = tp * tq;
     double best = 0.95 * whole;
@@ -228,7 +269,7 @@ Choice choose(int dt, int layout, int64_t M, int64_t N, int64_t K) {
       const double cost = (double)((across * n1 + slots - 1) / slots) * 65536.0 + tail;
       if (cost < best) {
         best = cost;
-        c.L = four_wave(dt, nn, 0, k_tail(dt, K));
+        c.L = main_tile(dt, nn, 0, k_tail(dt, K));
         c.split = true;
         c.split_p = axis == 1;
         c.at = 256 * n1;
@@ -312,10 +353,11 @@ int plan(int dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
        (mx->ldsb & 15) != 0))
     return DGEMM_ERR_MISALIGNED;
 
-  const bool skinny = use_skinny(dt, layout, M);
   Choice ch{};
+  const bool forced = forced_choice(dt, layout == DGEMM_NN, K, &ch);
+  const bool skinny = !forced && use_skinny(dt, layout, M);
   if (skinny) ch.L = select_skinny(dt, M);
-  else ch = choose(dt, layout, M, N, K);
+  else if (!forced) ch = choose(dt, layout, M, N, K);
   const Launch L = ch.L;
   GemmArgs g{};
   if (!nn) {

@@ -35,4 +35,8 @@ Launch four_wave_fp8s_nn(int idx, bool kt);
 Launch four_wave_mx8_tn(int idx, bool kt);
 Launch four_wave_mx8_nn(int idx, bool kt);
 
+// The eight-wave ping-pong kernel (gemm_pp.hpp), TN, 256 x 256: op 0 FP16,
+// 1 BF16, 2 FP8, 3 FP8 with scale factors.
+Launch ping_pong_tn(int op, bool kt);
+
 }  // namespace dg

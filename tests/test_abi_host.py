@@ -196,7 +196,8 @@ def _kernel(lib, dt, layout, M, N, K):
     return buf.value.decode()
 
 
-# Tile choice of the four-wave kernel: rounds of workgroups over 256 CUs
+# Tile choice (TN 256 x 256 runs the eight-wave ping-pong kernel, every other
+# tile the four-wave kernel): rounds of workgroups over 256 CUs
 # times the time of one round. 256 x 256 tiles cost 1 per round, 128 x 128
 # ones (two per CU, two stages) 1/0.78 * 1/2, 256 x 128 ones 1/0.76 * 1/2;
 # 128 x 128 with four stages (one per CU) 1/0.47 * 1/4, for one round only;
@@ -224,6 +225,8 @@ def test_tile_choice(lib, M, N, K, tile16, tile8nn, tile16tn):
                 want = tile16tn[0] if layout == 1 else tile16tn[1]
             if dt == 5 and want.endswith("_s4"):
                 want = want[:-3]          # MXFP8 keeps two LDS stages (its scale ring)
+            if want == "256x256_w4" and layout == 1 and dt != 5:
+                want = "256x256_pp"       # TN 256 x 256: the eight-wave ping-pong kernel
             assert d.endswith(want), (dt, layout, full)
             assert " + " not in full, full
 
@@ -247,7 +250,8 @@ def test_tile_choice(lib, M, N, K, tile16, tile8nn, tile16tn):
 def test_split_choice(lib, dt, layout, M, N, K, axis, at, tail):
     full = _kernel(lib, dt, layout, M, N, K)
     main, rest = full.split(" + ")
-    assert "256x256_w4" in main.split()[0], full
+    big = "256x256_pp" if layout == 1 and dt != 5 else "256x256_w4"
+    assert main.split()[0].endswith(big), full
     assert rest.split()[0] == tail, full
     assert rest.endswith(f"from {axis}={at}"), full
 
@@ -258,7 +262,7 @@ def test_no_split_when_rounds_are_whole_or_it_does_not_pay(lib, M, N, K):
         assert " + " not in _kernel(lib, dt, 1, M, N, K)
     # 256 x 256 runs one tile per workgroup for every dtype (16 x 16 MFMA
     # tiles): the grid is the tile count.
-    for dt, name in ((3, "fp8_tn_256x256_w4"), (5, "mx8_tn_256x256_w4")):
+    for dt, name in ((3, "fp8_tn_256x256_pp"), (5, "mx8_tn_256x256_w4")):
         k = _kernel(lib, dt, 1, 5120, 5120, 1024)
         assert k.split()[0] == name and "grid=400 " in k, k
     # K not a whole number of 16-byte chunks: the eight-wave kernel.

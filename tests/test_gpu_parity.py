@@ -101,6 +101,9 @@ def test_four_wave_kernel(dtype, layout):
     # one 256 x 256).
     t192 = "192x256_w4" if layout == "tn" else "256x192_w4"
     q192 = "256x192_w4" if layout == "tn" else "256x256_w4"
+    # TN takes the eight-wave ping-pong kernel where the table picks 256 x 256
+    big = "256x256_pp" if layout == "tn" else "256x256_w4"
+    shapes = [(M, N, K, big if t == "256x256_w4" else t) for M, N, K, t in shapes]
     shapes += [(1536, 8192, 4096, t192), (1500, 8000, 4096 + 16, t192), (8192, 1500, 4096 + 16, q192)]
     for idx, (M, N, K, tile) in enumerate(shapes):
         name = kernel_name(dtype, layout, M, N, K)
@@ -139,7 +142,7 @@ def test_pm1_bit_exact(dtype, layout):
 # tolerance would hide it.  The kernel each case must reach is asserted.
 PM1_PATHS = [
     # four-wave FP8 with the K-tail instantiation (K = 3 * 128 + 16)
-    ("fp8", "tn", 5120, 5120, 400, "fp8_tn_256x256_w4", None),
+    ("fp8", "tn", 5120, 5120, 400, "fp8_tn_256x256_pp", None),
     ("fp8", "nn", 5120, 5120, 400, "fp8_nn_256x256_w4", None),
     ("fp8", "tn", 600, 520, 400, "fp8_tn_128x128_w4_s4", None),
     ("fp8", "nn", 600, 520, 400, "fp8_nn_256x128_w4", None),
@@ -150,9 +153,9 @@ PM1_PATHS = [
     ("fp8", "tn", 8192, 1500, 4112, "fp8_tn_256x192_w4", None),
     ("bf16", "tn", 8192, 1500, 4104, "bf16_tn_256x192_w4", None),
     # split launches: whole 256 x 256 rounds plus a second launch along q / p
-    ("bf16", "tn", 4352, 4352, 192, "bf16_tn_256x256_w4", "q"),
-    ("bf16", "tn", 14336, 4096, 192, "bf16_tn_256x256_w4", "p"),
-    ("fp8", "tn", 4352, 4352, 384, "fp8_tn_256x256_w4", "q"),
+    ("bf16", "tn", 4352, 4352, 192, "bf16_tn_256x256_pp", "q"),
+    ("bf16", "tn", 14336, 4096, 192, "bf16_tn_256x256_pp", "p"),
+    ("fp8", "tn", 4352, 4352, 384, "fp8_tn_256x256_pp", "q"),
     ("fp8", "nn", 4096, 14336, 384, "fp8_nn_256x256_w4", "p"),
 ]
 
@@ -644,3 +647,72 @@ def test_clock_trace_reports_the_engine_clock():
     assert int(buf.abs().sum()) == 0, "trace still on"
     with pytest.raises(TypeError):
         binding.trace_clock(torch.zeros(8, dtype=torch.int32, device="cuda"))
+
+
+# The eight-wave ping-pong kernel (gemm_pp.hpp), forced through DGEMM_CONFIG:
+# single and partial tiles, several rounds of 256 x 256 tiles, K tails
+# (copies with per-lane masks), +-1 bit-exact, repeatable bit for bit, and
+# FP8 with per-row scale factors.
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "fp8"])
+def test_ping_pong_kernel(dtype, monkeypatch):
+    import torch
+    bk = 128 if dtype == "fp8" else 64
+    name = f"{dtype}_tn_256x256_pp"
+    monkeypatch.setenv("DGEMM_CONFIG", name)
+    shapes = [(256, 256, 2 * bk), (16, 16, 2 * bk), (1, 1, 2 * bk + 16), (300, 521, 2 * bk), (600, 520, 4 * bk),
+              (129, 77, 5 * bk + 16), (1000, 1100, 9 * bk + 16), (5120, 5120, 3 * bk), (5120, 5120, 3 * bk + 16),
+              (2048, 2048, 64 * bk)]
+    for idx, (M, N, K) in enumerate(shapes):
+        kern = kernel_name(dtype, "tn", M, N, K)
+        assert kern.startswith(name + " "), kern
+        p = make_problem(dtype, "tn", M, N, K, seed=9300 + idx, pad=idx % 2)
+        say(f"case pp {kern} M={M} N={N} K={K}")
+        cij, pad = c_host(p, run_gpu(p))
+        assert pad_untouched(pad, dtype)
+        ok, err, nbad = compare(p, cij)
+        assert ok, f"{name} {(M, N, K)}: max err {err:.3e}, {nbad} bad"
+    for idx, (M, N, K) in enumerate([(4096, 4096, 16 * bk), (1000, 1100, 9 * bk + 16)]):
+        p = make_problem(dtype, "tn", M, N, K, seed=9400 + idx, dist="pm1")
+        say(f"case pp pm1 {name} M={M} N={N} K={K}")
+        cij, _ = c_host(p, run_gpu(p))
+        ok, _, nbad = compare(p, cij, exact=True)
+        assert ok, f"{name} pm1 {(M, N, K)}: {nbad} elements differ"
+    p = make_problem(dtype, "tn", 5120, 5120, 4 * bk, seed=9500)
+    A, B = to_dev(p.A), to_dev(p.B)
+    say(f"case pp determinism {name}")
+    assert torch.equal(run_gpu(p, A=A, B=B), run_gpu(p, A=A, B=B))
+
+
+def test_ping_pong_scaled_fp8(monkeypatch):
+    monkeypatch.setenv("DGEMM_CONFIG", "fp8s_tn_256x256_pp")
+    rng = np.random.default_rng(9600)
+    for idx, (M, N, K) in enumerate([(1000, 1100, 1168), (5120, 5120, 384)]):
+        kern = kernel_name("fp8s", "tn", M, N, K)
+        assert kern.startswith("fp8s_tn_256x256_pp "), kern
+        p = make_problem("fp8", "tn", M, N, K, seed=9610 + idx)
+        sa, sb = _factors(rng, M), _factors(rng, N)
+        say(f"case pp scaled {kern} M={M} N={N} K={K}")
+        cij, pad = c_host(p, run_scaled(p, sa, sb))
+        assert pad_untouched(pad, "fp8")
+        ok, err = compare_scaled(p, cij, sa, sb)
+        assert ok, f"{(M, N, K)}: max err {err:.3e}"
+
+
+# The four-wave kernel's TN 256 x 256 tile (the eight-wave kernel serves that
+# tile by default; the four-wave one stays reachable through DGEMM_CONFIG and
+# serves MXFP8), with and without a K tail, +-1 bit-exact.
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "fp8"])
+def test_four_wave_256_tn_forced(dtype, monkeypatch):
+    bk = 128 if dtype == "fp8" else 64
+    name = f"{dtype}_tn_256x256_w4"
+    monkeypatch.setenv("DGEMM_CONFIG", name)
+    for idx, (M, N, K, dist) in enumerate([(5120, 5120, 3 * bk, None), (1000, 1100, 9 * bk + 16, None),
+                                           (4096, 4096, 16 * bk, "pm1")]):
+        kern = kernel_name(dtype, "tn", M, N, K)
+        assert kern.startswith(name + " "), kern
+        p = make_problem(dtype, "tn", M, N, K, seed=9700 + idx, dist=dist, pad=idx % 2)
+        say(f"case w4 forced {kern} M={M} N={N} K={K}")
+        cij, pad = c_host(p, run_gpu(p))
+        assert pad_untouched(pad, dtype)
+        ok, err, nbad = compare(p, cij, exact=dist == "pm1")
+        assert ok, f"{name} {(M, N, K)}: max err {err:.3e}, {nbad} bad"
