@@ -77,6 +77,13 @@ __device__ __forceinline__ void copy4_lds(i32x4 desc, uint32_t voff, const void*
                : "memory", "m0");
 }
 
+// This lane's index in its wave, computed afresh (mbcnt) rather than taken
+// from threadIdx: code after a long loop that uses it then keeps no thread
+// index register live across the loop.
+__device__ __forceinline__ int lane_id() {
+  return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
 }

@@ -542,7 +542,7 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   // Clock trace: the start stamps go out now, so that nothing of the trace
   // stays live across the stage loop.
   auto stamp = [&](int at) {
-    if (a.trace != nullptr && tid == 0 && tile < a.trace_n) {
+    if (a.trace != nullptr && wave_u == 0 && lane_id() == 0 && tile < a.trace_n) {
       unsigned long long* t = a.trace + 4 * tile + at;
       t[0] = __builtin_amdgcn_s_memtime();
       t[1] = __builtin_amdgcn_s_memrealtime();
@@ -589,11 +589,13 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   // tiles: q = 16 j + l % 16, p = 16 i + 4 (l / 16)).
   constexpr int NG = MT * MT / 256;   // register groups of four per tile
   auto direct_epilogue = [&](int64_t t) {
+    // (lane values recomputed here, not kept live across the stage loop)
+    const int lr = lane_id() % MT, lg = lane_id() / MT;
     int64_t tp, tq;
     tile_map(a.tiles_p, a.tiles_q, a.group, t, &tp, &tq);
     const int64_t pb = tp * Cfg::BP + wp * Cfg::WTP, qb = tq * Cfg::BQ + wq * Cfg::WTQ;
     [[maybe_unused]] EpiScale<TQ, MT> sc;
-    if constexpr (Op::SCALED) sc.init(a, lane, qb);
+    if constexpr (Op::SCALED) sc.init(a, lane_id(), qb);
     // Column by column: a lane's four stores into one column of C follow
     // each other, so each 128-byte line is written whole while it is open.
 #pragma unroll
@@ -634,6 +636,9 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
   // Copies issued past the tile read zeros; let them land before the LDS is
   // reused and before exit.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  // End stamp of the clock trace at the end of the stage loop (the clock
+  // over the loop; nothing of the trace stays live into the epilogue).
+  stamp(2);
   if constexpr (Cfg::STAGED_EPI) {
     // The stage buffers are free for an LDS-staged epilogue once every wave
     // is past its last read.
@@ -641,12 +646,11 @@ __device__ __forceinline__ void gemm_tn_body(const GemmArgs& a) {
     int64_t tp, tq;
     tile_map(a.tiles_p, a.tiles_q, a.group, tile, &tp, &tq);
     static_assert(!Cfg::STAGED_EPI || Cfg::WTQ * 256 * NW <= 2 * Cfg::STAGE, "staging fits in the stage buffers");
-    staged_epilogue<Op, Cfg::WTP, Cfg::WTQ, TP, TQ, MT, Acc>(a, smem + wave_u * (Cfg::WTQ * 256), acc, lane,
+    staged_epilogue<Op, Cfg::WTP, Cfg::WTQ, TP, TQ, MT, Acc>(a, smem + wave_u * (Cfg::WTQ * 256), acc, lane_id(),
                                                              tp * Cfg::BP + wp * Cfg::WTP, tq * Cfg::BQ + wq * Cfg::WTQ);
   } else {
     direct_epilogue(tile);
   }
-  stamp(2);
 }
 
 // KT: some stage ends inside K (K not a multiple of the stage depth), so
