@@ -13,7 +13,10 @@ compiled here on the CPU from the same sources and flags as the library.
   reports for it, and fits gfx950's 160 KiB.
 * The figures of the kernels in a committed kernel trace
   (profiles/kernel_resources.md: rocprofv3 --kernel-trace, same sources) match
-  the compiler's: VGPRs (allocation granularity 8), AGPRs, LDS and scratch.
+  the compiler's: LDS, scratch, and the VGPR field of the kernel
+  descriptor.  gfx950 allocates the unified VGPR/AGPR file of a wave64 in
+  granules of 8 registers and the descriptor stores the granule count; the
+  trace prints that count times 4, half the registers actually allocated.
 """
 
 import concurrent.futures as cf
@@ -31,10 +34,17 @@ _REMARK = re.compile(r"remark:\s+(Function Name|TotalSGPRs|VGPRs|AGPRs|ScratchSi
                      r"LDS Size \[bytes/block\]|Occupancy \[waves/SIMD\]|VGPRs Spill|SGPRs Spill):\s+(\S+)")
 
 
+_DESC = re.compile(r"^\s*\.amdhsa_kernel\s+(\S+)(.*?)^\s*\.end_amdhsa_kernel", re.S | re.M)
+_NEXT_VGPR = re.compile(r"\.amdhsa_next_free_vgpr\s+(\d+)")
+
+
 def _remarks(unit, outdir):
+    # Device-only compile to assembly: the remarks on stderr, the kernel
+    # descriptors (.amdhsa_kernel blocks) in the output.
     src, obj, flags = unit
+    out = os.path.join(outdir, os.path.basename(obj)[:-2] + ".s")
     cmd = (["/opt/rocm/bin/hipcc"] + B.HIPCC_FLAGS + flags +
-           ["-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", os.path.join(outdir, os.path.basename(obj))])
+           ["-Rpass-analysis=kernel-resource-usage", "--offload-device-only", "-S", src, "-o", out])
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
     kernels, cur = {}, None
@@ -44,6 +54,10 @@ def _remarks(unit, outdir):
             cur = kernels.setdefault(val, {})
         elif cur is not None:
             cur[key.split(" [")[0]] = int(val) if val.lstrip("-").isdigit() else val
+    with open(out) as f:
+        for m in _DESC.finditer(f.read()):
+            if m.group(1) in kernels:
+                kernels[m.group(1)]["next_free_vgpr"] = int(_NEXT_VGPR.search(m.group(2)).group(1))
     return kernels
 
 
@@ -61,6 +75,7 @@ def usage(tmp_path_factory):
 
 def test_every_kernel_is_reported(usage):
     names = list(usage)
+    assert all("next_free_vgpr" in u for u in usage.values())
     assert sum("gemm_tn_kernel" in n for n in names) >= 80
     assert any("gemm_f32_kernel" in n for n in names)
     assert any("gemm_skinny_kernel" in n for n in names)
@@ -151,5 +166,11 @@ def test_kernel_trace_matches_the_compiler(usage):
         u = usage[name]
         assert scratch == u["ScratchSize"] == 0, name
         assert lds == u["LDS Size"], name
-        assert agpr == u["AGPRs"], name
-        assert vgpr == -(-u["VGPRs"] // 8) * 8, (name, vgpr, u["VGPRs"])
+        # gfx950 has one unified VGPR/AGPR file: the trace's accumulation
+        # count stays 0 and the AGPRs are inside the VGPR granules.
+        assert agpr == 0, name
+        nfv = u["next_free_vgpr"]
+        # The descriptor covers every VGPR and AGPR the compiler reports
+        # (AGPRs start at a 4-aligned offset after the VGPRs).
+        assert nfv >= (-(-u["VGPRs"] // 4) * 4 if u["AGPRs"] else u["VGPRs"]) + u["AGPRs"], name
+        assert vgpr == -(-nfv // 8) * 4, (name, vgpr, nfv)
