@@ -151,18 +151,26 @@ def time_gemm(dtype, steps, warmup, spec=None, rotate=1, made=None):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    # One event before every launch and one after the last: the region from
-    # the first to the last event is the timed one (mean = its length / K);
-    # consecutive events give each launch's own time (min, median).
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    # The timed region: K launches back to back between two events (mean =
+    # its length / K).  An event recorded between launches costs the stream
+    # a few microseconds, so the per-launch spread (min, median, max) comes
+    # from a second pass of K launches with an event before each one; those
+    # figures include that cost.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     for i in range(steps):
         ev[i].record(stream)
         step()
     ev[steps].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev[0].elapsed_time(ev[steps]) / steps
     each = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     flops = p.flops
     res = {"ms_per_launch": ms, "tflops": flops / (ms * 1e-3) / 1e12, "wall_s": wall,

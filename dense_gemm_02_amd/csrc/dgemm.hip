@@ -137,16 +137,25 @@ unsigned tile_mask(int dt, bool nn, int64_t K) {
   return (dt == DT_MX8 ? 0b0101u : 0b1101u) | t192;
 }
 
-template <bool PT>
+template <bool PT, int BT>
 Launch f32_launch(const char* name) {
-  using Cfg = F32Cfg<128, 128, 2, 2, PT>;
-  return Launch{(const void*)&gemm_f32_kernel<128, 128, 2, 2, PT>, name, 128, 128, Cfg::NT, 2 * Cfg::STAGE, PT};
+  using Cfg = F32Cfg<BT, BT, 2, 2, PT>;
+  return Launch{(const void*)&gemm_f32_kernel<BT, BT, 2, 2, PT>, name, BT, BT, Cfg::NT, 2 * Cfg::STAGE, PT};
+}
+
+// FP32 tile: 128 x 128 (four waves of 64 x 64) once the grid has at least
+// half as many tiles as there are CUs; below that 64 x 64 (four waves of
+// 32 x 32), four times the workgroups.  A 256^3 product is 4 workgroups at
+// 128 x 128, each a full K loop on one CU, against 16 at 64 x 64.
+Launch f32_tile(bool nn, bool small) {
+  if (small) return nn ? f32_launch<true, 64>("f32_nn_64x64") : f32_launch<false, 64>("f32_tn_64x64");
+  return nn ? f32_launch<true, 128>("f32_nn_128x128") : f32_launch<false, 128>("f32_tn_128x128");
 }
 
 template <class Op, int PF>
 Launch skinny_launch(const char* name) {
   return Launch{(const void*)&gemm_skinny_kernel<Op, PF>, name, 16 * PF, SkinnyCfg<Op, PF>::BQ, SkinnyCfg<Op, PF>::NT,
-                (int)(16 * SkinnyCfg<Op, PF>::NW * PF * SkinnyCfg<Op, PF>::QF * 64), false};
+                (int)SkinnyCfg<Op, PF>::LDS, false};
 }
 
 // Skinny TN problems (at most 32 rows of A) stream B once with a split-K
@@ -208,6 +217,16 @@ struct Choice {
 bool forced_choice(int dt, bool nn, int64_t K, Choice* c) {
   const char* want = getenv("DGEMM_CONFIG");
   if (want == nullptr || *want == 0) return false;
+  if (dt == DT_F32) {
+    for (int small = 0; small < 2; ++small) {
+      const Launch L = f32_tile(nn, small != 0);
+      if (strcmp(L.name, want) == 0) {
+        c->L = L;
+        return true;
+      }
+    }
+    return false;
+  }
   const int e = in_elem(dt);
   if (!(dt == DT_MX8 || (dt != DT_F32 && K % (16 / e) == 0 && K >= 2 * (128 / e)))) return false;
   const bool kt = k_tail(dt, K);
@@ -279,7 +298,7 @@ Choice choose(int dt, int layout, int64_t M, int64_t N, int64_t K) {
     return c;
   }
   switch (dt) {
-    case DT_F32:  c.L = nn ? f32_launch<true>("f32_nn_128x128") : f32_launch<false>("f32_tn_128x128"); break;
+    case DT_F32:  c.L = f32_tile(nn, ((Pn + 127) / 128) * ((Qn + 127) / 128) < kPlanCus / 2); break;
     case DT_F16:  c.L = nn ? mfma_launch<OpF16, true>("f16_nn_256x256") : mfma_launch<OpF16, false>("f16_tn_256x256"); break;
     case DT_BF16: c.L = nn ? mfma_launch<OpBF16, true>("bf16_nn_256x256") : mfma_launch<OpBF16, false>("bf16_tn_256x256"); break;
     case DT_FP8S: c.L = nn ? mfma_launch<OpFP8S, true>("fp8s_nn_256x256") : mfma_launch<OpFP8S, false>("fp8s_tn_256x256"); break;

@@ -196,6 +196,20 @@ def _kernel(lib, dt, layout, M, N, K):
     return buf.value.decode()
 
 
+@pytest.mark.parametrize("layout,M,N,K,tile", [
+    (0, 256, 256, 256, "64x64"),         # 4 tiles of 128^2 -> 16 of 64^2
+    (1, 256, 256, 256, "64x64"),
+    (0, 1024, 1024, 1024, "64x64"),      # 64 < 128 tiles of 128^2
+    (0, 1408, 1408, 64, "64x64"),        # 11^2 = 121 tiles of 128^2
+    (0, 1536, 1408, 64, "128x128"),      # 12 x 11 = 132
+    (0, 2048, 2048, 2048, "128x128"),
+    (1, 4096, 4096, 4096, "128x128"),
+])
+def test_f32_tile_by_grid(lib, layout, M, N, K, tile):
+    d = _kernel(lib, 0, layout, M, N, K)
+    assert d.startswith(f"f32_{'tn' if layout else 'nn'}_{tile}"), d
+
+
 # Tile choice (TN 256 x 256 runs the eight-wave ping-pong kernel, every other
 # tile the four-wave kernel): rounds of workgroups over 256 CUs
 # times the time of one round. 256 x 256 tiles cost 1 per round, 128 x 128

@@ -327,11 +327,12 @@ def test_odd_ldc_scalar_store_path():
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_skinny_split_k_path(dtype):
     # TN with at most 32 rows of A runs the split-K skinny kernel: K is cut
-    # into 8 slices whose boundaries and tail chunks must all line up.
+    # into 8 slices of whole 128-k steps whose boundaries and tail chunks
+    # must all line up.
     idx = 0
     for M in (1, 5, 16, 17, 31, 32):
         for N in (1, 33, 300):
-            for K in (1, 7, 8, 31, 33, 255, 1000, 2049):
+            for K in (1, 7, 8, 31, 33, 127, 128, 129, 255, 1000, 1032, 2049):
                 p = make_problem(dtype, "tn", M, N, K, seed=6000 + idx, pad=idx % 2)
                 idx += 1
                 cij, pad = c_host(p, run_gpu(p))
@@ -714,5 +715,24 @@ def test_four_wave_256_tn_forced(dtype, monkeypatch):
         say(f"case w4 forced {kern} M={M} N={N} K={K}")
         cij, pad = c_host(p, run_gpu(p))
         assert pad_untouched(pad, dtype)
+        ok, err, nbad = compare(p, cij, exact=dist == "pm1")
+        assert ok, f"{name} {(M, N, K)}: max err {err:.3e}, {nbad} bad"
+
+
+# Both FP32 tiles on both layouts at ragged multi-tile shapes: the default
+# choice (64 x 64 below half a chip of 128 x 128 tiles) and the other tile
+# forced through DGEMM_CONFIG, with +-1 inputs bit-exact.
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+@pytest.mark.parametrize("tile", ["64x64", "128x128"])
+def test_f32_tiles_forced(layout, tile, monkeypatch):
+    name = f"f32_{layout}_{tile}"
+    monkeypatch.setenv("DGEMM_CONFIG", name)
+    for idx, (M, N, K, dist) in enumerate([(300, 200, 77, None), (257, 129, 1029, None), (520, 600, 96, "pm1")]):
+        kern = kernel_name("f32", layout, M, N, K)
+        assert kern.startswith(name + " "), kern
+        p = make_problem("f32", layout, M, N, K, seed=9800 + idx, dist=dist, pad=idx % 2)
+        say(f"case f32 forced {kern} M={M} N={N} K={K}")
+        cij, pad = c_host(p, run_gpu(p))
+        assert pad_untouched(pad, "f32")
         ok, err, nbad = compare(p, cij, exact=dist == "pm1")
         assert ok, f"{name} {(M, N, K)}: max err {err:.3e}, {nbad} bad"

@@ -146,11 +146,18 @@ def test_four_wave_lds_matches_its_layout(usage):
 
 
 def _trace_table():
+    """Rows of the committed trace summary, if it was taken on the current
+    kernel sources (its "Sources hash"); otherwise none."""
     path = os.path.join(ROOT, "profiles", "kernel_resources.md")
     if not os.path.exists(path):
         return []
+    import bench
+    text = open(path).read()
+    m = re.search(r"Sources hash: `([0-9a-f]+)`", text)
+    if not m or m.group(1) != bench.kernel_source_hash():
+        return []
     rows = []
-    for line in open(path):
+    for line in text.splitlines():
         cells = [c.strip() for c in line.strip().strip("|").split("|")]
         if len(cells) == 6 and cells[0].startswith("_Z"):
             rows.append((cells[0], *[int(c) for c in cells[1:]]))
@@ -160,7 +167,7 @@ def _trace_table():
 def test_kernel_trace_matches_the_compiler(usage):
     rows = _trace_table()
     if not rows:
-        pytest.skip("no kernel trace summary committed")
+        pytest.skip("no kernel trace summary of the current kernel sources")
     for name, vgpr, agpr, lds, scratch, _sgpr in rows:
         assert name in usage, name
         u = usage[name]
