@@ -314,18 +314,55 @@ __device__ __forceinline__ void staged_epilogue(const GemmArgs& a, char* reg, co
         d = (kr & 1) ? u32x4{raw[2], raw[3], raw[0], raw[1]} : raw;
       }
       const int64_t q = qbase + row;
-      const int64_t p = pbase + pass * TPP * MT + m * EPC;
+      const int64_t p0 = pbase + pass * TPP * MT;   // first p of the staged row
+      const int64_t p = p0 + m * EPC;
       if (q >= a.Qn) continue;
       char* c = (char*)a.C + (q * a.ldc + p) * OE;
       if (a.vec16 && p + EPC <= a.Pn) {
         *(u32x4*)c = d;
-      } else {
+        continue;
+      }
+      if constexpr (OE == 2) {
+        // The row's 256 bytes of C start off the 16-byte grid (odd ldc or
+        // C not 16-byte aligned), delta bytes past a boundary.  Whole rows
+        // are stored as the aligned 16-byte blocks that cover them: lane m
+        // (m < 15) stores block m + 1, which starts at row byte
+        // 16 (m + 1) - delta and is gathered from the staged row as five
+        // dwords shifted by (16 (m + 1) - delta) mod 4 bytes; lane 15 stores
+        // the partial blocks at both ends element by element.  Rows that
+        // end at the p edge keep the element-wise stores below.
+        const char* rowc = (const char*)a.C + (q * a.ldc + p0) * 2;
+        const int delta = (int)((uintptr_t)rowc & 15);
+        if (p0 + RB / 2 <= a.Pn && delta != 0) {
+          auto dword_at = [&](int b) {   // dword at logical byte b (4-aligned) of the staged row
+            return *(const uint32_t*)(reg + row * RB + ((((b >> 3) ^ kr) << 3) | (b & 7)));
+          };
+          if (m < 15) {
+            const int b0 = 16 * (m + 1) - delta;
+            const int bw = b0 & ~3, sh = b0 & 3;
+            uint32_t w[5];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          if (p + e < a.Pn) {
-            if constexpr (OE == 4) ((uint32_t*)c)[e] = d[e];
-            else ((uint16_t*)c)[e] = (uint16_t)(d[e >> 1] >> ((e & 1) * 16));
+            for (int k = 0; k < 5; ++k) w[k] = dword_at(bw + 4 * k);
+            u32x4 blk;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) blk[k] = __builtin_amdgcn_alignbyte(w[k + 1], w[k], (unsigned)sh);
+            *(u32x4*)(rowc + b0) = blk;
+          } else {
+            auto elem_at = [&](int e) {
+              return (uint16_t)(dword_at((2 * e) & ~3) >> ((e & 1) * 16));
+            };
+            const int head = (16 - delta) / 2, tail = delta / 2;   // elements
+            for (int e = 0; e < head; ++e) ((uint16_t*)rowc)[e] = elem_at(e);
+            for (int e = RB / 2 - tail; e < RB / 2; ++e) ((uint16_t*)rowc)[e] = elem_at(e);
           }
+          continue;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        if (p + e < a.Pn) {
+          if constexpr (OE == 4) ((uint32_t*)c)[e] = d[e];
+          else ((uint16_t*)c)[e] = (uint16_t)(d[e >> 1] >> ((e & 1) * 16));
         }
       }
     }

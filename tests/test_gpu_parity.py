@@ -736,3 +736,27 @@ def test_f32_tiles_forced(layout, tile, monkeypatch):
         assert pad_untouched(pad, "f32")
         ok, err, nbad = compare(p, cij, exact=dist == "pm1")
         assert ok, f"{name} {(M, N, K)}: max err {err:.3e}, {nbad} bad"
+
+
+# C rows off the 16-byte grid: a C base 2..14 bytes past a 16-byte boundary
+# with a 16-byte pitch (every row equally off), and an odd pitch (every
+# offset), for the 16-bit outputs; the storage around C stays untouched.
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_c_rows_off_the_16_byte_grid(dtype):
+    import torch
+    from dense_gemm_02_amd import binding
+    for idx, (M, N, K, ldc, off) in enumerate([(600, 300, 256, 608, 1), (600, 300, 256, 608, 7),
+                                               (515, 260, 320, 515, 0), (1000, 77, 192, 1001, 3)]):
+        p = make_problem(dtype, "tn", M, N, K, seed=9900 + idx)
+        p.ldc = ldc
+        say(f"case C off-grid {dtype} M={M} N={N} K={K} ldc={ldc} offset={off}")
+        flat = torch.full((off + N * ldc + 8,), -1, dtype=torch.int16, device="cuda")
+        C = flat[off:off + N * ldc].view(N, ldc)
+        binding.gemm(p.dtype, p.layout, M, N, K, to_dev(p.A), p.lda, to_dev(p.B), p.ldb, C, ldc)
+        torch.cuda.synchronize()
+        f = flat.cpu().numpy().view(np.uint16)
+        assert np.all(f[:off] == 0xFFFF) and np.all(f[off + N * ldc:] == 0xFFFF), "wrote outside C"
+        cij, pad = c_host(p, C)
+        assert pad_untouched(pad, dtype)
+        ok, err, nbad = compare(p, cij)
+        assert ok, f"{dtype} {(M, N, K, ldc, off)}: max err {err:.3e}, {nbad} bad"
