@@ -276,7 +276,20 @@ Choice choose(int dt, int layout, int64_t M, int64_t N, int64_t K) {
     const int64_t slots = kPlanCus;
     const int64_t tp = (Pn + 255) / 256, tq = (Qn + 255) / 256, tiles = tp * tq;
     double best = 0.95 * whole;
-    for (int axis = 0; axis < 2 && tiles % slots != 0; ++axis) {
+    // A last round of 256 x 256 tiles at least half full runs at a higher
+    // clock than a full one (fewer CUs under the power limit) and costs
+    // less than the round model says: measured, a single launch beat the
+    // split or tied it at 1.5 and 3.5 rounds (bf16 5120^2 x 4096 1356 vs
+    // 1308 TF/s, fp8 2362 vs 2211; 4096 x 14336 x 4096 1404 vs 1397, fp8
+    // 2501 vs 2484; 8192 x 5120 x 4096 1400 vs 1384), while the split won
+    // with a last round a quarter full or less (4352^2 x 4096 1205 vs 1007,
+    // 6144^2 x 4096 1307 vs 1256, 7168^2 x 4096 1368 vs 1251).
+    // (Measured with the eight-wave TN kernel as the main launch; with the
+    // four-wave one (NN, MXFP8) the split also paid at 2.5 rounds: fp8
+    // 8192 x 5120 x 8192 2287 -> 2455-2540.)
+    const bool pp_main = !nn && dt != DT_MX8;
+    const bool consider = tiles % slots != 0 && (!pp_main || 2 * (tiles % slots) < slots);
+    for (int axis = 0; axis < 2 && consider; ++axis) {
       // axis 0 splits q, axis 1 splits p: n1 whole tiles of the split axis
       // fit the full rounds.
       const int64_t across = axis == 0 ? tp : tq, along = axis == 0 ? tq : tp;

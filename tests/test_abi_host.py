@@ -248,18 +248,17 @@ def test_tile_choice(lib, M, N, K, tile16, tile8nn, tile16tn):
 # A 256 x 256 grid that ends in a partial round: its whole rounds run as one
 # launch over the first part of q (TN: columns of C) or p, the rest as a
 # second launch with the tile the table picks for it.
+# (TN with the eight-wave main launch splits only when the last round is
+# less than half full.)
 @pytest.mark.parametrize("dt,layout,M,N,K,axis,at,tail", [
-    (2, 1, 4096, 14336, 4096, "q", 12288, "bf16_tn_128x128_w4"),    # 896 tiles: 3 rounds + 4096 x 2048
-    (3, 1, 4096, 14336, 4096, "q", 12288, "fp8_tn_128x128_w4"),
-    (5, 1, 4096, 14336, 4096, "q", 12288, "mx8_tn_128x128_w4"),
+    (5, 1, 4096, 14336, 4096, "q", 12288, "mx8_tn_128x128_w4"),     # 896 tiles: 3 rounds + 4096 x 2048
     (2, 0, 4096, 14336, 4096, "p", 12288, "bf16_nn_128x128_w4"),    # NN: p runs along N
     (3, 0, 4096, 14336, 4096, "p", 12288, "fp8_nn_256x128_w4"),
-    (2, 1, 14336, 4096, 4096, "p", 12288, "bf16_tn_128x128_w4"),
-    (1, 0, 6144, 6144, 4096, "q", 5376, "f16_nn_128x128_w4"),        # 576 tiles: 504 + 48 x 6 of 128 (TN: 768 of 192 x 256)
+    (1, 0, 6144, 6144, 4096, "q", 5376, "f16_nn_128x128_w4"),        # 576 tiles: 504 + 48 x 6 of 128
+    (2, 1, 6144, 6144, 4096, "q", 5376, "bf16_tn_128x128_w4"),       # TN, last round a quarter full
     (2, 1, 4352, 4352, 1024, "q", 3840, "bf16_tn_128x128_w4_s4"),    # 289 tiles: 255 + 136 of 128, one per CU
     (4, 1, 2560, 14336, 2048, "q", 13056, "fp8s_tn_128x128_w4_s4"),  # (K >= 4096: 750 tiles of 256 x 192)
-    (2, 1, 5120, 5120, 4096, "q", 3072, "bf16_tn_192x256_w4"),       # 400 tiles: 240 + 216 of 192 x 256
-    (1, 1, 3584, 8192, 8192, "p", 2048, "f16_tn_192x256_w4"),        # 448 tiles: 256 + 256 of 192 x 256
+    (5, 1, 5120, 5120, 4096, "q", 3072, "mx8_tn_192x256_w4"),        # 400 tiles: 240 + 216 of 192 x 256
 ])
 def test_split_choice(lib, dt, layout, M, N, K, axis, at, tail):
     full = _kernel(lib, dt, layout, M, N, K)
@@ -268,6 +267,16 @@ def test_split_choice(lib, dt, layout, M, N, K, axis, at, tail):
     assert main.split()[0].endswith(big), full
     assert rest.split()[0] == tail, full
     assert rest.endswith(f"from {axis}={at}"), full
+
+
+@pytest.mark.parametrize("dt,M,N,K", [
+    (2, 4096, 14336, 4096), (3, 4096, 14336, 4096),   # 896 tiles: last round half full
+    (2, 14336, 4096, 4096), (2, 5120, 5120, 4096),    # 1.56 rounds
+    (1, 3584, 8192, 8192),                            # 1.75 rounds
+])
+def test_tn_single_launch_when_the_last_round_is_half_full(lib, dt, M, N, K):
+    k = _kernel(lib, dt, 1, M, N, K)
+    assert " + " not in k and "_256x256_pp " in k, k
 
 
 @pytest.mark.parametrize("M,N,K", [(8192, 8192, 8192), (3584, 8192, 2048), (8191, 8190, 8200), (3072, 4096, 8192)])

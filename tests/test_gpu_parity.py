@@ -91,8 +91,8 @@ def test_four_wave_kernel(dtype, layout):
     small = "256x128_w4" if fp8nn else "128x128_w4_s4"
     mid = "256x128_w4" if fp8nn else "128x128_w4"
     # the last two split into whole 256 x 256 rounds plus a second launch
-    # (along q, then along p)
-    psplit = (14336, 4096) if layout == "tn" else (4096, 14336)
+    # (along q, then along p; TN splits only a last round under half full)
+    psplit = (20480, 2560) if layout == "tn" else (4096, 14336)
     shapes = [(512, 512, 2 * bk, small), (300, 521, 3 * bk, small), (5120, 5120, 3 * bk, "256x256_w4"),
               (1000, 1100, 9 * bk + 16, small), (2048, 1800, 2 * bk + 16, small), (2560, 2304, 3 * bk, mid),
               (129, 77, 5 * bk + 16, small), (5120, 5120, 3 * bk + 16, "256x256_w4"),
@@ -154,7 +154,7 @@ PM1_PATHS = [
     ("bf16", "tn", 8192, 1500, 4104, "bf16_tn_256x192_w4", None),
     # split launches: whole 256 x 256 rounds plus a second launch along q / p
     ("bf16", "tn", 4352, 4352, 192, "bf16_tn_256x256_pp", "q"),
-    ("bf16", "tn", 14336, 4096, 192, "bf16_tn_256x256_pp", "p"),
+    ("bf16", "tn", 20480, 2560, 192, "bf16_tn_256x256_pp", "p"),
     ("fp8", "tn", 4352, 4352, 384, "fp8_tn_256x256_pp", "q"),
     ("fp8", "nn", 4096, 14336, 384, "fp8_nn_256x256_w4", "p"),
 ]
@@ -187,7 +187,7 @@ DETERMINISM = [
     ("fp8", "nn", 5120, 5120, 1184, "mx"),       # MX scale ring, partial scale group
     ("bf16", "tn", 1536, 8192, 4096, None),      # 192 x 256, direct epilogue
     ("bf16", "tn", 1000, 1000, 2048, None),      # 128 x 128, four LDS stages
-    ("bf16", "tn", 14336, 4096, 192, None),      # split launch along p
+    ("bf16", "tn", 20480, 2560, 192, None),      # split launch along p
     ("bf16", "tn", 1000, 1000, 1001, None),      # eight-wave kernel, ragged K
     ("bf16", "tn", 16, 3000, 4096, None),        # skinny split-K, LDS reduction
     ("f32", "nn", 1000, 1000, 1000, None),       # FP32 MFMA kernel
@@ -382,7 +382,7 @@ def compare_scaled(p, cij, sa, sb, rows=None, exact=False):
 def test_fp8_scaled_against_oracle(layout, mode):
     rng = np.random.default_rng(6000 + (layout == "nn") + 2 * (mode == "row"))
     shapes = [(1, 1, 1), (257, 129, 77), (33, 65, 300), (300, 521, 384), (512, 512, 256), (1000, 1100, 1168),
-              (5120, 5120, 384), (5120, 5120, 400), (70, 90, 0), (4352, 4352, 384), (14336, 4096, 384)
+              (5120, 5120, 384), (5120, 5120, 400), (70, 90, 0), (4352, 4352, 384), (20480, 2560, 384)
               if layout == "tn" else (4096, 14336, 384), (1500, 8000, 4096 + 16)]
     for idx, (M, N, K) in enumerate(shapes):
         p = make_problem("fp8", layout, M, N, K, seed=6100 + idx, pad=idx % 2)
