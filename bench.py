@@ -246,6 +246,83 @@ def cpu_baseline(dtype, target_s=25.0):
             "sample": f"{what} of {dtype} {layout} {M}x{N}x{K}, {dt_s:.1f} s wall on {cores} threads"}
 
 
+def run_tool(name, *args):
+    """stdout of a ROCm command-line tool (PATH, then /opt/rocm/bin), or ""."""
+    import shutil
+    import subprocess
+    exe = shutil.which(name) or os.path.join("/opt/rocm/bin", name)
+    try:
+        return subprocess.run([exe, *args], capture_output=True, text=True, timeout=20).stdout
+    except (OSError, subprocess.SubprocessError):
+        return ""
+
+
+def parse_smi(txt):
+    """Socket power (W) and per-XCD engine clocks (MHz) from the text of
+    `amd-smi metric -p -c`; None / [] where a field is missing."""
+    import re
+    m = re.search(r"SOCKET_POWER:\s*(\d+(?:\.\d+)?)\s*W", txt)
+    clocks = [int(c) for _, c in re.findall(r"GFX_(\d+):\s*\n\s*CLK:\s*(\d+)\s*MHz", txt)]
+    return (float(m.group(1)) if m else None), clocks
+
+
+def smi_sample():
+    return parse_smi(run_tool("amd-smi", "metric", "-p", "-c"))
+
+
+def power_cap_w():
+    import re
+    txt = run_tool("rocm-smi", "-M")
+    m = re.search(r"Max Graphics Package Power \(W\):\s*([\d.]+)", txt)
+    return float(m.group(1)) if m else None
+
+
+def sustain(dtype, seconds, made):
+    """One workload launched back to back for `seconds` of wall time; over the
+    second half, a few samples of socket power and per-XCD engine clocks.
+    Shows whether the chip runs at its power cap while the GEMM runs."""
+    import threading
+    import torch
+    from dense_gemm_02_amd import binding
+    p, A, B, C = made
+    stream = torch.cuda.current_stream()
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        if stop.wait(seconds / 2):
+            return
+        while not stop.is_set():
+            samples.append(smi_sample())
+            stop.wait(1.0)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    for _ in range(20):
+        binding.gemm(p.dtype, p.layout, p.M, p.N, p.K, A, p.lda, B, p.ldb, C, p.ldc, stream=stream)
+    torch.cuda.synchronize()
+    th.start()
+    t0 = time.perf_counter()
+    n = 0
+    last = t0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            binding.gemm(p.dtype, p.layout, p.M, p.N, p.K, A, p.lda, B, p.ldb, C, p.ldc, stream=stream)
+        torch.cuda.synchronize()
+        n += 20
+        if time.perf_counter() - last > 2.0:
+            last = time.perf_counter()
+            print(f"[bench] sustain {dtype}: {last - t0:.0f} s, {n} launches", file=sys.stderr, flush=True)
+    el = time.perf_counter() - t0
+    stop.set()
+    th.join()
+    tf = p.flops * n / el / 1e12
+    pw = [s[0] for s in samples if s[0] is not None]
+    return {"sustain": f"{p.dtype}_{p.layout}_{p.M}x{p.N}x{p.K}", "seconds": round(el, 2), "launches": n,
+            "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS[dtype], 4),
+            "socket_power_w": pw, "power_cap_w": power_cap_w(),
+            "xcd_clock_mhz": [s[1] for s in samples if s[1]]}
+
+
 def timing_fields(r, peak=None):
     """Per-launch statistics and the measured engine clock; with a peak, the
     throughput as a fraction of the peak at that clock (the published peak
@@ -273,6 +350,9 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the GEMM, run a plain device copy of MIB MiB three times "
                          "(reference dispatch for the HBM byte counters)")
+    ap.add_argument("--sustain", type=float, default=0, metavar="SECONDS",
+                    help="instead of the timed region, launch each format's workload back to back for SECONDS "
+                         "and sample socket power and engine clocks (amd-smi) over the second half")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -319,6 +399,11 @@ def main():
     # first timed launch, so no host-side input generation separates the
     # timed regions.
     order = [args.dtype] + ([] if args.only else [d for d in WORKLOADS if d != args.dtype])
+    if args.sustain:
+        for d in order:
+            print(json.dumps(sustain(d, args.sustain, make_inputs(d))), flush=True)
+            torch.cuda.empty_cache()
+        return
     made = {d: make_inputs(d) for d in order}
     p, head = time_gemm(args.dtype, args.steps, args.warmup, made=made[args.dtype])
     print(f"[bench] {args.dtype}: {head['ms_per_launch']:.4f} ms/launch, {head['tflops']:.1f} TFLOP/s, "

@@ -181,3 +181,15 @@ def test_kernel_trace_matches_the_compiler(usage):
         # (AGPRs start at a 4-aligned offset after the VGPRs).
         assert nfv >= (-(-u["VGPRs"] // 4) * 4 if u["AGPRs"] else u["VGPRs"]) + u["AGPRs"], name
         assert vgpr == -(-nfv // 8) * 4, (name, vgpr, nfv)
+
+
+def test_bench_reads_power_and_clocks_from_amd_smi_text():
+    """bench.py --sustain reads socket power and the per-XCD engine clocks
+    from amd-smi's text; a layout it does not know gives None and []."""
+    import bench
+    txt = ("GPU: 0\n    POWER:\n        SOCKET_POWER: 1398 W\n        GFX_VOLTAGE: N/A\n    CLOCK:\n"
+           "        GFX_0:\n            CLK: 1795 MHz\n            MIN_CLK: 500 MHz\n"
+           "        GFX_1:\n            CLK: 1713 MHz\n            MIN_CLK: 500 MHz\n"
+           "        MEM_0:\n            CLK: 2000 MHz\n")
+    assert bench.parse_smi(txt) == (1398.0, [1795, 1713])
+    assert bench.parse_smi("") == (None, [])
