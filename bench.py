@@ -7,7 +7,9 @@ A and B i.i.d. N(0,1)/sqrt(K) rounded to FP16 (seed 3), FP32 accumulation,
 FP16 output.  BF16 TN and FP8 E4M3 TN at the same size are timed in the
 same run and reported under "per_dtype".
 
-Timing: W untimed warm-up steps, then exactly K steps between two
+Timing: the workload back to back for --settle-ms of wall time (the chip's
+power controller dips after an idle spell and recovers over 50-100
+launches), W untimed warm-up steps, then exactly K steps between two
 synchronisations, with HIP events recorded on the stream the kernels run on
 (one before each launch, so the mean, min and median per launch are
 known).  TFLOP/s = 2*M*N*K / t.  After the timed region one more launch runs
@@ -117,7 +119,7 @@ def make_inputs(dtype, spec=None):
     return p, A, B, C
 
 
-def time_gemm(dtype, steps, warmup, spec=None, rotate=1, made=None):
+def time_gemm(dtype, steps, warmup, spec=None, rotate=1, made=None, settle_ms=0.0):
     import torch
     from dense_gemm_02_amd import binding
     p, A, B, C = made if made is not None else make_inputs(dtype, spec)
@@ -148,6 +150,19 @@ def time_gemm(dtype, steps, warmup, spec=None, rotate=1, made=None):
         else:
             binding.gemm(p.dtype, p.layout, p.M, p.N, p.K, A, p.lda, b, p.ldb, C, p.ldc, stream=stream)
 
+    # Settle: the workload back to back for settle_ms of wall time before the
+    # warm-up steps.  After an idle spell the chip's power controller first
+    # lets the clock run high, then pulls it below its steady value and only
+    # recovers over the next 50-100 launches (launches 3-10 of a cold start
+    # run up to 35% slower than steady state, profiles/warmup_transient_8192.md);
+    # the timed region is meant to see the steady state.
+    settle_n, t_s = 0, time.perf_counter()
+    while settle_ms > 0 and (time.perf_counter() - t_s) * 1e3 < settle_ms:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        settle_n += 10
+    settle_wall = (time.perf_counter() - t_s) * 1e3
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -174,6 +189,7 @@ def time_gemm(dtype, steps, warmup, spec=None, rotate=1, made=None):
     each = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     flops = p.flops
     res = {"ms_per_launch": ms, "tflops": flops / (ms * 1e-3) / 1e12, "wall_s": wall,
+           "settle_launches": settle_n, "settle_ms": round(settle_wall, 1),
            "min_ms": each[0], "median_ms": each[len(each) // 2] if steps % 2 else
            0.5 * (each[steps // 2 - 1] + each[steps // 2]), "max_ms": each[-1]}
     res["clock_mhz"] = engine_clock(step, stream, kernel_grid(p))
@@ -323,12 +339,34 @@ def sustain(dtype, seconds, made):
             "xcd_clock_mhz": [s[1] for s in samples if s[1]]}
 
 
+def transient(dtype, n, made):
+    """Per-launch durations (us) of the first n launches of one workload after
+    3 s of idle, one event before each launch."""
+    import torch
+    from dense_gemm_02_amd import binding
+    p, A, B, C = made
+    stream = torch.cuda.current_stream()
+    f = lambda: binding.gemm(p.dtype, p.layout, p.M, p.N, p.K, A, p.lda, B, p.ldb, C, p.ldc, stream=stream)
+    f()
+    torch.cuda.synchronize()
+    time.sleep(3.0)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    for i in range(n):
+        ev[i].record(stream)
+        f()
+    ev[n].record(stream)
+    torch.cuda.synchronize()
+    us = [round(ev[i].elapsed_time(ev[i + 1]) * 1e3, 1) for i in range(n)]
+    return {"transient": f"{p.dtype}_{p.layout}_{p.M}x{p.N}x{p.K}", "launch_us": us}
+
+
 def timing_fields(r, peak=None):
     """Per-launch statistics and the measured engine clock; with a peak, the
     throughput as a fraction of the peak at that clock (the published peak
     scaled by measured clock / 2400 MHz)."""
     out = {"mean_ms": round(r["ms_per_launch"], 5), "min_ms": round(r["min_ms"], 5),
            "median_ms": round(r["median_ms"], 5), "max_ms": round(r["max_ms"], 5),
+           "settle_launches": r["settle_launches"], "settle_ms": r["settle_ms"],
            "clock_mhz": None if r["clock_mhz"] is None else round(r["clock_mhz"], 1)}
     if peak is not None and r["clock_mhz"]:
         at = peak * r["clock_mhz"] / PEAK_CLOCK_MHZ
@@ -350,6 +388,12 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the GEMM, run a plain device copy of MIB MiB three times "
                          "(reference dispatch for the HBM byte counters)")
+    ap.add_argument("--settle-ms", type=float, default=150.0, metavar="MS",
+                    help="before each format's warm-up steps, run its workload back to back for MS of wall time "
+                         "(the power controller's transient after idle; 0: none)")
+    ap.add_argument("--transient", type=int, default=0, metavar="N",
+                    help="instead of the timed region, time each of the first N launches of each format after "
+                         "3 s of idle (no settle, no warm-up)")
     ap.add_argument("--sustain", type=float, default=0, metavar="SECONDS",
                     help="instead of the timed region, launch each format's workload back to back for SECONDS "
                          "and sample socket power and engine clocks (amd-smi) over the second half")
@@ -379,7 +423,8 @@ def main():
     if args.workload:
         spec = EXTRA[args.workload]
         skinny = spec[2] <= 32
-        p, r = time_gemm(spec[0], args.steps, args.warmup, spec=spec, rotate=ROTATE if skinny else 1)
+        p, r = time_gemm(spec[0], args.steps, args.warmup, spec=spec, rotate=ROTATE if skinny else 1,
+                         settle_ms=args.settle_ms)
         out_b = 4 if spec[0] in ("f32", "fp8") else 2
         in_b = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}[spec[0]]
         nbytes = (p.M * p.K + p.N * p.K) * in_b + p.M * p.N * out_b
@@ -404,8 +449,13 @@ def main():
             print(json.dumps(sustain(d, args.sustain, make_inputs(d))), flush=True)
             torch.cuda.empty_cache()
         return
+    if args.transient:
+        for d in order:
+            print(json.dumps(transient(d, args.transient, make_inputs(d))), flush=True)
+            torch.cuda.empty_cache()
+        return
     made = {d: make_inputs(d) for d in order}
-    p, head = time_gemm(args.dtype, args.steps, args.warmup, made=made[args.dtype])
+    p, head = time_gemm(args.dtype, args.steps, args.warmup, made=made[args.dtype], settle_ms=args.settle_ms)
     print(f"[bench] {args.dtype}: {head['ms_per_launch']:.4f} ms/launch, {head['tflops']:.1f} TFLOP/s, "
           f"min {head['min_ms']:.4f} median {head['median_ms']:.4f} ms, clock {head['clock_mhz']} MHz",
           file=sys.stderr, flush=True)
@@ -414,7 +464,7 @@ def main():
         for d in WORKLOADS:
             if d == args.dtype:
                 continue
-            _, r = time_gemm(d, args.steps, args.warmup, made=made.pop(d))
+            _, r = time_gemm(d, args.steps, args.warmup, made=made.pop(d), settle_ms=args.settle_ms)
             per[d] = {"tflops": round(r["tflops"], 1), "ms_per_launch": round(r["ms_per_launch"], 4),
                       "frac_of_peak": round(r["tflops"] / PEAK_TFLOPS[d], 4), **timing_fields(r, PEAK_TFLOPS[d])}
             print(f"[bench] {d}: {r['ms_per_launch']:.4f} ms/launch, {r['tflops']:.1f} TFLOP/s, "
