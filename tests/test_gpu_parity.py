@@ -585,6 +585,26 @@ def test_leading_dimensions_at_the_descriptor_limit(dtype, layout):
     torch.cuda.empty_cache()
 
 
+# Grids of extreme aspect: one row of 4096 tiles along q (N = 2^20) and one
+# column of 1024 tiles along p (M = 2^18), K two stages: the tile scheduler's
+# spread over the XCDs and its grouping with a single tile on one axis, and
+# workgroup indices far past one round, against the whole oracle output.
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_extreme_aspect_grids(dtype):
+    import torch
+    bk = 128 if dtype == "fp8" else 64
+    for idx, (M, N) in enumerate([(256, 1 << 20), (1 << 18, 256), (250, (1 << 20) - 3)]):
+        K = 2 * bk
+        p = make_problem(dtype, "tn", M, N, K, seed=9800 + idx)
+        say(f"case aspect {kernel_name(dtype, 'tn', M, N, K)} M={M} N={N} K={K}")
+        cij, pad = c_host(p, run_gpu(p))
+        assert pad_untouched(pad, dtype)
+        ok, err, nbad = compare(p, cij)
+        assert ok, f"{dtype} {(M, N, K)}: max err {err:.3e}, {nbad} bad"
+        del cij, pad
+        torch.cuda.empty_cache()
+
+
 # The tensor-level calls refuse, before any launch, device tensors too small
 # for what the call would read or write, and host, float64 or strided scale
 # factors.
