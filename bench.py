@@ -230,12 +230,13 @@ def engine_clock(step, stream, grid):
     return float(np.median(mhz)) if mhz.size else None
 
 
-def cpu_baseline(dtype, target_s=25.0):
+def cpu_baseline(dtype, target_s=25.0, full_s=60.0):
     """The oracle (never tuned) on the headline workload, timed wall-clock on
-    every core this process may run on.  A short run on 32 rows measures its
-    rate; then whole output rows, up to all of them, are computed in one
-    timed call sized to about `target_s` seconds, so the default bench stays
-    within minutes on hosts where the full product would take longer."""
+    every core this process may run on.  A short run on 256 rows measures its
+    rate; if the whole product is estimated at full_s seconds or less it is
+    computed in one timed call, otherwise as many whole output rows as fit
+    about target_s seconds, so the default bench stays within minutes on
+    hosts where the full product would take longer."""
     import oracle
     from dense_gemm_02_amd import inputs
     dt, layout, M, N, K, seed, dist = WORKLOADS[dtype]
@@ -244,11 +245,11 @@ def cpu_baseline(dtype, target_s=25.0):
     lay = oracle.TN if layout == "tn" else oracle.NN
     cores = len(os.sched_getaffinity(0))
     rng = np.random.default_rng(0)
-    probe = np.sort(rng.choice(M, 32, replace=False))
+    probe = np.sort(rng.choice(M, min(M, 256), replace=False))
     t0 = time.perf_counter()
     oracle.gemm(fmt, lay, M, N, K, p.A, p.lda, p.B, p.ldb, rows=probe, threads=cores)
     per_row = (time.perf_counter() - t0) / len(probe)
-    nrows = int(min(M, max(64, target_s / max(per_row, 1e-6))))
+    nrows = M if per_row * M <= full_s else int(min(M, max(64, target_s / max(per_row, 1e-6))))
     rows = None if nrows >= M else np.sort(rng.choice(M, nrows, replace=False))
     t0 = time.perf_counter()
     oracle.gemm(fmt, lay, M, N, K, p.A, p.lda, p.B, p.ldb, rows=rows, threads=cores)
