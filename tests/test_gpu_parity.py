@@ -585,6 +585,40 @@ def test_leading_dimensions_at_the_descriptor_limit(dtype, layout):
     torch.cuda.empty_cache()
 
 
+# Random shapes, pitches and C placements: M, N up to 700 and K up to 1500
+# (log-uniform, so single tiles, ragged edges and several rounds all occur),
+# A and B pitches padded by 0-3 16-byte units, C's pitch by 0-5 elements and
+# its base 0-7 elements past an allocation; the whole output against the
+# oracle, the padding and the storage around C untouched.
+@pytest.mark.parametrize("dtype,layout", COMBOS)
+def test_random_shapes_pitches_and_offsets(dtype, layout):
+    import torch
+    from dense_gemm_02_amd import binding
+    rng = np.random.default_rng(12000 + COMBOS.index((dtype, layout)))
+    for idx in range(12):
+        M, N = (int(np.exp(rng.uniform(0, np.log(700)))) for _ in range(2))
+        K = int(np.exp(rng.uniform(0, np.log(1500))))
+        la, lb, lc = inputs.min_ld(layout, M, N, K)
+        lda = aligned_ld(la, dtype, int(rng.integers(0, 4)))
+        ldb = aligned_ld(lb, dtype, int(rng.integers(0, 4)))
+        ldc = lc + int(rng.integers(0, 6))
+        off = int(rng.integers(0, 8))
+        p = inputs.make(dtype, layout, M, N, K, 12100 + idx, DIST[dtype], lda=lda, ldb=ldb, ldc=ldc)
+        rows = N if layout == "tn" else M
+        tdt = torch.int32 if dtype in ("f32", "fp8") else torch.int16
+        flat = torch.full((off + rows * ldc + 8,), -1, dtype=tdt, device="cuda")
+        C = flat[off:off + rows * ldc].view(rows, ldc)
+        say(f"case random {kernel_name(dtype, layout, M, N, K)} M={M} N={N} K={K} ld={lda},{ldb},{ldc} off={off}")
+        binding.gemm(dtype, layout, M, N, K, to_dev(p.A), lda, to_dev(p.B), ldb, C, ldc)
+        torch.cuda.synchronize()
+        f = flat.cpu().numpy()
+        assert np.all(f[:off] == -1) and np.all(f[off + rows * ldc:] == -1), "wrote outside C"
+        cij, pad = c_host(p, C)
+        assert pad_untouched(pad, dtype)
+        ok, err, nbad = compare(p, cij)
+        assert ok, f"{dtype} {layout} {(M, N, K, lda, ldb, ldc, off)}: max err {err:.3e}, {nbad} bad"
+
+
 # Grids of extreme aspect: one row of 4096 tiles along q (N = 2^20) and one
 # column of 1024 tiles along p (M = 2^18), K two stages: the tile scheduler's
 # spread over the XCDs and its grouping with a single tile on one axis, and
