@@ -619,6 +619,42 @@ def test_random_shapes_pitches_and_offsets(dtype, layout):
         assert ok, f"{dtype} {layout} {(M, N, K, lda, ldb, ldc, off)}: max err {err:.3e}, {nbad} bad"
 
 
+# The same for the scaled entry points: random shapes and pitches, per-tensor
+# or per-row factors (gemm_fp8_scaled) and E8M0 block scales with a padded
+# scale pitch (gemm_mxfp8, K a multiple of 32), whole outputs.
+@pytest.mark.parametrize("layout", ["tn", "nn"])
+def test_random_shapes_scaled_and_mx(layout):
+    rng = np.random.default_rng(12500 + (layout == "nn"))
+    for idx in range(10):
+        M, N = (int(np.exp(rng.uniform(0, np.log(700)))) for _ in range(2))
+        K = int(np.exp(rng.uniform(0, np.log(1500))))
+        la, lb, lc = inputs.min_ld(layout, M, N, K)
+        lda = aligned_ld(la, "fp8", int(rng.integers(0, 4)))
+        ldb = aligned_ld(lb, "fp8", int(rng.integers(0, 4)))
+        ldc = lc + int(rng.integers(0, 6))
+        p = inputs.make("fp8", layout, M, N, K, 12600 + idx, DIST["fp8"], lda=lda, ldb=ldb, ldc=ldc)
+        row = bool(rng.integers(0, 2))
+        sa, sb = _factors(rng, M if row else 1), _factors(rng, N if row else 1)
+        say(f"case random scaled {kernel_name('fp8s', layout, M, N, K)} M={M} N={N} K={K} per_row={row}")
+        cij, pad = c_host(p, run_scaled(p, sa, sb))
+        assert pad_untouched(pad, "fp8")
+        ok, err = compare_scaled(p, cij, sa, sb)
+        assert ok, f"scaled {layout} {(M, N, K, lda, ldb, ldc)}: max err {err:.3e}"
+        Km = 32 * max(1, K // 32)
+        pm = inputs.make("fp8", layout, M, N, Km, 12700 + idx, DIST["fp8"],
+                         lda=aligned_ld(inputs.min_ld(layout, M, N, Km)[0], "fp8", int(rng.integers(0, 4))),
+                         ldb=aligned_ld(inputs.min_ld(layout, M, N, Km)[1], "fp8", int(rng.integers(0, 4))),
+                         ldc=inputs.min_ld(layout, M, N, Km)[2] + int(rng.integers(0, 6)))
+        nb = Km // 32
+        ld = ((nb + 15) // 16) * 16 + 16 * int(rng.integers(0, 2))
+        SA, SB = mx_scales(rng, M, nb, ld), mx_scales(rng, N, nb, ld)
+        say(f"case random mx {kernel_name('mx8', layout, M, N, Km)} M={M} N={N} K={Km} ld={ld}")
+        cij, pad = c_host(pm, run_mx(pm, SA, ld, SB, ld))
+        assert pad_untouched(pad, "fp8")
+        ok, err = compare_mx(pm, cij, SA, ld, SB, ld)
+        assert ok, f"mx {layout} {(M, N, Km, ld)}: max err {err:.3e}"
+
+
 # Grids of extreme aspect: one row of 4096 tiles along q (N = 2^20) and one
 # column of 1024 tiles along p (M = 2^18), K two stages: the tile scheduler's
 # spread over the XCDs and its grouping with a single tile on one axis, and
