@@ -619,6 +619,24 @@ def test_random_shapes_pitches_and_offsets(dtype, layout):
         assert ok, f"{dtype} {layout} {(M, N, K, lda, ldb, ldc, off)}: max err {err:.3e}, {nbad} bad"
 
 
+# Larger random shapes (M, N from 700 to 6000, K from 100 to 5000): several
+# rounds, part-filled last rounds, split launches and the one-round tiles at
+# random sizes, with padded pitches; whole outputs against the oracle's
+# full-size form.
+@pytest.mark.parametrize("dtype,layout", COMBOS)
+def test_random_large_shapes(dtype, layout):
+    rng = np.random.default_rng(13000 + COMBOS.index((dtype, layout)))
+    for idx in range(3):
+        M, N = (int(np.exp(rng.uniform(np.log(700), np.log(6000)))) for _ in range(2))
+        K = int(np.exp(rng.uniform(np.log(100), np.log(5000))))
+        p = make_problem(dtype, layout, M, N, K, seed=13100 + idx, pad=int(rng.integers(0, 3)))
+        say(f"case random large {kernel_name(dtype, layout, M, N, K)} M={M} N={N} K={K}")
+        cij, pad = c_host(p, run_gpu(p))
+        assert pad_untouched(pad, dtype)
+        ok, err, nbad = compare(p, cij)
+        assert ok, f"{dtype} {layout} {(M, N, K)}: max err {err:.3e}, {nbad} bad"
+
+
 # The same for the scaled entry points: random shapes and pitches, per-tensor
 # or per-row factors (gemm_fp8_scaled) and E8M0 block scales with a padded
 # scale pitch (gemm_mxfp8, K a multiple of 32), whole outputs.
