@@ -314,6 +314,43 @@ def test_deterministic_and_stream_ordered():
     assert ok, err
 
 
+def test_concurrent_calls_from_threads_and_streams():
+    # Host threads calling the library at once, each on its own stream (the
+    # binding drops the interpreter lock inside the C calls): every result
+    # must match the oracle, as the planning state is per call and the
+    # diagnostics per thread.
+    import threading
+    import torch
+    cases = [("bf16", "tn", 1000, 900, 700), ("fp8", "tn", 600, 1300, 512), ("f16", "nn", 800, 700, 300),
+             ("f32", "nn", 700, 500, 260), ("bf16", "nn", 16, 3000, 4096), ("fp8", "nn", 5120, 2048, 256)]
+    probs = [make_problem(d, l, M, N, K, seed=14000 + i) for i, (d, l, M, N, K) in enumerate(cases)]
+    devs = [(to_dev(p.A), to_dev(p.B), alloc_c(p)) for p in probs]
+    streams = [torch.cuda.Stream() for _ in probs]
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(i):
+        try:
+            p, (A, B, C), st = probs[i], devs[i], streams[i]
+            for _ in range(3):
+                run_gpu(p, A=A, B=B, C=C, stream=st, sync=False)
+        except Exception as e:  # noqa: BLE001 -- reported below
+            errors.append((i, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(probs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for p, (_, _, C) in zip(probs, devs):
+        cij, pad = c_host(p, C)
+        assert pad_untouched(pad, p.dtype)
+        ok, err, nbad = compare(p, cij)
+        assert ok, f"{p.dtype} {p.layout} {(p.M, p.N, p.K)}: max err {err:.3e}, {nbad} bad"
+
+
 def test_odd_ldc_scalar_store_path():
     for dtype in ("bf16", "f16", "fp8", "f32"):
         p = make_problem(dtype, "tn", 301, 133, 200, seed=11)
