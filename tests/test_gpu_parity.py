@@ -351,6 +351,52 @@ def test_concurrent_calls_from_threads_and_streams():
         assert ok, f"{p.dtype} {p.layout} {(p.M, p.N, p.K)}: max err {err:.3e}, {nbad} bad"
 
 
+def test_calls_captured_in_a_hip_graph():
+    # The library allocates nothing and issues only kernel launches on the
+    # caller's stream, so its calls can be captured: a graph holding a split
+    # launch (BF16 TN 4352 x 4352, two kernels), an FP8 call and a skinny call
+    # is replayed three times with new operands copied in eagerly between the
+    # replays; every replay must equal an eager run on the same operands bit
+    # for bit.
+    import torch
+    from dense_gemm_02_amd import binding
+    cases = [("bf16", "tn", 4352, 4352, 192), ("fp8", "tn", 1000, 1100, 640), ("bf16", "tn", 16, 3000, 4096)]
+    assert " + " in kernel_name("bf16", "tn", 4352, 4352, 192)
+    probs = [[make_problem(d, l, M, N, K, seed=15000 + 10 * i + r) for r in range(3)]
+             for i, (d, l, M, N, K) in enumerate(cases)]
+    bufs = [(to_dev(ps[0].A), to_dev(ps[0].B), alloc_c(ps[0])) for ps in probs]
+
+    def calls():
+        for ps, (A, B, C) in zip(probs, bufs):
+            p = ps[0]
+            binding.gemm(p.dtype, p.layout, p.M, p.N, p.K, A, p.lda, B, p.ldb, C, p.ldc)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()                      # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    torch.cuda.synchronize()
+    for r in range(3):
+        for ps, (A, B, C) in zip(probs, bufs):
+            A.copy_(to_dev(ps[r].A))
+            B.copy_(to_dev(ps[r].B))
+            C.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for ps, (A, B, C) in zip(probs, bufs):
+            eager = run_gpu(ps[r], A=A, B=B)
+            assert torch.equal(C, eager), (ps[r].dtype, ps[r].M, ps[r].N, ps[r].K, r)
+            cij, pad = c_host(ps[r], C)
+            ok, err, nbad = compare(ps[r], cij)
+            assert ok, f"replay {r} {(ps[r].M, ps[r].N, ps[r].K)}: max err {err:.3e}, {nbad} bad"
+
+
 def test_odd_ldc_scalar_store_path():
     for dtype in ("bf16", "f16", "fp8", "f32"):
         p = make_problem(dtype, "tn", 301, 133, 200, seed=11)
