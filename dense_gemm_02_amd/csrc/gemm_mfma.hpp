@@ -23,8 +23,8 @@
 //    issued before the current stage's MFMAs and written to the other LDS
 //    buffer after them, one barrier per stage (Step 2).
 //  * MFMA: v_mfma_f32_32x32x16_{f16,bf16} (k = 16, 16 bytes per lane per
-//    operand) or v_mfma_scale_f32_32x32x64_f8f6f4 with unit E8M0 scales
-//    (k = 64, 32 bytes per lane), FP32 accumulators in registers.
+//    operand) or the unscaled v_mfma_f32_32x32x64_f8f6f4 (k = 64, 32 bytes
+//    per lane), FP32 accumulators in registers.
 //  * Epilogue: each lane holds four consecutive p of one q, contiguous in C;
 //    convert with round-to-nearest-even and store 8 or 16 bytes at a time.
 #pragma once
@@ -98,9 +98,12 @@ struct OpFP8 {
     const i32x4 hi = *(const i32x4*)(base + off[1]);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
-  // Formats 0/0 = E4M3 for both operands; scales 127 = 2^0 in E8M0.
+  // Formats 0/0 = E4M3 for both operands.  Scale operands 0: the compiler
+  // then emits the unscaled v_mfma_f32_32x32x64_f8f6f4 (the plain product;
+  // measured bit-identical to unit E8M0 scales, 127, on random E4M3 data)
+  // instead of the scaled form with its extra scale dword.
   __device__ static f32x16 mma(Frag a, Frag b, f32x16 c) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
   }
   __device__ static f32x16 mma_parts(const u32x4 (&a)[2], const u32x4 (&b)[2], f32x16 c) {
     const i32x8 av = __builtin_shufflevector(__builtin_bit_cast(i32x4, a[0]), __builtin_bit_cast(i32x4, a[1]), 0, 1,
@@ -117,7 +120,8 @@ struct OpFP8 {
                                              2, 3, 4, 5, 6, 7);
     const i32x8 bv = __builtin_shufflevector(__builtin_bit_cast(i32x4, b[0]), __builtin_bit_cast(i32x4, b[1]), 0, 1,
                                              2, 3, 4, 5, 6, 7);
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
+    // Unscaled form, as mma above (v_mfma_f32_16x16x128_f8f6f4).
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
   }
 };
 

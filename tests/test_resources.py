@@ -193,3 +193,16 @@ def test_bench_reads_power_and_clocks_from_amd_smi_text():
            "        MEM_0:\n            CLK: 2000 MHz\n")
     assert bench.parse_smi(txt) == (1398.0, [1795, 1713])
     assert bench.parse_smi("") == (None, [])
+
+
+def test_fp8_kernels_use_the_unscaled_mfma():
+    """The FP8 ping-pong kernels issue v_mfma_f32_16x16x128_f8f6f4 (the scale
+    builtin with zero scale operands compiles to it) and no scaled MFMA."""
+    u = [x for x in B.units() if os.path.basename(x[0]) == "pp.hip"][0]
+    out = subprocess.run(["/opt/rocm/bin/hipcc"] + B.HIPCC_FLAGS + u[2] +
+                         ["--offload-device-only", "-S", "-o", "-", "-c", u[0]],
+                         capture_output=True, text=True, timeout=600)
+    assert out.returncode == 0, out.stderr[-2000:]
+    asm = out.stdout
+    assert asm.count("v_mfma_f32_16x16x128_f8f6f4") > 0
+    assert "v_mfma_scale_" not in asm
