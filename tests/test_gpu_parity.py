@@ -668,6 +668,20 @@ def test_leading_dimensions_at_the_descriptor_limit(dtype, layout):
     torch.cuda.empty_cache()
 
 
+# Long K: 2^18 + 16 (4097 stages of the 16-bit kernels, 2049 of FP8, a K
+# tail), +-1 inputs so that every sum is an exact integer below 2^24: the
+# whole output bit for bit, on both layouts.
+@pytest.mark.parametrize("dtype,layout", [("bf16", "tn"), ("fp8", "tn"), ("f16", "nn"), ("fp8", "nn")])
+def test_long_k_bit_exact(dtype, layout):
+    K = (1 << 18) + 16
+    p = make_problem(dtype, layout, 300, 260, K, seed=16000, dist="pm1")
+    say(f"case long K {kernel_name(dtype, layout, 300, 260, K)} K={K}")
+    cij, pad = c_host(p, run_gpu(p))
+    assert pad_untouched(pad, dtype)
+    ok, _, nbad = compare(p, cij, exact=True)
+    assert ok, f"{dtype} {layout} K={K}: {nbad} elements differ"
+
+
 # Random shapes, pitches and C placements: M, N up to 700 and K up to 1500
 # (log-uniform, so single tiles, ragged edges and several rounds all occur),
 # A and B pitches padded by 0-3 16-byte units, C's pitch by 0-5 elements and
