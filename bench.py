@@ -421,6 +421,10 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
         return
 
+    if args.workload and args.sustain:
+        spec = EXTRA[args.workload]
+        print(json.dumps(sustain(spec[0], args.sustain, make_inputs(spec[0], spec))), flush=True)
+        return
     if args.workload:
         spec = EXTRA[args.workload]
         skinny = spec[2] <= 32
