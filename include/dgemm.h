@@ -25,7 +25,9 @@
  *
  * Memory and ownership.  A, B and C are DEVICE pointers owned by the caller;
  * the library never allocates, frees or retains them and keeps no mutable
- * global state (beyond a thread-local error code), so calls are reentrant.
+ * global state (beyond two thread-local diagnostics: the last HIP error code
+ * and the clock-trace buffer set with dgemm_trace_clock), so calls are
+ * reentrant.
  * A and B must not overlap C, and must be readable over whole rows of
  * their pitch: A over M*lda elements, B over K*ldb (NN) or N*ldb (TN); the
  * kernels copy 16-byte pieces and may read the padding of the last row.
@@ -41,7 +43,7 @@
  * kernel surface at the caller's next synchronisation.
  *
  * Errors.  Each call returns a dgemm_status and never prints or aborts; the
- * only state kept is the thread-local code of the last HIP failure.
+ * code of the last HIP failure is kept per thread (dgemm_last_hip_error).
  * Checks, in this order: layout -> DGEMM_ERR_INVALID_LAYOUT; any of M, N, K
  * negative -> DGEMM_ERR_INVALID_DIM; M == 0 or N == 0 -> DGEMM_OK with no
  * work; a NULL A or B (when K > 0) or NULL C -> DGEMM_ERR_NULL_POINTER; a
